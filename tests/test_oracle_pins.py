@@ -1,0 +1,471 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one oracle function to a value printed on the pages, a closed
+form, an invariant, a library routine (numpy stable sort, torch's float8 and
+bfloat16 casts) or brute force on tiny inputs, chosen so that a plausible slip
+(dropped term, wrong sign or index, transposed operand) fails at least one.
+CPU only.
+"""
+
+from math import comb
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+# ---------------------------------------------------------------------------
+# helpers written independently of oracle.c
+# ---------------------------------------------------------------------------
+
+
+def finite_e4m3_table():
+    """(codes, values) of the 254 finite E4M3FN codes, from the bit-field definition."""
+    codes, vals = [], []
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            continue
+        v = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        codes.append(c)
+        vals.append(-v if s else v)
+    return np.array(codes, np.uint8), np.array(vals, np.float64)
+
+
+def brute_force_e4m3(q: np.ndarray) -> np.ndarray:
+    """Nearest finite code by exhaustive search, ties to the even mantissa; |q| > 464 -> NaN."""
+    codes, vals = finite_e4m3_table()
+    out = np.empty(q.shape, np.uint8)
+    for i, x in enumerate(q.astype(np.float64)):
+        if abs(x) > 464.0:
+            out[i] = 0xFF if x < 0 else 0x7F
+            continue
+        # same-sign candidates only, so +-0 keep their sign
+        neg = np.signbit(x)
+        sel = (codes >= 0x80) if neg else (codes < 0x80)
+        cc, vv = codes[sel], vals[sel]
+        d = np.abs(vv - x)
+        best = np.flatnonzero(d == d.min())
+        if len(best) > 1:
+            best = [b for b in best if (cc[b] & 1) == 0]
+        out[i] = cc[best[0]]
+    return out
+
+
+def bf16_bits_to_f64(h: np.ndarray) -> np.ndarray:
+    return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def torch_bf16_bits(f: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(f, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def small_workload(P=4, S=64, E=16, K=2, H=512, A=16, routing="uniform", seed=0, zero_padding=True):
+    return synth.Workload("t", P, S, E, K, H, A, zero_padding, routing, seed=seed)
+
+
+# ---------------------------------------------------------------------------
+# scalar encodings
+# ---------------------------------------------------------------------------
+
+
+def test_e4m3_encode_matches_brute_force_search():
+    rng = np.random.default_rng(1)
+    codes, vals = finite_e4m3_table()
+    pos = np.sort(vals[vals > 0])
+    mids = (pos[1:] + pos[:-1]) / 2
+    q = np.concatenate([
+        rng.uniform(-464, 464, 3000), rng.normal(0, 1, 2000) * 2.0 ** rng.integers(-12, 8, 2000),
+        mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, 1000), vals, [0.0, -0.0, 464.0, 448.0, 465.0, -470.0],
+        np.arange(0, 20) * 2.0 ** -10,  # subnormal grid and its midpoints
+    ]).astype(np.float32)
+    np.testing.assert_array_equal(oracle.e4m3_encode(q), brute_force_e4m3(q))
+
+
+def test_e4m3_encode_matches_torch_cast_on_dense_sample():
+    # every 97th fp32 pattern in [0, 464] plus +-3 ulp around every midpoint
+    pats = np.arange(0, 0x43E80001, 97, dtype=np.uint32)
+    _, vals = finite_e4m3_table()
+    pos = np.sort(vals[vals > 0]).astype(np.float32)
+    mids = ((pos[1:].astype(np.float64) + pos[:-1]) / 2).astype(np.float32).view(np.uint32)
+    near = (mids[:, None].astype(np.int64) + np.arange(-3, 4)[None, :]).ravel().astype(np.uint32)
+    q = np.concatenate([pats, near]).view(np.float32)
+    q = np.concatenate([q, -q])
+    ref = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.e4m3_encode(q), ref)
+
+
+def test_e4m3_decode_matches_torch():
+    c = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    got = oracle.e4m3_decode(c)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok].view(np.uint32), ref[ok].view(np.uint32))
+
+
+def test_bf16_round_matches_torch_including_ties():
+    rng = np.random.default_rng(2)
+    r = rng.integers(0, 2 ** 32, 200000, dtype=np.uint64).astype(np.uint32)
+    ties = (r & 0xFFFF0000) | 0x8000  # exact halfway cases
+    near = np.concatenate([ties - 1, ties + 1])
+    f = np.concatenate([r, ties, near]).view(np.float32)
+    f = f[np.isfinite(f)]
+    f = np.concatenate([f, np.array([0.0, -0.0, np.inf, -np.inf, 3.4e38, 1e-40], np.float32)])
+    np.testing.assert_array_equal(oracle.bf16_round(f), torch_bf16_bits(f))
+
+
+# ---------------------------------------------------------------------------
+# layout
+# ---------------------------------------------------------------------------
+
+
+def brute_force_layout(P, S, E, K, A, topk):
+    """Definitions written out with direct counts (quadratic, tiny inputs only)."""
+    T, El = P * S, E // P
+    itr = np.zeros((T, P), np.uint8)
+    for u in range(T):
+        for j in range(K):
+            if topk[u, j] >= 0:
+                itr[u, topk[u, j] // El] = 1
+    ntpr = np.array([[itr[s * S:(s + 1) * S, d].sum() for d in range(P)] for s in range(P)])
+    ntpe = np.array([[(topk[s * S:(s + 1) * S] == e).sum() for e in range(E)] for s in range(P)])
+    send_head = np.full((T, P), -1)
+    for u in range(T):
+        for d in range(P):
+            if itr[u, d]:
+                send_head[u, d] = itr[:u, d].sum()  # #{u' < u : itr[u'][d]}
+    return itr, ntpr, ntpe, send_head
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_layout_tiny_brute_force(seed):
+    w = synth.CONFIGS["tiny-p4-s64-e16-k2-h512"] if seed == 0 else small_workload(seed=seed)
+    topk = synth.gen_routing(w)
+    if seed == 2:  # unused slots and duplicate experts inside a token
+        topk = topk.copy()
+        topk[::7, 1] = -1
+        topk[3::11, 1] = topk[3::11, 0]
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    itr, ntpr, ntpe, send_head = brute_force_layout(w.P, w.S, w.E, w.K, w.A, topk)
+    np.testing.assert_array_equal(lay.is_token_in_rank, itr)
+    np.testing.assert_array_equal(lay.num_tokens_per_rank, ntpr)
+    np.testing.assert_array_equal(lay.num_tokens_per_expert, ntpe)
+    np.testing.assert_array_equal(lay.rank_prefix_matrix, np.cumsum(ntpr, axis=0))
+    np.testing.assert_array_equal(lay.num_recv_tokens, ntpr.sum(0))
+    np.testing.assert_array_equal(lay.send_head, send_head)
+    # recv_src_idx is the inverse of send_head: recv_src_idx[d][send_head[u][d]] = t(u)
+    for u in range(w.T):
+        for d in range(w.P):
+            if send_head[u, d] >= 0:
+                assert lay.recv_src_idx[lay.recv_src_base[d] + send_head[u, d]] == u % w.S
+    # the source rank of a received token is the s with rank_prefix[s-1][d] <= i < rank_prefix[s][d]
+    for d in range(w.P):
+        for i in range(int(lay.num_recv_tokens[d])):
+            s = int(np.searchsorted(lay.rank_prefix_matrix[:, d], i, side="right"))
+            u = s * w.S + int(lay.recv_src_idx[lay.recv_src_base[d] + i])
+            assert send_head[u, d] == i
+
+
+def test_layout_dst_slot_is_stable_sort_by_expert():
+    """dst_slot equals numpy's stable argsort of the flattened (u, j) stream by expert,
+    and the tutorial's deterministic key expert * 1e10 + src_token_global_idx."""
+    for w in [synth.CONFIGS["tiny-p4-s64-e16-k2-h512"], small_workload(P=8, S=300, E=64, K=6, A=8, seed=5),
+              small_workload(P=8, S=96, E=32, K=4, A=1, routing="zipf", seed=3)]:
+        topk = synth.gen_routing(w)
+        if w.K > 2:
+            topk = topk.copy()
+            topk[::5, -1] = -1
+            topk[1::9, 2] = topk[1::9, 1]  # duplicates
+        lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+        El = w.E // w.P
+        flat = topk.ravel()
+        valid = np.flatnonzero(flat >= 0)
+        keys = flat[valid]
+        order = np.argsort(keys, kind="stable")
+        sk = keys[order]
+        rank_in_expert = np.empty(len(keys), np.int64)
+        rank_in_expert[order] = np.arange(len(keys)) - np.searchsorted(sk, sk, side="left")
+        expect = np.full(flat.shape, -1, np.int64)
+        expect[valid] = lay.expert_offset[keys // El, keys % El] + rank_in_expert
+        np.testing.assert_array_equal(lay.dst_slot.ravel(), expect)
+        # page key (exact in float64: 256 * 1e10 < 2**53); within-token ties keep slot order
+        u = valid // w.K
+        page_key = keys.astype(np.float64) * 1e10 + u
+        np.testing.assert_array_equal(np.argsort(page_key, kind="stable"), order)
+
+
+@pytest.mark.parametrize("A", [1, 16, 128])
+def test_num_expanded_closed_form(A):
+    w = small_workload(P=8, S=512, E=64, K=4, A=A, routing="zipf", seed=7)
+    topk = synth.gen_routing(w)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    n = np.bincount(topk[topk >= 0], minlength=w.E)
+    np.testing.assert_array_equal(lay.num_tokens_per_expert_total, n)
+    padded = -(-n // A) * A
+    El = w.E // w.P
+    np.testing.assert_array_equal(lay.num_expanded, padded.reshape(w.P, El).sum(1))
+    assert np.all(lay.expert_offset % A == 0)
+    np.testing.assert_array_equal(lay.window_row_base, np.concatenate([[0], np.cumsum(lay.num_expanded)]))
+    # dst_slot is a bijection from valid slots onto the non-padding rows
+    rows = lay.window_row_base[topk[topk >= 0] // El] + lay.dst_slot[topk >= 0]
+    assert len(np.unique(rows)) == len(rows)
+    e_of = np.repeat(np.arange(w.E), n)
+    starts = lay.window_row_base[e_of // El] + lay.expert_offset[e_of // El, e_of % El]
+    within = np.concatenate([np.arange(c) for c in n]) if len(n) else np.array([])
+    np.testing.assert_array_equal(np.sort(rows), np.sort(starts + within))
+
+
+def test_distinct_ranks_with_replacement_matches_page_formula():
+    """Tutorial section 1.3: expected distinct ranks per token R(1-(1-1/R)^k) for independent slots."""
+    rng = np.random.default_rng(11)
+    for R, E, K in [(8, 256, 6), (8, 256, 8), (32, 256, 8), (128, 256, 6)]:
+        T = R * (40000 // R)
+        topk = rng.integers(0, E, (T, K)).astype(np.int64)  # duplicates allowed -> dedup exercised
+        lay = oracle.layout(R, T // R, E, K, 1, topk)
+        cnt = lay.is_token_in_rank.sum(1).astype(np.float64)
+        expect = R * (1 - (1 - 1 / R) ** K)
+        assert abs(cnt.mean() - expect) < 5 * cnt.std() / np.sqrt(T) + 1e-9, (R, K, cnt.mean(), expect)
+
+
+def test_distinct_ranks_without_replacement_exact_mean():
+    """Distinct experts (the workloads' routing): mean distinct ranks is R(1 - C(E-E_l,K)/C(E,K))."""
+    for w in [synth.CONFIGS["dsv3-bf16-p8-s4096-e256-k8-h7168"], synth.CONFIGS["tiny-p4-s64-e16-k2-h512"]]:
+        topk = synth.gen_routing(w)
+        lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+        cnt = lay.is_token_in_rank.sum(1).astype(np.float64)
+        El = w.E // w.P
+        exact = w.P * (1 - comb(w.E - El, w.K) / comb(w.E, w.K))
+        assert abs(cnt.mean() - exact) < 5 * cnt.std() / np.sqrt(w.T) + 1e-9
+        page = w.P * (1 - (1 - 1 / w.P) ** w.K)
+        if w.T > 1000:  # the with-replacement formula is within 1% for 8 ranks x top-8
+            assert abs(cnt.mean() - page) / page < 0.01
+
+
+def test_local_experts_and_ledger_values_from_pages(golden):
+    g = golden["local_experts"]
+    assert g["num_experts"] // 8 == g["ep8_local"] and g["num_experts"] // 128 == g["ep128_local"]
+    # Dispatch one token with K=6 distinct experts at H=7168: the oracle writes exactly K rows
+    # of H*b payload bytes per token; combine reads K bf16 rows plus K fp32 weights.
+    led = golden["byte_ledger"]
+    K, H = led["k"], led["hidden"]
+    P, E = 8, 256
+    topk = np.array([[3, 40, 77, 150, 151, 250]] + [[-1] * K] * (P - 1), np.int64)
+    x = synth.gen_bf16_rows(0, 1, P, H)
+    w = np.full((P, K), 1.0 / K, np.float32)
+    lay = oracle.layout(P, 1, E, K, 1, topk)
+    for fp8, fill, b, key in [(True, 0x7F, 1, "fp8_dispatch_bytes_per_token"),
+                              (False, 0xFFFF, 2, "bf16_dispatch_bytes_per_token")]:
+        rx, sc, rw, meta = oracle.dispatch(lay, H, x, w, fp8, False, fill=fill)
+        rows_of_token0 = np.flatnonzero(meta[:, 0] == 0)
+        payload = rx[rows_of_token0]
+        assert payload.size * b == led[key]
+        assert not np.any(payload == fill)  # every byte of those rows was written
+        if fp8:
+            assert sc.shape[1] * 4 // 2 == golden["fp8_scale_packs"]["num_sf_packs_int16"]
+    combine_bytes = len(rows_of_token0) * H * 2 + K * 4
+    assert combine_bytes == led["bf16_combine_bytes_per_token_with_weights"]
+
+
+def test_routing_errors_and_unused_slots():
+    topk = np.array([[0, 1], [2, -1], [-1, -1], [3, 3]], np.int64)
+    lay = oracle.layout(2, 2, 4, 2, 2, topk)
+    np.testing.assert_array_equal(lay.dst_slot, [[0, 2], [0, -1], [-1, -1], [2, 3]])
+    np.testing.assert_array_equal(lay.is_token_in_rank, [[1, 0], [0, 1], [0, 0], [0, 1]])
+    np.testing.assert_array_equal(lay.num_expanded, [4, 4])
+    for bad in (4, -2, 1 << 40):
+        t2 = topk.copy()
+        t2[1, 1] = bad
+        with pytest.raises(oracle.OracleError) as ei:
+            oracle.layout(2, 2, 4, 2, 2, t2)
+        assert ei.value.status == oracle.ERR_ROUTING
+
+
+def test_symmetric_windows_only_move_bases():
+    w = small_workload(P=8, S=256, E=32, K=4, A=8, routing="zipf", seed=4)
+    topk = synth.gen_routing(w)
+    a = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    b = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk, symmetric=True)
+    for f in ("dst_slot", "send_head", "expert_offset", "num_expanded", "recv_src_idx", "rank_prefix_matrix"):
+        np.testing.assert_array_equal(getattr(a, f), getattr(b, f))
+    np.testing.assert_array_equal(b.window_row_base, np.arange(w.P + 1) * a.num_expanded.max())
+
+
+@pytest.mark.parametrize("shape", [(1, 50, 4, 3, 4), (4, 0, 8, 2, 4), (3, 17, 3, 1, 1), (4, 33, 64, 8, 5)])
+def test_layout_edge_shapes(shape):
+    P, S, E, K, A = shape
+    rng = np.random.default_rng(sum(shape))
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(P * S)]) if P * S else np.zeros((0, K), np.int64)
+    lay = oracle.layout(P, S, E, K, A, topk)
+    itr, ntpr, ntpe, send_head = brute_force_layout(P, S, E, K, A, topk.astype(np.int64))
+    np.testing.assert_array_equal(lay.is_token_in_rank, itr)
+    np.testing.assert_array_equal(lay.send_head, send_head)
+    n = np.bincount(topk[topk >= 0].ravel(), minlength=E)
+    assert lay.total_rows == int((-(-n // A) * A).sum())
+
+
+# ---------------------------------------------------------------------------
+# dispatch
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("zero_padding", [True, False])
+def test_dispatch_bf16_rows_are_token_copies(zero_padding):
+    w = small_workload(P=4, S=64, E=16, K=3, H=256, A=16, seed=9)
+    topk = synth.gen_routing(w).copy()
+    topk[::13, 2] = -1
+    x = synth.gen_bf16_rows(1, 1, w.T, w.H)
+    wt = synth.gen_weights(w)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    rx, _, rw, meta = oracle.dispatch(lay, w.H, x, wt, False, zero_padding, fill=0xFFFF)
+    El = w.E // w.P
+    covered = np.zeros(lay.total_rows, bool)
+    for u in range(w.T):
+        for j in range(w.K):
+            e = topk[u, j]
+            if e < 0:
+                continue
+            r = lay.window_row_base[e // El] + lay.dst_slot[u, j]
+            np.testing.assert_array_equal(rx[r], x[u])
+            assert rw[r] == wt[u, j] and tuple(meta[r]) == (u, j)
+            covered[r] = True
+    pad = ~covered
+    assert np.all(meta[pad] == -1) and np.all(rw[pad] == 0)
+    assert np.all(rx[pad] == (0 if zero_padding else 0xFFFF))
+    n = np.bincount(topk[topk >= 0], minlength=w.E)
+    assert pad.sum() == int((-(-n // w.A) * w.A - n).sum())
+
+
+def test_quantize_row_scale_codes_and_error_bound():
+    rng = np.random.default_rng(3)
+    H = 1024
+    x = synth.gen_bf16_rows(2, 1, 4, H)
+    x[1, 128:256] = 0  # amax == 0 block
+    x[1, 130] = 0x8000  # -0.0 inside it
+    x[2, 256:384] = torch_bf16_bits(rng.normal(0, 1e-3, 128).astype(np.float32))
+    x[3, 0:128] = torch_bf16_bits((rng.normal(0, 1, 128) * 2.0 ** -120).astype(np.float32))  # tiny
+    for r in range(4):
+        codes, scales = oracle.quantize_row(x[r])
+        xf = bf16_bits_to_f64(x[r]).astype(np.float32)
+        for b in range(H // 128):
+            blk = xf[128 * b:128 * (b + 1)]
+            amax = np.abs(blk).max()
+            assert scales[b].view(np.uint32) == (np.float32(amax) / np.float32(448.0)).view(np.uint32)
+            cb = codes[128 * b:128 * (b + 1)]
+            if amax == 0:
+                np.testing.assert_array_equal(cb, np.where(np.signbit(blk), 0x80, 0x00))
+                continue
+            q = blk / scales[b]  # numpy float32 division (IEEE)
+            np.testing.assert_array_equal(cb, brute_force_e4m3(q))
+            i = int(np.argmax(np.abs(blk)))
+            assert cb[i] == (0xFE if blk[i] < 0 else 0x7E)
+            deq = oracle.e4m3_decode(cb).astype(np.float64) * np.float64(scales[b])
+            err = np.abs(deq - blk.astype(np.float64))
+            normal = np.abs(q) >= 2.0 ** -6
+            assert np.all(err[normal] <= (2.0 ** -4 + 2.0 ** -20) * np.abs(blk.astype(np.float64))[normal])
+            assert np.all(err[~normal] <= (2.0 ** -10 + 2.0 ** -30) * scales[b])
+
+
+def test_dispatch_fp8_rows_and_zero_padding():
+    w = small_workload(P=4, S=32, E=8, K=2, H=384, A=8, seed=12)
+    topk = synth.gen_routing(w)
+    x = synth.gen_bf16_rows(5, 1, w.T, w.H)
+    wt = synth.gen_weights(w)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    rx, sc, rw, meta = oracle.dispatch(lay, w.H, x, wt, True, True, fill=0x7F)
+    El = w.E // w.P
+    for u in range(w.T):
+        codes, scales = oracle.quantize_row(x[u])
+        for j in range(w.K):
+            r = lay.window_row_base[topk[u, j] // El] + lay.dst_slot[u, j]
+            np.testing.assert_array_equal(rx[r], codes)
+            np.testing.assert_array_equal(sc[r], scales)
+    pad = meta[:, 0] < 0
+    assert np.all(rx[pad] == 0) and np.all(sc[pad] == 0)
+    # partial row ranges reproduce the same rows
+    lo, hi = 5, lay.total_rows - 3
+    rx2, sc2, rw2, meta2 = oracle.dispatch(lay, w.H, x, wt, True, True, lo, hi, fill=0x7F)
+    np.testing.assert_array_equal(rx2, rx[lo:hi])
+    np.testing.assert_array_equal(meta2, meta[lo:hi])
+
+
+# ---------------------------------------------------------------------------
+# combine
+# ---------------------------------------------------------------------------
+
+
+def bf16_ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in bf16 units in the last place (monotone integer mapping of the bit patterns)."""
+    def key(h):
+        h = h.astype(np.int32)
+        return np.where(h & 0x8000, 0x8000 - (h & 0x7FFF), 0x8000 + (h & 0x7FFF))
+    return np.abs(key(a) - key(b))
+
+
+def test_combine_unit_weights_is_exact_k_times_x():
+    """With unit weights every valid row carries x[u]; K*x is exact in fp32 for bf16 x and
+    K <= 8, so out == bf16(K_valid * x) bit-exactly whatever the order or fusion."""
+    w = small_workload(P=4, S=64, E=16, K=4, H=256, A=4, seed=21)
+    topk = synth.gen_routing(w).copy()
+    topk[::3, 3] = -1
+    topk[::10] = -1  # tokens with no valid slot combine to +0
+    x = synth.gen_bf16_rows(6, 1, w.T, w.H)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    y, _, _, _ = oracle.dispatch(lay, w.H, x, np.ones((w.T, w.K), np.float32), False, True)
+    out = oracle.combine(lay, w.H, y, None)
+    kv = (topk >= 0).sum(1).astype(np.float64)
+    expect = torch_bf16_bits((bf16_bits_to_f64(x) * kv[:, None]).astype(np.float32))
+    expect[kv == 0] = 0  # no valid slot: the empty sum is +0
+    np.testing.assert_array_equal(out, expect)
+    out_id = oracle.combine_identity(w.K, w.H, False, topk, x, None, 0, w.T)
+    np.testing.assert_array_equal(out_id, expect)
+    assert np.all(out[::10] == 0)
+
+
+def test_combine_general_rows_within_one_ulp_of_exact_sum():
+    w = small_workload(P=4, S=96, E=32, K=8, H=256, A=8, seed=22)
+    topk = synth.gen_routing(w)
+    wt = synth.gen_weights(w)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    y = synth.gen_bf16_rows(7, 4, lay.total_rows, w.H)
+    out = oracle.combine(lay, w.H, y, wt)
+    El = w.E // w.P
+    rows = lay.window_row_base[topk // El] + lay.dst_slot  # [T, K]
+    exact = np.einsum("tk,tkh->th", wt.astype(np.float64), bf16_bits_to_f64(y[rows]))
+    ref = torch_bf16_bits(exact.astype(np.float32))
+    ulp = bf16_ulp_diff(out, ref)
+    assert ulp.max() <= 1
+    assert (ulp == 0).mean() > 0.99
+    # transposed weights (a plausible index slip) must be caught
+    out_bad = oracle.combine(lay, w.H, y, np.ascontiguousarray(wt[:, ::-1]))
+    assert bf16_ulp_diff(out_bad, ref).max() > 1
+
+
+def test_combine_identity_equals_x_times_weight_sum():
+    """combine(dispatch(x)) with identity experts is x * sum(w) within 1 bf16 ulp."""
+    w = small_workload(P=8, S=64, E=64, K=8, H=512, A=16, seed=23)
+    topk = synth.gen_routing(w)
+    wt = synth.gen_weights(w)
+    x = synth.gen_bf16_rows(8, 1, w.T, w.H)
+    out = oracle.combine_identity(w.K, w.H, False, topk, x, wt, 0, w.T)
+    ref = torch_bf16_bits((bf16_bits_to_f64(x) * wt.astype(np.float64).sum(1)[:, None]).astype(np.float32))
+    assert bf16_ulp_diff(out, ref).max() <= 1
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    y, _, _, _ = oracle.dispatch(lay, w.H, x, wt, False, True)
+    np.testing.assert_array_equal(oracle.combine(lay, w.H, y, wt), out)
+
+
+def test_combine_identity_fp8_error_bound():
+    w = small_workload(P=4, S=32, E=16, K=4, H=512, A=8, seed=24)
+    topk = synth.gen_routing(w)
+    wt = synth.gen_weights(w)
+    x = synth.gen_bf16_rows(9, 1, w.T, w.H)
+    out = bf16_bits_to_f64(oracle.combine_identity(w.K, w.H, True, topk, x, wt, 0, w.T))
+    xf = bf16_bits_to_f64(x)
+    sw = wt.astype(np.float64).sum(1)[:, None]
+    # |out - x*sum(w)| <= sum(w)*|x - dequant(x)| + bf16 rounding of the dequant and of the sum
+    bound = sw * (2.0 ** -4 * np.abs(xf) + 2.0 ** -8 * np.abs(xf)) + 2.0 ** -7 * np.abs(xf * sw) + 1e-30
+    scale_floor = np.repeat(np.abs(xf).reshape(w.T, -1, 128).max(2) / 448 * 2.0 ** -9, 128, axis=1)
+    assert np.all(np.abs(out - xf * sw) <= bound + sw * scale_floor)
