@@ -1,0 +1,318 @@
+"""ctypes binding of the C ABI in include/ep_mi355x.h (argument marshalling only)."""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import enum
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libep_mi355x.so"
+EP_ABI_VERSION = 1
+
+# dispatch flags
+_FP8 = 1
+_ZERO_PADDING = 2
+_SYMMETRIC_WINDOWS = 1
+
+
+class Status(enum.IntEnum):
+    OK = 0
+    ERR_NULL = -1
+    ERR_SHAPE = -2
+    ERR_ROUTING = -3
+    ERR_OVERFLOW = -4
+    ERR_HANDLE_MISMATCH = -5
+    ERR_HIP = -6
+    ERR_NOMEM = -7
+
+
+# handle tensor ids -> (name, id, numpy-ish dtype name)
+TENSORS = {
+    "is_token_in_rank": (0, "uint8"),
+    "num_tokens_per_rank": (1, "int32"),
+    "num_tokens_per_expert": (2, "int32"),
+    "rank_prefix_matrix": (3, "int32"),
+    "num_recv_tokens": (4, "int32"),
+    "num_tokens_per_expert_total": (5, "int32"),
+    "expert_offset": (6, "int64"),
+    "num_expanded": (7, "int64"),
+    "window_row_base": (8, "int64"),
+    "dst_slot": (9, "int32"),
+    "send_head": (10, "int32"),
+    "recv_src_idx": (11, "int32"),
+    "recv_src_base": (12, "int64"),
+    "dst_row": (13, "int32"),
+}
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+class EpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        try:
+            name = Status(status).name
+        except ValueError:
+            name = str(status)
+        super().__init__(f"{name}: {message}")
+        self.status = status
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [
+        ("num_ranks", ctypes.c_int32),
+        ("num_tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("num_topk", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("expert_alignment", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    """P virtual ranks x S tokens, hidden H, top-K of E experts, expert_alignment A."""
+
+    P: int
+    S: int
+    H: int
+    K: int
+    E: int
+    A: int
+    symmetric_windows: bool = False
+
+    def _c(self) -> _Config:
+        return _Config(self.P, self.S, self.H, self.K, self.E, self.A,
+                       _SYMMETRIC_WINDOWS if self.symmetric_windows else 0)
+
+    @property
+    def T(self) -> int:
+        return self.P * self.S
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.path.join(PKG, _LIB_NAME)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libep_mi355x.so (built in-tree by build.py); raise if it is not there."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise LibraryMissing(f"{path} is not built; run `python -m combine_topk_idx_expert_amd.build` "
+                                 "or __graft_entry__.build()")
+        L = ctypes.CDLL(path)
+        vp, i32, u32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64
+        L.ep_get_layout.argtypes = [ctypes.POINTER(_Config), vp, vp, ctypes.POINTER(vp), ctypes.POINTER(i64)]
+        L.ep_relayout.argtypes = [vp, vp, vp, ctypes.POINTER(i64)]
+        L.ep_dispatch.argtypes = [vp, u32, vp, vp, vp, vp, vp, vp, vp]
+        L.ep_dispatch_cached.argtypes = [vp, u32, vp, vp, vp, vp]
+        L.ep_combine.argtypes = [vp, vp, vp, vp, vp]
+        L.ep_handle_free.argtypes = [vp]
+        L.ep_handle_free.restype = None
+        L.ep_handle_config.argtypes = [vp, ctypes.POINTER(_Config)]
+        L.ep_handle_check.argtypes = [vp, ctypes.POINTER(_Config)]
+        L.ep_handle_counts.argtypes = [vp, vp, vp, vp]
+        L.ep_handle_tensor.argtypes = [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(i32)]
+        for fn in ("ep_get_layout", "ep_relayout", "ep_dispatch", "ep_dispatch_cached", "ep_combine",
+                   "ep_handle_config", "ep_handle_check", "ep_handle_counts", "ep_handle_tensor"):
+            getattr(L, fn).restype = i32
+        L.ep_last_error.argtypes = []
+        L.ep_last_error.restype = ctypes.c_char_p
+        L.ep_abi_version.argtypes = []
+        L.ep_abi_version.restype = i32
+        if L.ep_abi_version() != EP_ABI_VERSION:
+            raise LibraryMissing(f"{path}: ABI version {L.ep_abi_version()} != {EP_ABI_VERSION}")
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise EpError(status, lib().ep_last_error().decode(errors="replace"))
+
+
+def _stream(device) -> int:
+    import torch
+
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _require(t, dtype, shape, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Handle:
+    """Owns an ep_handle*: the layout of one routing table."""
+
+    def __init__(self, ptr: int, cfg: Config, total_rows: int, device):
+        self._ptr = ptr
+        self.cfg = cfg
+        self.total_rows = total_rows
+        self.device = device
+
+    @property
+    def ptr(self) -> int:
+        if not self._ptr:
+            raise ValueError("handle was freed")
+        return self._ptr
+
+    def free(self) -> None:
+        if self._ptr:
+            lib().ep_handle_free(self._ptr)
+            self._ptr = None
+
+    def __del__(self):  # pragma: no cover - best effort
+        try:
+            self.free()
+        except Exception:
+            pass
+
+    def check(self, cfg: Config) -> None:
+        c = cfg._c()
+        _check(lib().ep_handle_check(self.ptr, ctypes.byref(c)))
+
+    def counts(self):
+        """(num_expanded [P], num_recv_tokens [P], window_row_base [P+1]) as numpy int64."""
+        import numpy as np
+
+        P = self.cfg.P
+        ne, nr, wb = np.zeros(P, np.int64), np.zeros(P, np.int64), np.zeros(P + 1, np.int64)
+        _check(lib().ep_handle_counts(self.ptr, ne.ctypes.data, nr.ctypes.data, wb.ctypes.data))
+        return ne, nr, wb
+
+    def tensor(self, name: str):
+        """A device copy (torch tensor) of one of the handle's arrays."""
+        import torch
+
+        which, dt = TENSORS[name]
+        p, n, b = ctypes.c_void_p(), ctypes.c_int64(), ctypes.c_int32()
+        _check(lib().ep_handle_tensor(self.ptr, which, ctypes.byref(p), ctypes.byref(n), ctypes.byref(b)))
+        out = torch.empty(n.value, dtype=getattr(torch, dt), device=self.device)
+        if n.value:
+            _hip_memcpy_d2d(out.data_ptr(), p.value, n.value * b.value, _stream(self.device))
+        return out
+
+
+_hip = None
+
+
+def _hip_memcpy_d2d(dst: int, src: int, nbytes: int, stream: int) -> None:
+    """Stream-ordered device-to-device copy through the HIP runtime (plumbing)."""
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                        ctypes.c_void_p]
+        _hip.hipMemcpyAsync.restype = ctypes.c_int
+    rc = _hip.hipMemcpyAsync(dst, src, nbytes, 3, stream)  # hipMemcpyDeviceToDevice
+    if rc != 0:
+        raise EpError(Status.ERR_HIP, f"hipMemcpyAsync failed ({rc})")
+
+
+def get_layout(cfg: Config, topk_idx) -> Handle:
+    """ep_get_layout: topk_idx int64 [T, K] on the device -> Handle (synchronizes once)."""
+    import torch
+
+    _require(topk_idx, torch.int64, (cfg.T, cfg.K), "topk_idx")
+    c = cfg._c()
+    h = ctypes.c_void_p()
+    rows = ctypes.c_int64()
+    with torch.cuda.device(topk_idx.device):
+        _check(lib().ep_get_layout(ctypes.byref(c), _ptr(topk_idx), _stream(topk_idx.device), ctypes.byref(h),
+                                   ctypes.byref(rows)))
+    return Handle(h.value, cfg, rows.value, topk_idx.device)
+
+
+def relayout(h: Handle, topk_idx) -> Handle:
+    """ep_relayout: new routing for an existing handle of the same config (no allocation)."""
+    import torch
+
+    _require(topk_idx, torch.int64, (h.cfg.T, h.cfg.K), "topk_idx")
+    rows = ctypes.c_int64()
+    with torch.cuda.device(topk_idx.device):
+        _check(lib().ep_relayout(h.ptr, _ptr(topk_idx), _stream(topk_idx.device), ctypes.byref(rows)))
+    h.total_rows = rows.value
+    return h
+
+
+def _flags(fp8: bool, zero_padding: bool) -> int:
+    return (_FP8 if fp8 else 0) | (_ZERO_PADDING if zero_padding else 0)
+
+
+def _alloc_recv(h: Handle, fp8: bool, device):
+    import torch
+
+    H, R = h.cfg.H, h.total_rows
+    recv_x = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=device)
+    recv_scales = torch.empty((R, H // 128), dtype=torch.float32, device=device) if fp8 else None
+    return recv_x, recv_scales
+
+
+def dispatch(h: Handle, x, topk_weights, fp8: bool = False, zero_padding: bool = False, out=None):
+    """ep_dispatch -> (recv_x, recv_scales | None, recv_weights, recv_src_meta).
+
+    out: optional preallocated (recv_x, recv_scales, recv_weights, recv_src_meta)."""
+    import torch
+
+    cfg = h.cfg
+    _require(x, torch.bfloat16, (cfg.T, cfg.H), "x")
+    _require(topk_weights, torch.float32, (cfg.T, cfg.K), "topk_weights")
+    if out is None:
+        recv_x, recv_scales = _alloc_recv(h, fp8, x.device)
+        recv_w = torch.empty(h.total_rows, dtype=torch.float32, device=x.device)
+        recv_meta = torch.empty((h.total_rows, 2), dtype=torch.int32, device=x.device)
+    else:
+        recv_x, recv_scales, recv_w, recv_meta = out
+    _check(lib().ep_dispatch(h.ptr, _flags(fp8, zero_padding), _ptr(x), _ptr(topk_weights), _ptr(recv_x),
+                             _ptr(recv_scales), _ptr(recv_w), _ptr(recv_meta), _stream(x.device)))
+    return recv_x, recv_scales, recv_w, recv_meta
+
+
+def dispatch_cached(h: Handle, x, fp8: bool = False, zero_padding: bool = False, out=None):
+    """ep_dispatch_cached -> (recv_x, recv_scales | None); out: optional (recv_x, recv_scales)."""
+    import torch
+
+    cfg = h.cfg
+    _require(x, torch.bfloat16, (cfg.T, cfg.H), "x")
+    recv_x, recv_scales = _alloc_recv(h, fp8, x.device) if out is None else out
+    _check(lib().ep_dispatch_cached(h.ptr, _flags(fp8, zero_padding), _ptr(x), _ptr(recv_x), _ptr(recv_scales),
+                                    _stream(x.device)))
+    return recv_x, recv_scales
+
+
+def combine(h: Handle, y, topk_weights=None, out=None):
+    """ep_combine: y bf16 [total_rows, H] -> out bf16 [T, H]."""
+    import torch
+
+    cfg = h.cfg
+    _require(y, torch.bfloat16, (h.total_rows, cfg.H), "y")
+    if topk_weights is not None:
+        _require(topk_weights, torch.float32, (cfg.T, cfg.K), "topk_weights")
+    if out is None:
+        out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=y.device)
+    _check(lib().ep_combine(h.ptr, _ptr(y), _ptr(topk_weights), _ptr(out), _stream(y.device)))
+    return out

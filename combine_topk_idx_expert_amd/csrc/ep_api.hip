@@ -1,0 +1,437 @@
+// ep_api.hip -- host side of the C ABI declared in include/ep_mi355x.h.
+//
+// Validation and status codes follow the pages' host path: missing routing
+// tensors are errors, capacities are computed with checked products, and a
+// cached handle must match the config it is used with ("Ascend DeepEP MoE
+// Dispatch Optimization", sections "Entering the real call chain from the
+// Python interface" and "Host side: building a communication map"; TileLang
+// tutorial ch. 38, section 2.4).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "ep_mi355x.h"
+#include "ep_dispatch.hpp"
+#include "ep_layout.hpp"
+
+using namespace ep;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ep_status fail(ep_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+#define EP_HIP(call)                                                                      \
+  do {                                                                                    \
+    hipError_t e_ = (call);                                                               \
+    if (e_ != hipSuccess) return fail(EP_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+#define EP_LAUNCHED(name)                                                                     \
+  do {                                                                                        \
+    hipError_t e_ = hipGetLastError();                                                        \
+    if (e_ != hipSuccess) return fail(EP_ERR_HIP, "launch of %s: %s", name, hipGetErrorString(e_)); \
+  } while (0)
+
+bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+}  // namespace
+
+struct ep_handle {
+  ep_config cfg;
+  LayoutDims dims;
+  int64_t T;
+  int device;
+  // read back by the layout
+  int64_t total_rows = 0, total_pad = 0, sum_recv = 0;
+  bool valid = false;
+  // device arena and the arrays inside it
+  void* arena = nullptr;
+  size_t arena_bytes = 0;
+  uint8_t* is_token_in_rank;
+  int32_t *num_tokens_per_rank, *num_tokens_per_expert, *rank_prefix_matrix, *num_recv, *n_e;
+  int64_t *expert_offset, *num_expanded, *window_row_base, *recv_src_base;
+  int32_t *dst_slot, *dst_row, *send_head, *recv_src_idx;
+  int32_t *pad_base, *pad_rows, *chunk_hist, *col_total;
+  int64_t* summary_dev;
+  int64_t* summary_host = nullptr;  // pinned
+  hipEvent_t done = nullptr;        // end of the last layout's work
+  size_t lds_count, lds_scan, lds_finalize, lds_rank;
+};
+
+namespace {
+
+ep_status validate_config(const ep_config* c) {
+  if (!c) return fail(EP_ERR_NULL, "config is NULL");
+  if (c->num_ranks < 1 || c->num_ranks > EP_MAX_RANKS)
+    return fail(EP_ERR_SHAPE, "num_ranks %d outside [1, %d]", c->num_ranks, EP_MAX_RANKS);
+  if (c->num_tokens < 0) return fail(EP_ERR_SHAPE, "num_tokens %d < 0", c->num_tokens);
+  if (c->hidden < 8 || c->hidden % 8 != 0)
+    return fail(EP_ERR_SHAPE, "hidden %d must be a positive multiple of 8", c->hidden);
+  if (c->num_topk < 1 || c->num_topk > EP_MAX_TOPK)
+    return fail(EP_ERR_SHAPE, "num_topk %d outside [1, %d]", c->num_topk, EP_MAX_TOPK);
+  if (c->num_experts < c->num_ranks || c->num_experts % c->num_ranks != 0 ||
+      c->num_experts > EP_MAX_EXPERTS)
+    return fail(EP_ERR_SHAPE, "num_experts %d must be a multiple of num_ranks %d, <= %d",
+                c->num_experts, c->num_ranks, EP_MAX_EXPERTS);
+  if (c->expert_alignment < 1) return fail(EP_ERR_SHAPE, "expert_alignment %d < 1", c->expert_alignment);
+  if (c->flags & ~EP_LAYOUT_SYMMETRIC_WINDOWS) return fail(EP_ERR_SHAPE, "unknown layout flags 0x%x", c->flags);
+  const int64_t T = (int64_t)c->num_ranks * c->num_tokens;
+  const int64_t lim = (int64_t)1 << 31;
+  if (T * c->num_topk >= lim) return fail(EP_ERR_OVERFLOW, "T*K = %lld reaches 2^31", (long long)(T * c->num_topk));
+  if (T * c->num_ranks >= lim) return fail(EP_ERR_OVERFLOW, "T*P = %lld reaches 2^31", (long long)(T * c->num_ranks));
+  const int64_t max_rows = T * c->num_topk + (int64_t)c->num_experts * (c->expert_alignment - 1);
+  if (max_rows >= lim) return fail(EP_ERR_OVERFLOW, "expanded rows may reach 2^31 (bound %lld)", (long long)max_rows);
+  return EP_OK;
+}
+
+LayoutDims make_dims(const ep_config& c) {
+  LayoutDims d;
+  d.P = c.num_ranks;
+  d.S = c.num_tokens;
+  d.E = c.num_experts;
+  d.K = c.num_topk;
+  d.A = c.expert_alignment;
+  d.El = d.E / d.P;
+  d.cpr = (d.S + kChunk - 1) / kChunk;
+  d.num_chunks = d.P * d.cpr;
+  d.ncols = d.E + d.P + 1;
+  d.ebits = bits_for((uint32_t)d.E);
+  d.pbits = bits_for((uint32_t)d.P);
+  d.symmetric = (c.flags & EP_LAYOUT_SYMMETRIC_WINDOWS) ? 1 : 0;
+  return d;
+}
+
+ep_status allocate(ep_handle* h) {
+  const LayoutDims& d = h->dims;
+  const int64_t T = h->T, P = d.P, E = d.E, K = d.K;
+  struct Item {
+    void** ptr;
+    size_t bytes;
+  };
+  const int64_t max_pad = E * (d.A - 1);
+  Item items[] = {
+      {(void**)&h->is_token_in_rank, (size_t)(T * P)},
+      {(void**)&h->num_tokens_per_rank, (size_t)(P * P * 4)},
+      {(void**)&h->num_tokens_per_expert, (size_t)(P * E * 4)},
+      {(void**)&h->rank_prefix_matrix, (size_t)(P * P * 4)},
+      {(void**)&h->num_recv, (size_t)(P * 4)},
+      {(void**)&h->n_e, (size_t)(E * 4)},
+      {(void**)&h->expert_offset, (size_t)(P * (d.El + 1) * 8)},
+      {(void**)&h->num_expanded, (size_t)(P * 8)},
+      {(void**)&h->window_row_base, (size_t)((P + 1) * 8)},
+      {(void**)&h->recv_src_base, (size_t)((P + 1) * 8)},
+      {(void**)&h->dst_slot, (size_t)(T * K * 4)},
+      {(void**)&h->dst_row, (size_t)(T * K * 4)},
+      {(void**)&h->send_head, (size_t)(T * P * 4)},
+      {(void**)&h->recv_src_idx, (size_t)(T * std::min<int64_t>(K, P) * 4)},
+      {(void**)&h->pad_base, (size_t)((E + 1) * 4)},
+      {(void**)&h->pad_rows, (size_t)(std::max<int64_t>(max_pad, 1) * 4)},
+      {(void**)&h->chunk_hist, (size_t)((int64_t)d.ncols * d.num_chunks * 4)},
+      {(void**)&h->col_total, (size_t)(d.ncols * 4)},
+      {(void**)&h->summary_dev, (size_t)((kSummaryHeader + 3 * P + 1) * 8)},
+  };
+  size_t total = 0;
+  for (const Item& it : items) total += align_up(std::max<size_t>(it.bytes, 1));
+  hipError_t e = hipMalloc(&h->arena, total);
+  if (e != hipSuccess) return fail(EP_ERR_NOMEM, "hipMalloc(%zu): %s", total, hipGetErrorString(e));
+  h->arena_bytes = total;
+  size_t off = 0;
+  for (const Item& it : items) {
+    *it.ptr = (uint8_t*)h->arena + off;
+    off += align_up(std::max<size_t>(it.bytes, 1));
+  }
+  e = hipHostMalloc((void**)&h->summary_host, (size_t)((kSummaryHeader + 3 * P + 1) * 8), hipHostMallocDefault);
+  if (e != hipSuccess) return fail(EP_ERR_NOMEM, "hipHostMalloc: %s", hipGetErrorString(e));
+  e = hipEventCreateWithFlags(&h->done, hipEventDisableTiming);
+  if (e != hipSuccess) return fail(EP_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+
+  h->lds_count = (size_t)(d.ncols + kChunk * ((d.P + 31) / 32) + kChunk * d.K) * 4;
+  h->lds_scan = (size_t)(((d.P + 1) & ~1) * 4 + (kScanThreads / 64) * 8);
+  h->lds_finalize = (size_t)((d.E + 1) + ((d.E + 2) / 2) + 1 + kFinalizeThreads / 64) * 8;
+  h->lds_rank = (size_t)((d.E + 1) + (d.P + 1) + 2 * kChunk * d.K) * 4;
+  return EP_OK;
+}
+
+void release(ep_handle* h) {
+  if (!h) return;
+  if (h->done) {
+    (void)hipEventSynchronize(h->done);
+    (void)hipEventDestroy(h->done);
+  }
+  if (h->arena) (void)hipFree(h->arena);
+  if (h->summary_host) (void)hipHostFree(h->summary_host);
+  delete h;
+}
+
+// Enqueue the layout for the handle's config and read back the summary.
+ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64_t* total_rows) {
+  h->valid = false;
+  const LayoutDims& d = h->dims;
+  if (d.num_chunks > 0) {
+    layout_count_kernel<<<d.num_chunks, kWave, h->lds_count, s>>>(d, topk_idx, h->is_token_in_rank,
+                                                                   h->chunk_hist);
+    EP_LAUNCHED("layout_count_kernel");
+  }
+  layout_scan_kernel<<<d.ncols, kScanThreads, h->lds_scan, s>>>(
+      d, h->chunk_hist, h->col_total, h->num_tokens_per_expert, h->num_tokens_per_rank,
+      h->rank_prefix_matrix);
+  EP_LAUNCHED("layout_scan_kernel");
+  FinalizeOut fo{h->n_e, h->expert_offset, h->num_expanded, h->window_row_base, h->num_recv,
+                 h->recv_src_base, h->pad_base, h->pad_rows, h->summary_dev};
+  layout_finalize_kernel<<<1, kFinalizeThreads, h->lds_finalize, s>>>(d, h->col_total, fo);
+  EP_LAUNCHED("layout_finalize_kernel");
+  EP_HIP(hipMemcpyAsync(h->summary_host, h->summary_dev, (size_t)(kSummaryHeader + 3 * d.P + 1) * 8,
+                        hipMemcpyDeviceToHost, s));
+  if (d.num_chunks > 0) {
+    RankOut ro{h->dst_slot, h->dst_row, h->send_head, h->recv_src_idx};
+    layout_rank_kernel<<<d.num_chunks, kWave, h->lds_rank, s>>>(d, topk_idx, h->chunk_hist, h->expert_offset,
+                                                                 h->window_row_base, h->recv_src_base, ro);
+    EP_LAUNCHED("layout_rank_kernel");
+  }
+  EP_HIP(hipEventRecord(h->done, s));
+  EP_HIP(hipEventSynchronize(h->done));
+  const int64_t* sm = h->summary_host;
+  if (sm[2] != 0) return fail(EP_ERR_ROUTING, "topk_idx holds an expert id outside {-1} U [0, %d)", d.E);
+  if (sm[0] >= ((int64_t)1 << 31))
+    return fail(EP_ERR_OVERFLOW, "expanded rows %lld reach 2^31 (symmetric windows)", (long long)sm[0]);
+  h->total_rows = sm[0];
+  h->total_pad = sm[1];
+  h->sum_recv = sm[3];
+  h->valid = true;
+  if (total_rows) *total_rows = h->total_rows;
+  return EP_OK;
+}
+
+ep_status check_handle(const ep_handle* h) {
+  if (!h) return fail(EP_ERR_NULL, "handle is NULL");
+  if (!h->valid) return fail(EP_ERR_HANDLE_MISMATCH, "handle holds no valid layout");
+  return EP_OK;
+}
+
+// Largest column tile that still fits: 16-byte chunks per lane.
+int chunks_per_lane(int H) {
+  const int nchunk = H / 8;
+  return (nchunk + kWave - 1) / kWave;
+}
+
+template <bool FP8, bool META>
+ep_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+  const int64_t waves = (int64_t)a.T + a.total_pad;
+  if (waves == 0) return EP_OK;
+  const int blocks = (int)((waves + kRowWaves - 1) / kRowWaves);
+  const int nc = chunks_per_lane(a.H);
+  const int tile = nc <= 1 ? 1 : nc <= 2 ? 2 : nc <= 4 ? 4 : nc <= 8 ? 8 : nc <= 14 ? 14 : 16;
+  switch (tile) {
+    case 1: dispatch_kernel<1, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
+    case 2: dispatch_kernel<2, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
+    case 4: dispatch_kernel<4, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
+    case 8: dispatch_kernel<8, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
+    case 14: dispatch_kernel<14, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
+    default: dispatch_kernel<16, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
+  }
+  EP_LAUNCHED("dispatch_kernel");
+  return EP_OK;
+}
+
+ep_status dispatch_common(const ep_handle* h, uint32_t flags, const void* x, const float* w, void* recv_x,
+                          float* recv_scales, float* recv_weights, int32_t* recv_meta, bool meta,
+                          hipStream_t s) {
+  ep_status st = check_handle(h);
+  if (st != EP_OK) return st;
+  if (flags & ~(uint32_t)(EP_DISPATCH_FP8 | EP_DISPATCH_ZERO_PADDING))
+    return fail(EP_ERR_SHAPE, "unknown dispatch flags 0x%x", flags);
+  const bool fp8 = flags & EP_DISPATCH_FP8;
+  const bool zero_pad = flags & EP_DISPATCH_ZERO_PADDING;
+  if (fp8 && h->cfg.hidden % 128 != 0)
+    return fail(EP_ERR_SHAPE, "fp8 dispatch needs hidden %% 128 == 0 (hidden %d)", h->cfg.hidden);
+  const bool rows = h->total_rows > 0;
+  if (h->T > 0 && !x) return fail(EP_ERR_NULL, "x is NULL");
+  if (rows && !recv_x) return fail(EP_ERR_NULL, "recv_x is NULL");
+  if (rows && fp8 && !recv_scales) return fail(EP_ERR_NULL, "recv_scales is NULL (fp8)");
+  if (meta && h->T > 0 && !w) return fail(EP_ERR_NULL, "topk_weights is NULL");
+  if (meta && rows && (!recv_weights || !recv_meta)) return fail(EP_ERR_NULL, "recv_weights / recv_src_meta is NULL");
+  if (misaligned(x, 16) || misaligned(recv_x, 16) || misaligned(recv_scales, 4) || misaligned(w, 4) ||
+      misaligned(recv_weights, 4) || misaligned(recv_meta, 8))
+    return fail(EP_ERR_SHAPE, "x / recv_x must be 16-byte aligned, fp32 and int32 arrays naturally aligned");
+  DispatchArgs a;
+  a.x = (const uint16_t*)x;
+  a.w = w;
+  a.dst_row = h->dst_row;
+  a.pad_rows = h->pad_rows;
+  a.recv_x = recv_x;
+  a.recv_scales = recv_scales;
+  a.recv_weights = recv_weights;
+  a.recv_meta = recv_meta;
+  a.T = (int)h->T;
+  a.K = h->dims.K;
+  a.H = h->cfg.hidden;
+  a.total_pad = (meta || zero_pad) ? (int)h->total_pad : 0;
+  a.zero_pad = zero_pad ? 1 : 0;
+  if (fp8) return meta ? launch_dispatch<true, true>(a, s) : launch_dispatch<true, false>(a, s);
+  return meta ? launch_dispatch<false, true>(a, s) : launch_dispatch<false, false>(a, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+ep_status ep_get_layout(const ep_config* cfg, const int64_t* topk_idx, void* stream, ep_handle** out,
+                        int64_t* total_rows) {
+  if (!out) return fail(EP_ERR_NULL, "out is NULL");
+  *out = nullptr;
+  ep_status st = validate_config(cfg);
+  if (st != EP_OK) return st;
+  const int64_t T = (int64_t)cfg->num_ranks * cfg->num_tokens;
+  if (T > 0 && !topk_idx) return fail(EP_ERR_NULL, "topk_idx is NULL");
+  if (misaligned(topk_idx, 8)) return fail(EP_ERR_SHAPE, "topk_idx must be 8-byte aligned");
+  ep_handle* h = new ep_handle();
+  h->cfg = *cfg;
+  h->dims = make_dims(*cfg);
+  h->T = T;
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return fail(EP_ERR_HIP, "no HIP device");
+  }
+  st = allocate(h);
+  if (st == EP_OK) st = run_layout(h, topk_idx, (hipStream_t)stream, total_rows);
+  if (st != EP_OK) {
+    const std::string msg = g_last_error;
+    release(h);
+    g_last_error = msg;
+    return st;
+  }
+  *out = h;
+  return EP_OK;
+}
+
+ep_status ep_relayout(ep_handle* h, const int64_t* topk_idx, void* stream, int64_t* total_rows) {
+  if (!h) return fail(EP_ERR_NULL, "handle is NULL");
+  if (h->T > 0 && !topk_idx) return fail(EP_ERR_NULL, "topk_idx is NULL");
+  if (misaligned(topk_idx, 8)) return fail(EP_ERR_SHAPE, "topk_idx must be 8-byte aligned");
+  return run_layout(h, topk_idx, (hipStream_t)stream, total_rows);
+}
+
+ep_status ep_dispatch(const ep_handle* h, uint32_t flags, const void* x, const float* topk_weights,
+                      void* recv_x, float* recv_scales, float* recv_weights, int32_t* recv_src_meta,
+                      void* stream) {
+  return dispatch_common(h, flags, x, topk_weights, recv_x, recv_scales, recv_weights, recv_src_meta, true,
+                         (hipStream_t)stream);
+}
+
+ep_status ep_dispatch_cached(const ep_handle* h, uint32_t flags, const void* x, void* recv_x,
+                             float* recv_scales, void* stream) {
+  return dispatch_common(h, flags, x, nullptr, recv_x, recv_scales, nullptr, nullptr, false,
+                         (hipStream_t)stream);
+}
+
+ep_status ep_combine(const ep_handle* h, const void* y, const float* topk_weights, void* out, void* stream) {
+  ep_status st = check_handle(h);
+  if (st != EP_OK) return st;
+  if (h->T == 0) return EP_OK;
+  if (!out) return fail(EP_ERR_NULL, "out is NULL");
+  if (h->total_rows > 0 && !y) return fail(EP_ERR_NULL, "y is NULL");
+  if (misaligned(y, 16) || misaligned(out, 16) || misaligned(topk_weights, 4))
+    return fail(EP_ERR_SHAPE, "y / out must be 16-byte aligned, topk_weights 4-byte aligned");
+  CombineArgs a{(const uint16_t*)y, topk_weights, h->dst_row, (uint16_t*)out, (int)h->T, h->dims.K,
+                h->cfg.hidden};
+  const int blocks = (int)((h->T + kRowWaves - 1) / kRowWaves);
+  hipStream_t s = (hipStream_t)stream;
+  const int nc = chunks_per_lane(a.H);
+  if (nc <= 1)
+    combine_kernel<1, 4><<<blocks, kRowThreads, 0, s>>>(a);
+  else if (nc <= 2)
+    combine_kernel<2, 4><<<blocks, kRowThreads, 0, s>>>(a);
+  else
+    combine_kernel<4, 4><<<blocks, kRowThreads, 0, s>>>(a);
+  EP_LAUNCHED("combine_kernel");
+  return EP_OK;
+}
+
+void ep_handle_free(ep_handle* h) { release(h); }
+
+ep_status ep_handle_config(const ep_handle* h, ep_config* cfg) {
+  if (!h || !cfg) return fail(EP_ERR_NULL, "NULL argument");
+  *cfg = h->cfg;
+  return EP_OK;
+}
+
+ep_status ep_handle_check(const ep_handle* h, const ep_config* cfg) {
+  if (!h || !cfg) return fail(EP_ERR_NULL, "NULL argument");
+  const ep_config& a = h->cfg;
+  if (a.num_ranks != cfg->num_ranks || a.num_tokens != cfg->num_tokens || a.hidden != cfg->hidden ||
+      a.num_topk != cfg->num_topk || a.num_experts != cfg->num_experts ||
+      a.expert_alignment != cfg->expert_alignment || a.flags != cfg->flags)
+    return fail(EP_ERR_HANDLE_MISMATCH,
+                "handle built for P=%d S=%d H=%d K=%d E=%d A=%d flags=%u, got P=%d S=%d H=%d K=%d E=%d A=%d flags=%u",
+                a.num_ranks, a.num_tokens, a.hidden, a.num_topk, a.num_experts, a.expert_alignment, a.flags,
+                cfg->num_ranks, cfg->num_tokens, cfg->hidden, cfg->num_topk, cfg->num_experts,
+                cfg->expert_alignment, cfg->flags);
+  return EP_OK;
+}
+
+ep_status ep_handle_counts(const ep_handle* h, int64_t* num_expanded, int64_t* num_recv_tokens,
+                           int64_t* window_row_base) {
+  ep_status st = check_handle(h);
+  if (st != EP_OK) return st;
+  const int P = h->dims.P;
+  const int64_t* sm = h->summary_host + kSummaryHeader;
+  if (num_expanded) memcpy(num_expanded, sm, P * 8);
+  if (num_recv_tokens) memcpy(num_recv_tokens, sm + P, P * 8);
+  if (window_row_base) memcpy(window_row_base, sm + 2 * P, (P + 1) * 8);
+  return EP_OK;
+}
+
+ep_status ep_handle_tensor(const ep_handle* h, int32_t which, const void** dev_ptr, int64_t* numel,
+                           int32_t* elem_bytes) {
+  ep_status st = check_handle(h);
+  if (st != EP_OK) return st;
+  if (!dev_ptr || !numel || !elem_bytes) return fail(EP_ERR_NULL, "NULL argument");
+  const int64_t T = h->T, P = h->dims.P, E = h->dims.E, K = h->dims.K, El = h->dims.El;
+  const void* p = nullptr;
+  int64_t n = 0;
+  int32_t b = 4;
+  switch (which) {
+    case EP_T_IS_TOKEN_IN_RANK: p = h->is_token_in_rank; n = T * P; b = 1; break;
+    case EP_T_NUM_TOKENS_PER_RANK: p = h->num_tokens_per_rank; n = P * P; break;
+    case EP_T_NUM_TOKENS_PER_EXPERT: p = h->num_tokens_per_expert; n = P * E; break;
+    case EP_T_RANK_PREFIX_MATRIX: p = h->rank_prefix_matrix; n = P * P; break;
+    case EP_T_NUM_RECV_TOKENS: p = h->num_recv; n = P; break;
+    case EP_T_NUM_TOKENS_PER_EXPERT_TOTAL: p = h->n_e; n = E; break;
+    case EP_T_EXPERT_OFFSET: p = h->expert_offset; n = P * (El + 1); b = 8; break;
+    case EP_T_NUM_EXPANDED: p = h->num_expanded; n = P; b = 8; break;
+    case EP_T_WINDOW_ROW_BASE: p = h->window_row_base; n = P + 1; b = 8; break;
+    case EP_T_DST_SLOT: p = h->dst_slot; n = T * K; break;
+    case EP_T_SEND_HEAD: p = h->send_head; n = T * P; break;
+    case EP_T_RECV_SRC_IDX: p = h->recv_src_idx; n = h->sum_recv; break;
+    case EP_T_RECV_SRC_BASE: p = h->recv_src_base; n = P + 1; b = 8; break;
+    case EP_T_DST_ROW: p = h->dst_row; n = T * K; break;
+    default: return fail(EP_ERR_SHAPE, "unknown tensor id %d", which);
+  }
+  *dev_ptr = p;
+  *numel = n;
+  *elem_bytes = b;
+  return EP_OK;
+}
+
+const char* ep_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ep_abi_version(void) { return EP_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// ep_device.hpp -- wave64 helpers shared by the gfx950 kernels of the
+// MoE dispatch / combine library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// Number of set bits of m in lanes below the calling lane.
+__device__ __forceinline__ int count_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Lanes holding the same key as the calling lane.  gfx950 has no match
+// instruction, so the key is compared bit by bit with one ballot per bit.
+// Every lane of the wave must execute this (uniform control flow).
+__device__ __forceinline__ uint64_t match_any(uint32_t key, int bits) {
+  uint64_t peers = ballot(true);
+  for (int b = 0; b < bits; ++b) {
+    const bool bit = (key >> b) & 1u;
+    const uint64_t m = ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
+
+// Bits needed to represent values 0..n.
+__host__ __device__ inline int bits_for(uint32_t n) {
+  int b = 1;
+  while ((1u << b) <= n) ++b;
+  return b;
+}
+
+template <typename T>
+__device__ __forceinline__ T uniform(T v) {
+  return (T)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+// Maximum over the 16 lanes of a DPP row (rotations by 8, 4, 2, 1 within the
+// row), on the bit patterns of non-negative floats, which order like unsigned
+// integers.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));
+  return v;
+}
+
+// bf16 pair in a 32-bit word -> two floats (bf16 is the upper half of fp32).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo;
+  const __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// float -> OCP FP8 E4M3FN code (bias 7, 3 mantissa bits, no infinity, 0x7F NaN,
+// max finite 448), round to nearest, ties to even.  Magnitudes that round past
+// 448 (above 464), infinities and NaN give 0x7F (with the sign).
+//  - normal range (|q| >= 2^-6): round the fp32 pattern to 3 mantissa bits
+//    (the carry runs into the exponent), then rebias the exponent 127 -> 7;
+//  - below 2^-6 the code is the subnormal multiple round(|q| * 2^9), 0..8
+//    (8 being the smallest normal's code).
+__device__ __forceinline__ uint32_t e4m3_rne(float q) {
+  const uint32_t b = __float_as_uint(q);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7FFFFFFFu;
+  uint32_t nrm = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  nrm = nrm > 0x7Eu ? 0x7Fu : nrm;
+  // (clamped so the unused value stays in range when |q| is large)
+  const uint32_t sub = (uint32_t)__builtin_rintf(fminf(__uint_as_float(a) * 512.0f, 8.0f));
+  return sign | (a >= 0x3C800000u ? nrm : sub);
+}
+
+}  // namespace ep

@@ -1,0 +1,230 @@
+// ep_dispatch.hpp -- dispatch (pack/expand) and combine kernels.
+//
+// Dispatch: every token row of x is read from HBM once and written to each of
+// its K expanded rows (TileLang tutorial ch. 38, sections 2.2 and 4.3: the
+// local copy into the receive buffer; here every virtual rank is local).  With
+// FP8 the row is quantised once per token -- amax per 128 channels, scale =
+// amax / 448, E4M3 codes of x / scale (section 3.6) -- and the codes are
+// written K times.
+//
+// Combine: every token gathers its K expert rows and reduces them in a fixed
+// slot order in fp32, then rounds to bf16 (section 4.5).
+//
+// Work split: one wave per token (source-token partitioning keeps skewed
+// routing balanced: a hot expert means more rows written, not a longer wave).
+// A lane moves 16-byte vectors; a wave step covers 64 x 16 B = 1 KiB of a row.
+#pragma once
+
+#include "ep_device.hpp"
+
+namespace ep {
+
+constexpr int kRowThreads = 256;  // 4 waves per workgroup
+constexpr int kRowWaves = kRowThreads / kWave;
+
+struct DispatchArgs {
+  const uint16_t* x;        // [T][H] bf16
+  const float* w;           // [T][K]           (fresh only)
+  const int32_t* dst_row;   // [T][K] global row, -1 unused
+  const int32_t* pad_rows;  // [total_pad] global rows
+  void* recv_x;             // [rows][H] bf16 | u8
+  float* recv_scales;       // [rows][H/128]    (fp8)
+  float* recv_weights;      // [rows]           (fresh only)
+  int32_t* recv_meta;       // [rows][2]        (fresh only)
+  int T, K, H, total_pad;
+  int zero_pad;
+};
+
+// Wave-uniform global wave index of the calling lane.
+__device__ __forceinline__ int wave_index() {
+  return uniform((int)(blockIdx.x * kRowWaves + (threadIdx.x >> 6)));
+}
+
+// E4M3 codes of 8 bf16 values (packed in v) for one 128-channel block whose
+// scale is `scale` (> 0), little-endian bytes in two words.
+__device__ __forceinline__ u32x2 quantize8(u32x4 v, float scale, bool zero_block) {
+  u32x2 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t pair = v[2 * h + (k >> 1)];
+      const float xf = (k & 1) ? bf16_hi(pair) : bf16_lo(pair);
+      const uint32_t sign = (__float_as_uint(xf) >> 24) & 0x80u;
+      const uint32_t code = zero_block ? sign : e4m3_rne(xf / scale);
+      word |= code << (8 * k);
+    }
+    out[h] = word;
+  }
+  return out;
+}
+
+// NC: 16-byte chunks per lane per column tile (a tile is NC * 1 KiB of bf16).
+template <int NC, bool FP8, bool META>
+__global__ __launch_bounds__(kRowThreads) void dispatch_kernel(DispatchArgs a) {
+  const int gw = wave_index();
+  const int lane = lane_id();
+  const int nchunk = a.H >> 3;  // 16-byte bf16 chunks per row
+  const int64_t out_row_bytes = FP8 ? (int64_t)a.H : (int64_t)a.H * 2;
+  uint8_t* recv = (uint8_t*)a.recv_x;
+
+  if (gw < a.T) {
+    const int u = gw;
+    const u32x4* src = (const u32x4*)(a.x + (int64_t)u * a.H);
+    const int32_t* rows = a.dst_row + (int64_t)u * a.K;
+    for (int tile = 0; tile < nchunk; tile += NC * kWave) {
+      u32x4 v[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int q = tile + c * kWave + lane;
+        v[c] = q < nchunk ? __builtin_nontemporal_load(src + q) : u32x4{0, 0, 0, 0};
+      }
+      if constexpr (!FP8) {
+        for (int j = 0; j < a.K; ++j) {
+          const int row = rows[j];
+          if (row < 0) continue;
+          u32x4* dst = (u32x4*)(recv + (int64_t)row * out_row_bytes);
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const int q = tile + c * kWave + lane;
+            if (q < nchunk) dst[q] = v[c];
+          }
+        }
+      } else {
+        u32x2 codes[NC];
+        float scale[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          uint32_t m = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) m = max(m, max(v[c][k] & 0x7FFFu, (v[c][k] >> 16) & 0x7FFFu));
+          m = row16_max_u32(m);  // one DPP row = 16 lanes = one 128-channel block
+          scale[c] = __uint_as_float(m << 16) / 448.0f;
+          codes[c] = quantize8(v[c], scale[c], m == 0);
+        }
+        const int nblk = a.H >> 7;
+        for (int j = 0; j < a.K; ++j) {
+          const int row = rows[j];
+          if (row < 0) continue;
+          u32x2* dst = (u32x2*)(recv + (int64_t)row * out_row_bytes);
+          float* srow = a.recv_scales + (int64_t)row * nblk;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const int q = tile + c * kWave + lane;
+            if (q < nchunk) {
+              dst[q] = codes[c];
+              if ((lane & 15) == 0) srow[q >> 4] = scale[c];
+            }
+          }
+        }
+      }
+    }
+    if constexpr (META) {
+      if (lane < a.K) {
+        const int row = rows[lane];
+        if (row >= 0) {
+          a.recv_weights[row] = a.w[(int64_t)u * a.K + lane];
+          a.recv_meta[2 * (int64_t)row] = u;
+          a.recv_meta[2 * (int64_t)row + 1] = lane;
+        }
+      }
+    }
+  } else if (gw < a.T + a.total_pad) {
+    const int row = a.pad_rows[gw - a.T];
+    if constexpr (META) {
+      if (lane == 0) {
+        a.recv_weights[row] = 0.0f;
+        a.recv_meta[2 * (int64_t)row] = -1;
+        a.recv_meta[2 * (int64_t)row + 1] = -1;
+      }
+    }
+    if (a.zero_pad) {
+      uint8_t* dst = recv + (int64_t)row * out_row_bytes;
+      const int n16 = (int)(out_row_bytes >> 4);  // H % 8 == 0 -> whole 16-byte chunks
+      for (int q = lane; q < n16; q += kWave) ((u32x4*)dst)[q] = u32x4{0, 0, 0, 0};
+      if constexpr (FP8) {
+        const int nblk = a.H >> 7;
+        for (int b = lane; b < nblk; b += kWave) a.recv_scales[(int64_t)row * nblk + b] = 0.0f;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// combine
+// --------------------------------------------------------------------------
+struct CombineArgs {
+  const uint16_t* y;       // [rows][H] bf16
+  const float* w;          // [T][K] or null (unit weights)
+  const int32_t* dst_row;  // [T][K]
+  uint16_t* out;           // [T][H] bf16
+  int T, K, H;
+};
+
+// NCT: 16-byte chunks per lane per column tile; G: slots whose loads are in
+// flight together.  Accumulation order is always j = 0..K-1.
+template <int NCT, int G>
+__global__ __launch_bounds__(kRowThreads) void combine_kernel(CombineArgs a) {
+#pragma clang fp contract(off)
+  const int u = wave_index();
+  if (u >= a.T) return;
+  const int lane = lane_id();
+  const int nchunk = a.H >> 3;
+  const int32_t* rows = a.dst_row + (int64_t)u * a.K;
+  const float* wrow = a.w ? a.w + (int64_t)u * a.K : nullptr;
+  u32x4* dst = (u32x4*)(a.out + (int64_t)u * a.H);
+
+  for (int tile = 0; tile < nchunk; tile += NCT * kWave) {
+    float acc[NCT][8];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[c][k] = 0.0f;
+
+    for (int j0 = 0; j0 < a.K; j0 += G) {
+      u32x4 v[G][NCT];
+      int row[G];
+      float wj[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int j = j0 + g;
+        row[g] = j < a.K ? rows[j] : -1;
+        wj[g] = (j < a.K && wrow) ? wrow[j] : 1.0f;
+        if (row[g] >= 0) {
+          const u32x4* src = (const u32x4*)(a.y + (int64_t)row[g] * a.H);
+#pragma unroll
+          for (int c = 0; c < NCT; ++c) {
+            const int q = tile + c * kWave + lane;
+            v[g][c] = q < nchunk ? __builtin_nontemporal_load(src + q) : u32x4{0, 0, 0, 0};
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (row[g] < 0) continue;
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float p0 = wj[g] * bf16_lo(v[g][c][k]);
+            const float p1 = wj[g] * bf16_hi(v[g][c][k]);
+            acc[c][2 * k] = acc[c][2 * k] + p0;
+            acc[c][2 * k + 1] = acc[c][2 * k + 1] + p1;
+          }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int q = tile + c * kWave + lane;
+      if (q < nchunk) {
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(acc[c][2 * k], acc[c][2 * k + 1]);
+        dst[q] = o;
+      }
+    }
+  }
+}
+
+}  // namespace ep

@@ -1,0 +1,436 @@
+// ep_layout.hpp -- layout kernels: routing table -> handle arrays.
+//
+// What is computed ("Ascend DeepEP MoE Dispatch Optimization", sections
+// "What the six handle entries store" and "Notify exchanges counts and
+// prefixes first"; TileLang tutorial ch. 38, sections 2.2, 2.4, 3.5):
+// per-rank deduplicated destinations, per-expert / per-rank histograms, their
+// prefix sums, and the deterministic position of every slot and every
+// (token, destination) pair.
+//
+// How (no global atomics, so the result is the same on every run):
+//  1. layout_count  -- one wave per chunk of 64 tokens of one source rank:
+//     expert and rank histograms of the chunk in LDS, is_token_in_rank rows.
+//  2. layout_scan   -- one workgroup per histogram column (E experts + P
+//     ranks): exclusive scan over chunks in order, per-source-rank sums.
+//  3. layout_finalize -- one workgroup: aligned expert sizes, window offsets,
+//     window bases, receive-list bases, padding-row list, host summary.
+//  4. layout_rank   -- one wave per chunk again: walks the chunk's (u, j)
+//     slots 64 at a time in memory order; lanes holding the same expert (or
+//     the same first-seen destination rank) are found with ballots, their
+//     order within the step is their lane order and a per-key running counter
+//     in LDS carries the order across steps.  Seeded with the chunk's scanned
+//     offsets this yields the global stable order by (u, j).
+#pragma once
+
+#include "ep_device.hpp"
+
+namespace ep {
+
+constexpr int kChunk = 64;  // tokens per layout chunk; one wave per chunk
+
+struct LayoutDims {
+  int P, S, E, K, A, El;
+  int cpr;         // chunks per source rank, ceil(S / kChunk)
+  int num_chunks;  // P * cpr
+  int ncols;       // E + P + 1 histogram columns (experts, ranks, bad ids)
+  int ebits;       // bits for expert keys 0..E (E = "no expert")
+  int pbits;       // bits for rank keys 0..P (P = "not a new destination")
+  int symmetric;   // window policy
+};
+
+struct ChunkPos {
+  int c, s, t0, n;
+  int64_t u0;
+};
+
+__device__ __forceinline__ ChunkPos chunk_pos(const LayoutDims& d) {
+  ChunkPos p;
+  p.c = blockIdx.x;
+  p.s = p.c / d.cpr;
+  p.t0 = (p.c % d.cpr) * kChunk;
+  p.n = min(kChunk, d.S - p.t0);
+  p.u0 = (int64_t)p.s * d.S + p.t0;
+  return p;
+}
+
+// Stage the chunk's routing into LDS as int32: expert id, -1 for an unused
+// slot, -2 for an out-of-range id.  Coalesced: the chunk's n*K entries are
+// contiguous in topk_idx.
+__device__ __forceinline__ void stage_chunk_experts(const LayoutDims& d, const ChunkPos& p,
+                                                    const int64_t* __restrict__ topk_idx,
+                                                    int32_t* ex) {
+  const int total = p.n * d.K;
+  const int64_t* src = topk_idx + p.u0 * d.K;
+  for (int i = threadIdx.x; i < total; i += kWave) {
+    const int64_t e = src[i];
+    ex[i] = (e >= 0 && e < d.E) ? (int32_t)e : (e == -1 ? -1 : -2);
+  }
+}
+
+// Exclusive scan over a workgroup of NT threads (NT multiple of 64).
+template <int NT>
+__device__ __forceinline__ int64_t block_excl_scan(int64_t v, int64_t* wsum, int64_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wid] = x;
+  __syncthreads();
+  int64_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int64_t s = wsum[w];
+    before += (w < wid) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+// --------------------------------------------------------------------------
+// 1. counts
+// --------------------------------------------------------------------------
+// LDS: hist[E + P + 1] | rank bit masks [64][ceil(P/32)] | staged experts [64*K]
+// Column E + P counts out-of-range expert ids (a routing error).
+__global__ __launch_bounds__(64) void layout_count_kernel(LayoutDims d,
+                                                          const int64_t* __restrict__ topk_idx,
+                                                          uint8_t* __restrict__ is_token_in_rank,
+                                                          int32_t* __restrict__ chunk_hist) {
+  extern __shared__ int32_t lds[];
+  const int words = (d.P + 31) >> 5;
+  int32_t* hist = lds;
+  uint32_t* rmask = (uint32_t*)(lds + d.ncols);
+  int32_t* ex = lds + d.ncols + kChunk * words;
+  const ChunkPos p = chunk_pos(d);
+  const int lane = threadIdx.x;
+
+  for (int i = lane; i < d.ncols; i += kWave) hist[i] = 0;
+  for (int i = lane; i < kChunk * words; i += kWave) rmask[i] = 0;
+  stage_chunk_experts(d, p, topk_idx, ex);
+  __syncthreads();
+
+  if (lane < p.n) {
+    uint32_t* my = rmask + lane * words;
+    int bad = 0;
+    for (int j = 0; j < d.K; ++j) {
+      const int e = ex[lane * d.K + j];
+      bad += (e == -2);
+      if (e < 0) continue;
+      const int r = e / d.El;
+      atomicAdd(&hist[e], 1);
+      const uint32_t bit = 1u << (r & 31);
+      if (!(my[r >> 5] & bit)) {  // first slot of this token on rank r
+        my[r >> 5] |= bit;
+        atomicAdd(&hist[d.E + r], 1);
+      }
+    }
+    if (bad) atomicAdd(&hist[d.E + d.P], bad);
+  }
+  __syncthreads();
+
+  // is_token_in_rank rows of the chunk: one contiguous byte range.
+  uint8_t* itr = is_token_in_rank + p.u0 * d.P;
+  const int nbytes = p.n * d.P;
+  if ((d.P & 3) == 0) {
+    uint32_t* itr4 = (uint32_t*)itr;  // u0 * P is a multiple of 4
+    for (int wi = lane; wi < (nbytes >> 2); wi += kWave) {
+      const int t = (wi << 2) / d.P, r0 = (wi << 2) - t * d.P;
+      const uint32_t* m = rmask + t * words;
+      uint32_t v = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v |= ((m[(r0 + q) >> 5] >> ((r0 + q) & 31)) & 1u) << (8 * q);
+      itr4[wi] = v;
+    }
+  } else {
+    for (int bi = lane; bi < nbytes; bi += kWave) {
+      const int t = bi / d.P, r = bi - t * d.P;
+      itr[bi] = (uint8_t)((rmask[t * words + (r >> 5)] >> (r & 31)) & 1u);
+    }
+  }
+  for (int col = lane; col < d.ncols; col += kWave)
+    chunk_hist[(int64_t)col * d.num_chunks + p.c] = hist[col];
+}
+
+// --------------------------------------------------------------------------
+// 2. column scans
+// --------------------------------------------------------------------------
+// One workgroup (256 threads) per column.  chunk_hist[col][chunk] becomes the
+// exclusive prefix over chunks.  Per-source-rank sums give
+// num_tokens_per_expert[s][e], num_tokens_per_rank[s][d] and
+// rank_prefix_matrix[s][d] (inclusive over s).
+// LDS: rank_sum[P] | wave sums (int64) [4]
+constexpr int kScanThreads = 256;
+
+__global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
+    LayoutDims d, int32_t* __restrict__ chunk_hist, int32_t* __restrict__ col_total,
+    int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ num_tokens_per_rank,
+    int32_t* __restrict__ rank_prefix_matrix) {
+  extern __shared__ int32_t lds[];
+  int32_t* rank_sum = lds;
+  int64_t* wsum = (int64_t*)(lds + ((d.P + 1) & ~1));
+  const int col = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nc = d.num_chunks;
+  int32_t* v = chunk_hist + (int64_t)col * nc;
+
+  for (int i = tid; i < d.P; i += kScanThreads) rank_sum[i] = 0;
+  __syncthreads();
+
+  int64_t carry = 0;
+  for (int base = 0; base < nc; base += kScanThreads * 4) {
+    int32_t x[4];
+    int64_t tsum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = base + tid * 4 + q;
+      x[q] = i < nc ? v[i] : 0;
+      tsum += x[q];
+      if (i < nc && x[q] != 0) atomicAdd(&rank_sum[i / d.cpr], x[q]);
+    }
+    int64_t tile_total;
+    int64_t run = carry + block_excl_scan<kScanThreads>(tsum, wsum, &tile_total);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = base + tid * 4 + q;
+      if (i < nc) v[i] = (int32_t)run;
+      run += x[q];
+    }
+    carry += tile_total;
+  }
+  if (tid == 0) col_total[col] = (int32_t)carry;
+  __syncthreads();
+
+  if (col < d.E) {
+    for (int s = tid; s < d.P; s += kScanThreads)
+      num_tokens_per_expert[(int64_t)s * d.E + col] = rank_sum[s];
+  } else if (col < d.E + d.P) {
+    const int r = col - d.E;
+    int64_t run = 0;
+    for (int base = 0; base < d.P; base += kScanThreads) {
+      const int s = base + tid;
+      const int64_t val = s < d.P ? rank_sum[s] : 0;
+      int64_t tile_total;
+      const int64_t excl = run + block_excl_scan<kScanThreads>(val, wsum, &tile_total);
+      if (s < d.P) {
+        num_tokens_per_rank[s * d.P + r] = (int32_t)val;
+        rank_prefix_matrix[s * d.P + r] = (int32_t)(excl + val);
+      }
+      run += tile_total;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// 3. finalize
+// --------------------------------------------------------------------------
+// Host summary (int64): [0] total_rows  [1] total_pad  [2] error flag
+// [3] sum of num_recv_tokens (error flag = number of out-of-range ids)  [4, 4+P) num_expanded  [4+P, 4+2P) num_recv_tokens
+// [4+2P, 5+3P) window_row_base.
+constexpr int kSummaryHeader = 4;
+constexpr int kFinalizeThreads = 1024;
+
+struct FinalizeOut {
+  int32_t* n_e;             // [E]
+  int64_t* expert_offset;   // [P][El+1] window-local
+  int64_t* num_expanded;    // [P]
+  int64_t* window_row_base; // [P+1]
+  int32_t* num_recv;        // [P]
+  int64_t* recv_src_base;   // [P+1]
+  int32_t* pad_base;        // [E+1]
+  int32_t* pad_rows;        // [E*(A-1)] capacity
+  int64_t* summary;         // host summary, see above
+};
+
+// LDS: g[E+1] int64 (global prefix of aligned sizes) | pad_base[E+1] int32 | wave sums
+__global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
+    LayoutDims d, const int32_t* __restrict__ col_total, FinalizeOut o) {
+  extern __shared__ int64_t lds64[];
+  int64_t* g = lds64;
+  int32_t* pb = (int32_t*)(lds64 + d.E + 1);
+  int64_t* wsum = lds64 + d.E + 1 + ((d.E + 2) >> 1) + 1;
+  const int tid = threadIdx.x;
+
+  // aligned sizes p_e = ceil(n_e / A) * A and padding p_e - n_e, scanned over e
+  int64_t carry_g = 0, carry_p = 0;
+  for (int base = 0; base < d.E; base += kFinalizeThreads) {
+    const int e = base + tid;
+    const int64_t n = e < d.E ? col_total[e] : 0;
+    const int64_t pe = ((n + d.A - 1) / d.A) * d.A;
+    int64_t tg, tp;
+    const int64_t xg = block_excl_scan<kFinalizeThreads>(pe, wsum, &tg);
+    const int64_t xp = block_excl_scan<kFinalizeThreads>(pe - n, wsum, &tp);
+    if (e < d.E) {
+      g[e] = carry_g + xg;
+      pb[e] = (int32_t)(carry_p + xp);
+      o.n_e[e] = (int32_t)n;
+    }
+    carry_g += tg;
+    carry_p += tp;
+  }
+  if (tid == 0) {
+    g[d.E] = carry_g;
+    pb[d.E] = (int32_t)carry_p;
+  }
+  __syncthreads();
+
+  // window sizes; packed bases are the global prefix at each window's first expert
+  int64_t my_max = 0;
+  for (int r = tid; r < d.P; r += kFinalizeThreads) {
+    const int64_t ne = g[(r + 1) * d.El] - g[r * d.El];
+    o.num_expanded[r] = ne;
+    o.summary[kSummaryHeader + r] = ne;
+    my_max = ne > my_max ? ne : my_max;
+  }
+  for (int e = tid; e <= d.E; e += kFinalizeThreads) o.pad_base[e] = pb[e];
+  // max over the workgroup (symmetric windows)
+  for (int off = 32; off > 0; off >>= 1) {
+    const int64_t y = __shfl_xor(my_max, off, 64);
+    my_max = y > my_max ? y : my_max;
+  }
+  if ((tid & 63) == 0) wsum[tid >> 6] = my_max;
+  __syncthreads();
+  int64_t wmax = 0;
+  for (int w = 0; w < kFinalizeThreads / 64; ++w) wmax = wsum[w] > wmax ? wsum[w] : wmax;
+  __syncthreads();
+
+  for (int r = tid; r <= d.P; r += kFinalizeThreads) {
+    const int64_t base = d.symmetric ? (int64_t)r * wmax : g[min(r, d.P) * d.El];
+    o.window_row_base[r] = base;
+    o.summary[kSummaryHeader + 2 * d.P + r] = base;
+  }
+  for (int x = tid; x < d.P * (d.El + 1); x += kFinalizeThreads) {
+    const int r = x / (d.El + 1), l = x - r * (d.El + 1);
+    o.expert_offset[x] = g[r * d.El + l] - g[r * d.El];
+  }
+
+  // receive-list bases
+  int64_t carry_r = 0;
+  for (int base = 0; base < d.P; base += kFinalizeThreads) {
+    const int r = base + tid;
+    const int64_t nr = r < d.P ? col_total[d.E + r] : 0;
+    int64_t tr;
+    const int64_t xr = block_excl_scan<kFinalizeThreads>(nr, wsum, &tr);
+    if (r < d.P) {
+      o.num_recv[r] = (int32_t)nr;
+      o.recv_src_base[r] = carry_r + xr;
+      o.summary[kSummaryHeader + d.P + r] = nr;
+    }
+    carry_r += tr;
+  }
+  if (tid == 0) {
+    o.recv_src_base[d.P] = carry_r;
+    o.summary[0] = d.symmetric ? (int64_t)d.P * wmax : g[d.E];
+    o.summary[1] = pb[d.E];
+    o.summary[2] = col_total[d.E + d.P];
+    o.summary[3] = carry_r;
+  }
+
+  // padding rows, as global row indices, expert-major
+  const int total_pad = pb[d.E];
+  for (int i = tid; i < total_pad; i += kFinalizeThreads) {
+    int lo = 0, hi = d.E;  // last e with pb[e] <= i
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pb[mid] <= i) lo = mid; else hi = mid;
+    }
+    const int e = lo, r = e / d.El;
+    const int64_t first_pad = (d.symmetric ? (int64_t)r * wmax : g[r * d.El]) + (g[e] - g[r * d.El]) +
+                              col_total[e];
+    o.pad_rows[i] = (int32_t)(first_pad + (i - pb[e]));
+  }
+}
+
+// --------------------------------------------------------------------------
+// 4. stable ranks
+// --------------------------------------------------------------------------
+struct RankOut {
+  int32_t* dst_slot;      // [T][K]
+  int32_t* dst_row;       // [T][K]
+  int32_t* send_head;     // [T][P]
+  int32_t* recv_src_idx;  // [sum num_recv]
+};
+
+// LDS: cnt_e[E+1] | cnt_r[P+1] | staged experts [64*K] | send positions [64*K]
+__global__ __launch_bounds__(64) void layout_rank_kernel(
+    LayoutDims d, const int64_t* __restrict__ topk_idx, const int32_t* __restrict__ chunk_excl,
+    const int64_t* __restrict__ expert_offset, const int64_t* __restrict__ window_row_base,
+    const int64_t* __restrict__ recv_src_base, RankOut o) {
+  extern __shared__ int32_t lds[];
+  int32_t* cnt_e = lds;
+  int32_t* cnt_r = lds + d.E + 1;
+  int32_t* ex = cnt_r + d.P + 1;
+  int32_t* pos = ex + kChunk * d.K;
+  const ChunkPos p = chunk_pos(d);
+  const int lane = threadIdx.x;
+
+  for (int i = lane; i < d.E; i += kWave) cnt_e[i] = chunk_excl[(int64_t)i * d.num_chunks + p.c];
+  for (int i = lane; i < d.P; i += kWave)
+    cnt_r[i] = chunk_excl[(int64_t)(d.E + i) * d.num_chunks + p.c];
+  if (lane == 0) {
+    cnt_e[d.E] = 0;
+    cnt_r[d.P] = 0;
+  }
+  stage_chunk_experts(d, p, topk_idx, ex);
+  __syncthreads();
+
+  const int total = p.n * d.K;
+  for (int base = 0; base < total; base += kWave) {  // uniform trip count
+    const int i = base + lane;
+    const bool in = i < total;
+    const int e = in ? ex[i] : -1;
+    const int t = i / d.K, j = i - t * d.K;
+    const int r = e >= 0 ? e / d.El : d.P;
+    bool first = e >= 0;  // first slot of token t on rank r
+    if (e >= 0) {         // (only lanes holding a slot read the token's earlier slots)
+      for (int jj = 0; jj < j; ++jj) {
+        const int e2 = ex[t * d.K + jj];
+        first &= !(e2 >= 0 && e2 / d.El == r);
+      }
+    }
+    const uint32_t key_e = e >= 0 ? (uint32_t)e : (uint32_t)d.E;
+    const uint32_t key_r = first ? (uint32_t)r : (uint32_t)d.P;
+    const uint64_t pe = match_any(key_e, d.ebits);
+    const uint64_t pr = match_any(key_r, d.pbits);
+    const int be = cnt_e[key_e], br = cnt_r[key_r];
+    __builtin_amdgcn_wave_barrier();
+    if (lane == 63 - __builtin_clzll(pe)) cnt_e[key_e] = be + __builtin_popcountll(pe);
+    if (lane == 63 - __builtin_clzll(pr)) cnt_r[key_r] = br + __builtin_popcountll(pr);
+    __builtin_amdgcn_wave_barrier();
+    if (in) {
+      const int64_t u = p.u0 + t;
+      if (e >= 0) {
+        const int64_t slot = expert_offset[(int64_t)r * (d.El + 1) + (e - r * d.El)] + be + count_below(pe);
+        o.dst_slot[u * d.K + j] = (int32_t)slot;
+        o.dst_row[u * d.K + j] = (int32_t)(window_row_base[r] + slot);
+      } else {
+        o.dst_slot[u * d.K + j] = -1;
+        o.dst_row[u * d.K + j] = -1;
+      }
+      int32_t sh = -1;
+      if (first) {
+        sh = br + count_below(pr);
+        o.recv_src_idx[recv_src_base[r] + sh] = p.t0 + t;
+      }
+      pos[i] = sh;
+    }
+  }
+  __syncthreads();
+
+  // send_head rows of the chunk: one contiguous int32 range, -1 where not sent
+  int32_t* out = o.send_head + p.u0 * d.P;
+  for (int q = lane; q < p.n * d.P; q += kWave) {
+    const int t = q / d.P, r = q - t * d.P;
+    int32_t v = -1;
+    for (int j = 0; j < d.K; ++j) {
+      const int e = ex[t * d.K + j];
+      if (e >= 0 && e / d.El == r && pos[t * d.K + j] >= 0) v = pos[t * d.K + j];
+    }
+    out[q] = v;
+  }
+}
+
+}  // namespace ep

@@ -1,0 +1,232 @@
+/*
+ * ep_mi355x.h -- C ABI of the single-GPU MoE dispatch / combine path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method: dispatch is a routing-driven All-to-AllV that copies each token
+ * row to every expert-parallel (EP) rank holding one of its top-k experts and
+ * lays the rows out grouped by expert; combine is its inverse, gathering the
+ * k expert outputs of each token and reducing them with the top-k weights.
+ * ("Ascend DeepEP MoE Dispatch Optimization", section "A token's journey
+ * through MoE"; TileLang tutorial ch. 38 "DeepEP-Ascend", sections 2.1-2.2.)
+ *
+ * Here the P expert-parallel ranks are *virtual*: each rank's receive buffer
+ * is a window (a range of rows) of one expanded tensor in one GPU's HBM, and
+ * the remote Put of the multi-device method becomes a coalesced HBM store,
+ * ordered by the HIP stream.  No flags, no collectives.
+ *
+ * Conventions shared by every call
+ *  - Every tensor argument is a DEVICE pointer to row-major, contiguous memory
+ *    that the caller allocated and owns; the library never allocates a tensor
+ *    that the caller sees and never keeps a caller pointer after returning.
+ *    bf16 / fp8 row tensors (x, recv_x, y, out) must be 16-byte aligned, other
+ *    arrays aligned to their element size (else EP_ERR_SHAPE).
+ *  - `stream` is a hipStream_t (0 = the null stream).  All device work of a
+ *    call is enqueued on it; calls other than ep_get_layout / ep_relayout
+ *    return without waiting for it.
+ *  - Token u = s * S + t is token t of virtual rank s (the tutorial's source
+ *    token global index, section 2.1); T = P * S.
+ *  - Expert e lives on rank e / E_l, E_l = E / P (contiguous blocks; the
+ *    tutorial's EP8 example, section 7.2: 256 experts / 8 ranks = 32 local).
+ *  - topk_idx[u][j] == -1 marks an unused slot: it is skipped everywhere.  Any
+ *    other value outside [0, E) is a routing error.
+ *  - A non-OK status leaves outputs unspecified; validation errors return
+ *    before anything is enqueued.  ep_last_error() gives a message.
+ *  - One handle may be used by any number of ep_dispatch_cached / ep_combine
+ *    calls; ep_handle_free and ep_relayout require that none is in flight.
+ */
+#ifndef EP_MI355X_H
+#define EP_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EP_ABI_VERSION 1
+
+/* Limits of this build. */
+#define EP_MAX_RANKS 1024
+#define EP_MAX_EXPERTS 4096
+#define EP_MAX_TOPK 32
+
+typedef enum {
+  EP_OK = 0,
+  EP_ERR_NULL = -1,            /* a required pointer is NULL                              */
+  EP_ERR_SHAPE = -2,           /* bad sizes: H % 8, (fp8) H % 128, E % P, K, A, limits    */
+  EP_ERR_ROUTING = -3,         /* topk_idx outside {-1} U [0, E) (detected on the device) */
+  EP_ERR_OVERFLOW = -4,        /* T*K, T*P or the expanded row count reach 2^31           */
+  EP_ERR_HANDLE_MISMATCH = -5, /* config differs from the one the handle was built for    */
+  EP_ERR_HIP = -6,             /* a HIP runtime call or kernel launch failed              */
+  EP_ERR_NOMEM = -7            /* device or pinned host allocation failed                 */
+} ep_status;
+
+/* Layout-level flags (ep_config.flags). */
+#define EP_LAYOUT_SYMMETRIC_WINDOWS 1u /* every window gets max_d num_expanded rows     */
+
+/* Per-call dispatch flags. */
+#define EP_DISPATCH_FP8 1u          /* emit E4M3 codes + fp32 scales per 128 channels  */
+#define EP_DISPATCH_ZERO_PADDING 2u /* zero the alignment padding rows' payload         */
+
+/* Shape of one dispatch/combine problem.  The tutorial's EPBuffer is built for
+ * a token capacity, hidden size and top-k, and dispatch takes num_experts and
+ * expert_alignment (TileLang tutorial ch. 38, sections 3.1 and 3.3). */
+typedef struct {
+  int32_t num_ranks;        /* P, virtual EP ranks, 1..EP_MAX_RANKS                     */
+  int32_t num_tokens;       /* S, tokens per rank, >= 0                                  */
+  int32_t hidden;           /* H, multiple of 8 (16-byte bf16 vectors)                   */
+  int32_t num_topk;         /* K, 1..EP_MAX_TOPK                                         */
+  int32_t num_experts;      /* E, multiple of P, <= EP_MAX_EXPERTS                       */
+  int32_t expert_alignment; /* A >= 1: every expert's row count is padded to a multiple  */
+  uint32_t flags;           /* EP_LAYOUT_* bits                                          */
+} ep_config;
+
+typedef struct ep_handle ep_handle; /* opaque; owns its device arrays */
+
+/* --------------------------------------------------------------------------
+ * ep_get_layout -- plan a fresh dispatch ("Ascend DeepEP MoE Dispatch
+ * Optimization", sections "Notify exchanges counts and prefixes first" and
+ * "What the six handle entries store"; TileLang tutorial ch. 38, sections 2.2,
+ * 2.4 and 3.5).
+ *
+ *   topk_idx  device, int64 [T, K]; read during the call only (the handle
+ *             keeps what it needs, so later writes to topk_idx are harmless).
+ *   out       receives a new handle (NULL on error); free with ep_handle_free.
+ *   total_rows  host, receives the row count the caller must allocate for the
+ *             expanded tensors (recv_x, recv_scales, recv_weights,
+ *             recv_src_meta, and the combine input y).  May be NULL.
+ *
+ * Computes on the device, deterministically (no global atomics):
+ *   is_token_in_rank [T,P] u8, num_tokens_per_rank [P,P], num_tokens_per_expert
+ *   [P,E], rank_prefix_matrix [P,P] (inclusive over source ranks),
+ *   num_recv_tokens [P], aligned per-expert row offsets, num_expanded [P]
+ *   (= sum_e ceil(n_e/A)*A over the rank's experts), window row bases,
+ *   dst_slot [T,K] (window-local row of each slot, -1 if unused), send_head
+ *   [T,P] (position in the destination's receive list, -1 if not sent) and
+ *   recv_src_idx (per destination, the local token index of each received
+ *   token).  Receive lists are ordered by source rank then token; the rows of
+ *   one expert are ordered by (u, j) -- the tutorial's deterministic order.
+ * Allocates the handle's device memory (hipMalloc) and synchronizes `stream`
+ * once to read back the per-window row counts (the pages' do_cpu_sync mode).
+ * Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_OVERFLOW, EP_ERR_ROUTING,
+ * EP_ERR_NOMEM, EP_ERR_HIP.
+ */
+ep_status ep_get_layout(const ep_config *cfg, const int64_t *topk_idx, void *stream,
+                        ep_handle **out, int64_t *total_rows);
+
+/* ep_relayout -- ep_get_layout into an existing handle for a new topk_idx of
+ * the same config, without allocating (one long-lived buffer reused across
+ * layers, TileLang tutorial ch. 38, section 2.6).  No call using `h` may be
+ * in flight.  On error the handle's layout is invalid until a successful
+ * ep_relayout. */
+ep_status ep_relayout(ep_handle *h, const int64_t *topk_idx, void *stream, int64_t *total_rows);
+
+/* --------------------------------------------------------------------------
+ * ep_dispatch -- fresh dispatch into the expanded, expert-grouped layout
+ * (TileLang tutorial ch. 38, sections 2.1, 2.2, 3.6 and 4.3).
+ *
+ *   x             device, bf16 [T, H].
+ *   topk_weights  device, fp32 [T, K].
+ *   recv_x        device, [total_rows, H]: bf16, or E4M3 bytes with EP_DISPATCH_FP8.
+ *   recv_scales   device, fp32 [total_rows, H/128] row-major; required with
+ *                 EP_DISPATCH_FP8 (H % 128 == 0), ignored otherwise.
+ *   recv_weights  device, fp32 [total_rows].
+ *   recv_src_meta device, int32 [total_rows, 2]: (u, j) of the slot a row came
+ *                 from ((-1, -1) for padding rows).
+ * Row r = window_row_base[rank(e)] + dst_slot[u][j] of every valid slot gets
+ * x[u] (bf16 copy, or its E4M3 codes: scale = amax/448 per 128-channel block
+ * in fp32, code = E4M3FN round-to-nearest-even of x/scale; a block with amax 0
+ * has scale 0 and signed-zero codes), recv_weights = topk_weights[u][j] and
+ * recv_src_meta = (u, j).  Padding rows get weight 0, meta (-1, -1) and, with
+ * EP_DISPATCH_ZERO_PADDING, a zero payload (and zero scales); otherwise their
+ * payload is left as it was ("Ascend DeepEP MoE Dispatch Optimization",
+ * section "Output length has a dynamic and a fixed mode"; tutorial 2.2).
+ * Rows past num_expanded in symmetric windows are not touched.
+ * Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_HIP.
+ */
+ep_status ep_dispatch(const ep_handle *h, uint32_t flags, const void *x, const float *topk_weights,
+                      void *recv_x, float *recv_scales, float *recv_weights,
+                      int32_t *recv_src_meta, void *stream);
+
+/* ep_dispatch_cached -- dispatch with a cached handle: the same routing, new
+ * x; only the payload (and fp8 scales) move, padding is re-zeroed when asked
+ * ("Ascend DeepEP MoE Dispatch Optimization", section "Entering the real call
+ * chain from the Python interface", cached dispatch; tutorial 2.4).  Its
+ * payload equals ep_dispatch's for the same x and flags. */
+ep_status ep_dispatch_cached(const ep_handle *h, uint32_t flags, const void *x, void *recv_x,
+                             float *recv_scales, void *stream);
+
+/* --------------------------------------------------------------------------
+ * ep_combine -- weighted reduction of the K expert rows of every token back
+ * to token order (TileLang tutorial ch. 38, sections 2.1, 3.6(5) and 4.5).
+ *
+ *   y             device, bf16 [total_rows, H] (expert outputs; padding rows
+ *                 are never read).
+ *   topk_weights  device, fp32 [T, K], or NULL for unit weights.
+ *   out           device, bf16 [T, H].
+ * out[u][h] = bf16_rne(acc) with acc = +0 and, for j = 0..K-1 over valid
+ * slots in order, acc = fl(acc + fl(w[u][j] * float(y[row(u,j)][h]))) in fp32
+ * (no fused multiply-add).  A token without valid slots gets +0.
+ * The backward of dispatch is this call and the backward of combine is
+ * ep_dispatch_cached, with the same handle (tutorial 2.3).
+ * Errors: EP_ERR_NULL, EP_ERR_HIP.
+ */
+ep_status ep_combine(const ep_handle *h, const void *y, const float *topk_weights, void *out,
+                     void *stream);
+
+/* ep_handle_free -- waits for the handle's own layout work, then releases its
+ * device and pinned host memory.  The caller guarantees no other call using
+ * `h` is still in flight (tutorial 2.6).  NULL is a no-op. */
+void ep_handle_free(ep_handle *h);
+
+/* --------------------------------------------------------------------------
+ * Introspection (host-side, no device work).
+ */
+
+/* Config the handle was built with. */
+ep_status ep_handle_config(const ep_handle *h, ep_config *cfg);
+
+/* EP_ERR_HANDLE_MISMATCH unless cfg's shape fields and flags equal the
+ * handle's (the tutorial's cached-handle check of num_experts,
+ * expert_alignment and token capacity, section 2.4). */
+ep_status ep_handle_check(const ep_handle *h, const ep_config *cfg);
+
+/* Host copies of the read-back counts: num_expanded [P], num_recv_tokens [P],
+ * window_row_base [P+1] (int64).  Any pointer may be NULL. */
+ep_status ep_handle_counts(const ep_handle *h, int64_t *num_expanded, int64_t *num_recv_tokens,
+                           int64_t *window_row_base);
+
+/* Device arrays of the handle, for parity checks and for callers that want
+ * the pages' handle tensors.  The pointer stays valid until ep_handle_free /
+ * ep_relayout; the caller must not write through it. */
+enum {
+  EP_T_IS_TOKEN_IN_RANK = 0,      /* u8  [T, P]                                       */
+  EP_T_NUM_TOKENS_PER_RANK = 1,   /* i32 [P, P]   [source][destination]               */
+  EP_T_NUM_TOKENS_PER_EXPERT = 2, /* i32 [P, E]   [source][expert]                    */
+  EP_T_RANK_PREFIX_MATRIX = 3,    /* i32 [P, P]   inclusive over source ranks         */
+  EP_T_NUM_RECV_TOKENS = 4,       /* i32 [P]                                          */
+  EP_T_NUM_TOKENS_PER_EXPERT_TOTAL = 5, /* i32 [E]                                    */
+  EP_T_EXPERT_OFFSET = 6,         /* i64 [P, E_l + 1] window-local, multiples of A    */
+  EP_T_NUM_EXPANDED = 7,          /* i64 [P]                                          */
+  EP_T_WINDOW_ROW_BASE = 8,       /* i64 [P + 1]                                      */
+  EP_T_DST_SLOT = 9,              /* i32 [T, K]   window-local row, -1 if unused      */
+  EP_T_SEND_HEAD = 10,            /* i32 [T, P]   receive-list position, -1 if unsent */
+  EP_T_RECV_SRC_IDX = 11,         /* i32 [sum num_recv_tokens], destination-major     */
+  EP_T_RECV_SRC_BASE = 12,        /* i64 [P + 1]  start of each destination's list    */
+  EP_T_DST_ROW = 13,              /* i32 [T, K]   global row (window base + dst_slot) */
+  EP_T_COUNT = 14
+};
+ep_status ep_handle_tensor(const ep_handle *h, int32_t which, const void **dev_ptr, int64_t *numel,
+                           int32_t *elem_bytes);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char *ep_last_error(void);
+
+/* EP_ABI_VERSION of the loaded library. */
+int32_t ep_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_MI355X_H */

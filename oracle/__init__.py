@@ -154,13 +154,15 @@ def dispatch(lay: Layout, H: int, x: np.ndarray, topk_weights: np.ndarray | None
              with_meta: bool = True, fill: int = 0):
     """Expanded rows [row_begin, row_end) -> (recv_x, recv_scales, recv_weights, recv_src_meta).
 
-    Rows the method leaves untouched keep ``fill`` (payload) / NaN-free zeros (metadata)."""
+    Rows the method leaves untouched keep ``fill`` (payload) / zeros (metadata).
+    Passing ``x=None`` computes the row metadata only (recv_x and recv_scales are None)."""
     if row_end is None:
         row_end = lay.total_rows
     n = row_end - row_begin
-    x = np.ascontiguousarray(x, dtype=np.uint16).reshape(lay.T, H)
-    recv_x = np.full((n, H), fill, np.uint8 if fp8 else np.uint16)
-    recv_scales = np.zeros((n, H // 128), np.float32) if fp8 else None
+    payload = x is not None
+    x = np.zeros((0,), np.uint16) if x is None else np.ascontiguousarray(x, dtype=np.uint16).reshape(lay.T, H)
+    recv_x = np.full((n, H), fill, np.uint8 if fp8 else np.uint16) if payload else None
+    recv_scales = np.zeros((n, H // 128), np.float32) if (fp8 and payload) else None
     recv_w = np.zeros(n, np.float32) if with_meta else None
     recv_meta = np.zeros((n, 2), np.int32) if with_meta else None
     w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)

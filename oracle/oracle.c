@@ -291,7 +291,8 @@ void oracle_quantize_row(const uint16_t *x, int H, uint8_t *codes, float *scales
  *
  * Output arrays hold only rows [row_begin, row_end): element (r, h) is at
  * (r - row_begin) * H + h.  recv_weights / recv_src_meta may be NULL (cached
- * dispatch moves payload only).  recv_scales is used only when fp8. */
+ * dispatch moves payload only); recv_x may be NULL (metadata only).
+ * recv_scales is used only when fp8. */
 int oracle_dispatch(int P, int S, int E, int K, int H, int A, int fp8, int zero_padding,
                     const int64_t *topk_idx, const int32_t *dst_slot,
                     const int32_t *num_tokens_per_expert_total, const int64_t *expert_offset,
@@ -316,7 +317,9 @@ int oracle_dispatch(int P, int S, int E, int K, int H, int A, int fp8, int zero_
       int64_t r = window_row_base[e / El] + dst_slot[u * K + j];
       if (r < row_begin || r >= row_end) continue;
       int64_t rr = r - row_begin;
-      if (fp8) {
+      if (!recv_x) {
+        /* metadata only */
+      } else if (fp8) {
         oracle_quantize_row(x + u * H, H, codes, scales);
         memcpy((uint8_t *)recv_x + rr * H, codes, (size_t)H);
         memcpy(recv_scales + rr * nb, scales, sizeof(float) * (size_t)nb);
@@ -344,7 +347,7 @@ int oracle_dispatch(int P, int S, int E, int K, int H, int A, int fp8, int zero_
         recv_src_meta[2 * rr] = -1;
         recv_src_meta[2 * rr + 1] = -1;
       }
-      if (zero_padding) {
+      if (zero_padding && recv_x) {
         if (fp8) {
           memset((uint8_t *)recv_x + rr * H, 0, (size_t)H);
           for (int b = 0; b < nb; b++) recv_scales[rr * nb + b] = 0.0f;

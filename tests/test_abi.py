@@ -1,0 +1,109 @@
+"""The C-ABI library loads and exports what include/ep_mi355x.h declares; host-side
+validation rejects bad configs with the documented status codes before any device
+work.  CPU only: nothing here launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_topk_idx_expert_amd as ep
+from combine_topk_idx_expert_amd._native import _Config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep_mi355x.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ep.lib_path()):
+        import combine_topk_idx_expert_amd.build as b
+
+        b.build()
+    return ep.lib()
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for fn in ("ep_get_layout", "ep_dispatch", "ep_dispatch_cached", "ep_combine", "ep_handle_free"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    missing = [fn for fn in declared_functions() if not hasattr(L, fn)]
+    assert not missing, missing
+    assert L.ep_abi_version() == ep.EP_ABI_VERSION
+
+
+def test_library_has_gfx950_code_object():
+    data = open(ep.lib_path(), "rb").read()
+    assert b"gfx950" in data
+
+
+def _layout_status(L, cfg: _Config, topk_ptr=1):
+    h = ctypes.c_void_p(123)
+    rows = ctypes.c_int64(-1)
+    st = L.ep_get_layout(ctypes.byref(cfg), ctypes.c_void_p(topk_ptr), None, ctypes.byref(h), ctypes.byref(rows))
+    return st, h.value
+
+
+GOOD = dict(num_ranks=8, num_tokens=4096, hidden=7168, num_topk=8, num_experts=256, expert_alignment=128, flags=0)
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(num_ranks=0), ep.Status.ERR_SHAPE),
+    (dict(num_ranks=2000, num_experts=4000), ep.Status.ERR_SHAPE),
+    (dict(num_tokens=-1), ep.Status.ERR_SHAPE),
+    (dict(hidden=7170), ep.Status.ERR_SHAPE),
+    (dict(hidden=0), ep.Status.ERR_SHAPE),
+    (dict(num_topk=0), ep.Status.ERR_SHAPE),
+    (dict(num_topk=33), ep.Status.ERR_SHAPE),
+    (dict(num_experts=250), ep.Status.ERR_SHAPE),
+    (dict(num_experts=4), ep.Status.ERR_SHAPE),
+    (dict(num_experts=8192), ep.Status.ERR_SHAPE),
+    (dict(expert_alignment=0), ep.Status.ERR_SHAPE),
+    (dict(flags=8), ep.Status.ERR_SHAPE),
+    (dict(num_ranks=8, num_tokens=1 << 28), ep.Status.ERR_OVERFLOW),       # T*K >= 2^31
+    (dict(num_ranks=1024, num_experts=1024, num_topk=1, num_tokens=1 << 21), ep.Status.ERR_OVERFLOW),  # T*P
+    (dict(num_tokens=(1 << 31) // 64 - 100, num_topk=8), ep.Status.ERR_OVERFLOW),
+])
+def test_validation_errors(L, change, status):
+    cfg = _Config(**{**GOOD, **change})
+    st, h = _layout_status(L, cfg)
+    assert st == status, (st, L.ep_last_error())
+    assert h is None  # *out is cleared on error
+    assert L.ep_last_error()
+
+
+def test_null_arguments(L):
+    cfg = _Config(**GOOD)
+    st, _ = _layout_status(L, cfg, topk_ptr=0)
+    assert st == ep.Status.ERR_NULL
+    assert L.ep_get_layout(None, None, None, ctypes.byref(ctypes.c_void_p()), None) == ep.Status.ERR_NULL
+    assert L.ep_get_layout(ctypes.byref(cfg), ctypes.c_void_p(1), None, None, None) == ep.Status.ERR_NULL
+    for call in (lambda: L.ep_dispatch(None, 0, None, None, None, None, None, None, None),
+                 lambda: L.ep_dispatch_cached(None, 0, None, None, None, None),
+                 lambda: L.ep_combine(None, None, None, None, None),
+                 lambda: L.ep_relayout(None, None, None, None),
+                 lambda: L.ep_handle_counts(None, None, None, None)):
+        assert call() == ep.Status.ERR_NULL
+    L.ep_handle_free(None)  # no-op
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+
+    cfg = ep.Config(P=2, S=4, H=64, K=2, E=4, A=1)
+    with pytest.raises(ValueError):
+        ep.get_layout(cfg, torch.zeros((8, 2), dtype=torch.int64))
+    with pytest.raises((TypeError, ValueError)):
+        ep.get_layout(cfg, torch.zeros((8, 2), dtype=torch.int32))
+    with pytest.raises(TypeError):
+        ep.get_layout(cfg, [[0, 1]] * 8)

@@ -1,0 +1,359 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar (from the method's statement of correctness): layout arrays, indices and
+dispatched payload (bf16 copies, E4M3 codes and fp32 scales) bit-exact; combine
+within 1 bf16 ulp of the oracle.  The kernels use the oracle's arithmetic order
+(non-fused multiply then add, slots in order), so combine is also checked for
+bit-exact equality, which is stronger than the bar.
+
+Small and medium shapes (several chunks, ragged tails, edge cases) are compared
+element by element.  Full-size workloads compare the whole layout, all row
+metadata and, for payload, every token (bf16 and fp8 rows against the oracle's
+per-token encoding) and sampled or full combine outputs.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import combine_topk_idx_expert_amd as ep
+import oracle
+import synth
+from synth import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+LAYOUT_TENSORS = ["is_token_in_rank", "num_tokens_per_rank", "num_tokens_per_expert", "rank_prefix_matrix",
+                  "num_recv_tokens", "num_tokens_per_expert_total", "expert_offset", "num_expanded",
+                  "window_row_base", "dst_slot", "send_head", "recv_src_idx", "recv_src_base"]
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def dev_bf16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def host_u16(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def layout_both(w, topk, symmetric=False):
+    say("layout", w.name, "symmetric" if symmetric else "packed")
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk, symmetric)
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A, symmetric), torch.from_numpy(topk).to(DEV))
+    torch.cuda.synchronize()
+    return lay, h
+
+
+def check_layout(lay, h):
+    assert h.total_rows == lay.total_rows
+    for name in LAYOUT_TENSORS:
+        got = h.tensor(name).cpu().numpy()
+        exp = getattr(lay, name).reshape(-1)
+        np.testing.assert_array_equal(got, exp.astype(got.dtype), err_msg=name)
+    El = lay.E // lay.P
+    rank = np.where(lay.topk_idx >= 0, lay.topk_idx // El, 0)
+    exp_row = np.where(lay.dst_slot >= 0, lay.window_row_base[rank] + lay.dst_slot, -1)
+    np.testing.assert_array_equal(h.tensor("dst_row").cpu().numpy(), exp_row.reshape(-1))
+    ne, nr, wb = h.counts()
+    np.testing.assert_array_equal(ne, lay.num_expanded)
+    np.testing.assert_array_equal(nr, lay.num_recv_tokens)
+    np.testing.assert_array_equal(wb, lay.window_row_base)
+
+
+def routing_with_holes(w, seed=0):
+    """Workload routing plus unused (-1) slots and duplicate experts inside tokens."""
+    topk = synth.gen_routing(w).copy()
+    rng = np.random.default_rng(seed)
+    T = w.T
+    if T and w.K > 1:
+        topk[rng.random(T) < 0.1, w.K - 1] = -1
+        dup = rng.random(T) < 0.05
+        topk[dup, 1] = topk[dup, 0]
+        topk[rng.random(T) < 0.02] = -1  # tokens routed nowhere
+    return topk
+
+
+# --------------------------------------------------------------------------
+# small and medium shapes, element-wise
+# --------------------------------------------------------------------------
+
+D = synth.CONFIGS
+SMALL = [
+    D["tiny-p4-s64-e16-k2-h512"],
+    synth.scaled(D["dsv3-bf16-p8-s4096-e256-k8-h7168"], S=300),                 # ragged last chunk
+    synth.scaled(D["ep128-zipf-p128-s1024-e256-k6-h7168"], S=70, H=1024),      # empty experts, P=128
+    synth.scaled(D["ep32-group-fwdbwd-p32-s8192-e256-k8-h4096"], S=130),
+    wl.Workload("p1-s100-e8-k3", 1, 100, 8, 3, 256, 4, True, "uniform", seed=3),
+    wl.Workload("el1-p16-s64-e16-k4", 16, 64, 16, 4, 128, 1, True, "uniform", seed=4),
+    wl.Workload("k1-p4-s65-e32-k1", 4, 65, 32, 1, 136, 8, True, "uniform", seed=5),  # H not a multiple of 64
+    wl.Workload("s1-p8-s1-e64-k8", 8, 1, 64, 8, 512, 16, True, "uniform", seed=6),
+    wl.Workload("big-e-p64-s33-e1024-k16", 64, 33, 1024, 16, 256, 32, True, "uniform", seed=7),
+    wl.Workload("k32-p2-s70-e64-k32", 2, 70, 64, 32, 128, 3, True, "uniform", seed=8),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("holes", [False, True], ids=["plain", "holes"])
+def test_layout_small(w, holes):
+    topk = routing_with_holes(w, 11) if holes else synth.gen_routing(w)
+    lay, h = layout_both(w, topk)
+    check_layout(lay, h)
+    h.free()
+
+
+def test_layout_symmetric_windows():
+    w = SMALL[2]
+    topk = synth.gen_routing(w)
+    lay, h = layout_both(w, topk, symmetric=True)
+    check_layout(lay, h)
+    h.free()
+
+
+def test_layout_empty_and_errors():
+    w = wl.Workload("empty", 4, 0, 16, 2, 64, 4, True, "uniform")
+    lay, h = layout_both(w, np.zeros((0, 2), np.int64))
+    check_layout(lay, h)
+    assert h.total_rows == 0
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    rx, _, rw, meta = ep.dispatch(h, x, torch.zeros((0, 2), dtype=torch.float32, device=DEV), zero_padding=True)
+    out = ep.combine(h, rx)
+    assert out.shape == (0, 64)
+    h.free()
+    w = D["tiny-p4-s64-e16-k2-h512"]
+    for bad in (16, -2, 1 << 33):
+        topk = synth.gen_routing(w).copy()
+        topk[77, 1] = bad
+        say("routing error case", bad)
+        with pytest.raises(ep.EpError) as ei:
+            ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A), torch.from_numpy(topk).to(DEV))
+        assert ei.value.status == ep.Status.ERR_ROUTING
+
+
+def test_relayout_reuses_handle():
+    w = SMALL[1]
+    a = synth.gen_routing(w)
+    b = synth.gen_routing(synth.scaled(w, seed=9))
+    lay_a, h = layout_both(w, a)
+    check_layout(lay_a, h)
+    ep.relayout(h, torch.from_numpy(b).to(DEV))
+    check_layout(oracle.layout(w.P, w.S, w.E, w.K, w.A, b), h)
+    h.check(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A))
+    with pytest.raises(ep.EpError) as ei:
+        h.check(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A * 2))
+    assert ei.value.status == ep.Status.ERR_HANDLE_MISMATCH
+    h.free()
+
+
+DISPATCH_CASES = [w for w in SMALL if w.T > 0]
+
+
+@pytest.mark.parametrize("w", DISPATCH_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_dispatch_and_combine_small(w, fp8):
+    if fp8 and w.H % 128:
+        pytest.skip("fp8 needs H % 128 == 0")
+    topk = routing_with_holes(w, 12)
+    x = synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H)
+    x[:3, :128] = 0  # an all-zero 128-channel block (amax == 0)
+    x[1, 5] = 0x8000  # -0.0 inside it
+    wt = synth.gen_weights(w)
+    lay, h = layout_both(w, topk)
+    check_layout(lay, h)
+    R = lay.total_rows
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    sentinel = 0x7F if fp8 else 0xFFFF
+    pad = None
+    for zp in (False, True):
+        say("dispatch", w.name, "fp8" if fp8 else "bf16", "zero_padding" if zp else "no_padding")
+        rx = torch.full((R, w.H), 0x7F if fp8 else -1, dtype=torch.uint8 if fp8 else torch.int16, device=DEV)
+        if not fp8:
+            rx = rx.view(torch.bfloat16)
+        sc = torch.full((R, w.H // 128), float("nan"), dtype=torch.float32, device=DEV) if fp8 else None
+        rw = torch.full((R,), float("nan"), dtype=torch.float32, device=DEV)
+        rm = torch.full((R, 2), 77, dtype=torch.int32, device=DEV)
+        ep.dispatch(h, xd, wd, fp8=fp8, zero_padding=zp, out=(rx, sc, rw, rm))
+        torch.cuda.synchronize()
+        ox, osc, ow, om = oracle.dispatch(lay, w.H, x, wt, fp8, zp, fill=sentinel)
+        got_x = rx.cpu().numpy() if fp8 else host_u16(rx)
+        np.testing.assert_array_equal(got_x, ox)
+        np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+        np.testing.assert_array_equal(rm.cpu().numpy(), om)
+        pad = om[:, 0] < 0
+        if fp8:
+            gs = sc.cpu().numpy()
+            rows = slice(None) if zp else ~pad
+            np.testing.assert_array_equal(gs[rows].view(np.uint32), osc[rows].view(np.uint32))
+            if not zp:
+                assert np.all(np.isnan(gs[pad]))  # untouched
+        # cached dispatch reproduces the fresh payload
+        say("dispatch_cached", w.name)
+        cx = torch.full_like(rx, 0) if zp else rx.clone()
+        csc = torch.zeros_like(sc) if (fp8 and zp) else (sc.clone() if fp8 else None)
+        ep.dispatch_cached(h, xd, fp8=fp8, zero_padding=zp, out=(cx, csc))
+        torch.cuda.synchronize()
+        assert torch.equal(cx.view(torch.uint8), rx.view(torch.uint8))
+        if fp8:
+            np.testing.assert_array_equal(csc.cpu().numpy().view(np.uint32)[~pad], osc.view(np.uint32)[~pad])
+
+    # combine of arbitrary expert outputs (bf16) with and without weights
+    y = synth.gen_expert_out(w, R)
+    yd = dev_bf16(y)
+    for weights in (wt, None):
+        say("combine", w.name, "weighted" if weights is not None else "unit")
+        out = ep.combine(h, yd, None if weights is None else wd)
+        torch.cuda.synchronize()
+        exp = oracle.combine(lay, w.H, y, weights)
+        got = host_u16(out)
+        assert ulp_diff(got, exp).max() <= 1  # the stated bar
+        np.testing.assert_array_equal(got, exp)  # same arithmetic order: exact
+    h.free()
+
+
+def ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    def key(hh):
+        hh = hh.astype(np.int32)
+        return np.where(hh & 0x8000, 0x8000 - (hh & 0x7FFF), 0x8000 + (hh & 0x7FFF))
+    return np.abs(key(a) - key(b))
+
+
+# --------------------------------------------------------------------------
+# full-size workloads
+# --------------------------------------------------------------------------
+
+def gather_rows(t: torch.Tensor, rows: np.ndarray) -> torch.Tensor:
+    return t.index_select(0, torch.from_numpy(rows.astype(np.int64)).to(DEV))
+
+
+def dequant_identity(rx: torch.Tensor, sc: torch.Tensor) -> torch.Tensor:
+    """Identity expert on fp8 rows: bf16(decode(code) * scale)."""
+    f = rx.view(torch.float8_e4m3fn).to(torch.float32)
+    return (f * sc.repeat_interleave(128, dim=1)).to(torch.bfloat16)
+
+
+def quantize_all(x: np.ndarray, H: int):
+    codes = np.empty((x.shape[0], H), np.uint8)
+    scales = np.empty((x.shape[0], H // 128), np.float32)
+    for u in range(x.shape[0]):
+        codes[u], scales[u] = oracle.quantize_row(x[u])
+    return codes, scales
+
+
+def check_payload_rows(rx, x_dev, lay, fp8, codes=None, scales=None, sc=None, chunk=4096):
+    """Every valid slot's row equals its token's row (bf16) or the oracle's codes (fp8)."""
+    El = lay.E // lay.P
+    for u0 in range(0, lay.T, chunk):
+        u1 = min(lay.T, u0 + chunk)
+        tk = lay.topk_idx[u0:u1]
+        for j in range(lay.K):
+            m = tk[:, j] >= 0
+            if not m.any():
+                continue
+            us = np.arange(u0, u1)[m]
+            rows = lay.window_row_base[tk[m, j] // El] + lay.dst_slot[u0:u1][m, j]
+            got = gather_rows(rx, rows)
+            if not fp8:
+                exp = gather_rows(x_dev, us)
+                assert torch.equal(got.view(torch.int16), exp.view(torch.int16)), (u0, j)
+            else:
+                np.testing.assert_array_equal(got.cpu().numpy(), codes[us], err_msg=f"codes {u0} {j}")
+                np.testing.assert_array_equal(gather_rows(sc, rows).cpu().numpy().view(np.uint32),
+                                              scales[us].view(np.uint32), err_msg=f"scales {u0} {j}")
+
+
+FULL = [D[n] for n in wl.CONFIG_ORDER]
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+def test_full_size(w):
+    topk = synth.gen_routing(w)
+    lay, h = layout_both(w, topk)
+    check_layout(lay, h)
+    R = lay.total_rows
+    say("generate x", w.name)
+    x = synth.gen_x(w)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    fp8 = w.fp8
+    say("dispatch", w.name, "fp8" if fp8 else "bf16", "rows", R)
+    rx, sc, rw, rm = ep.dispatch(h, xd, wd, fp8=fp8, zero_padding=w.zero_padding)
+    torch.cuda.synchronize()
+    _, _, ow, om = oracle.dispatch(lay, w.H, None, wt, fp8, w.zero_padding)
+    np.testing.assert_array_equal(rm.cpu().numpy(), om)
+    np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+    pad = np.flatnonzero(om[:, 0] < 0)
+    if w.zero_padding and len(pad):
+        assert int(gather_rows(rx.view(torch.uint8) if fp8 else rx.view(torch.int16), pad).abs().max()) == 0
+        if fp8:
+            assert float(gather_rows(sc, pad).abs().max()) == 0.0
+    codes = scales = None
+    if fp8:
+        say("oracle quantize", w.name)
+        codes, scales = quantize_all(x, w.H)
+    say("payload rows", w.name)
+    check_payload_rows(rx, xd, lay, fp8, codes, scales, sc)
+
+    # combine(identity(dispatch(x))) against the oracle's composition
+    step = 1 if w.T <= 40000 else 8
+    toks = np.arange(0, w.T, step)
+    say("combine", w.name, "tokens", len(toks))
+    y = dequant_identity(rx, sc) if fp8 else rx
+    out = ep.combine(h, y, wd)
+    torch.cuda.synchronize()
+    got = host_u16(gather_rows(out, toks)) if step > 1 else host_u16(out)
+    exp = np.concatenate([oracle.combine_identity(w.K, w.H, fp8, topk, x, wt, u, u + 1)
+                          for u in toks]) if step > 1 else \
+        oracle.combine_identity(w.K, w.H, fp8, topk, x, wt, 0, w.T)
+    assert ulp_diff(got, exp).max() <= 1
+    np.testing.assert_array_equal(got, exp)
+    del y, out
+
+    if w.cached_iters:
+        say("cached iterations", w.cached_iters)
+        cx, csc = torch.empty_like(rx), (torch.empty_like(sc) if fp8 else None)
+        for it in range(1, w.cached_iters + 1):
+            xi = synth.workloads.gen_cached_x(w, it)
+            xid = dev_bf16(xi)
+            ep.dispatch_cached(h, xid, fp8=fp8, zero_padding=w.zero_padding, out=(cx, csc))
+            if it in (1, w.cached_iters):
+                ci, si = quantize_all(xi, w.H) if fp8 else (None, None)
+                check_payload_rows(cx, xid, lay, fp8, ci, si, csc)
+            else:
+                fx, fsc, _, _ = ep.dispatch(h, xid, wd, fp8=fp8, zero_padding=w.zero_padding)
+                assert torch.equal(fx.view(torch.uint8), cx.view(torch.uint8))
+                if fp8:
+                    assert torch.equal(fsc[~torch.from_numpy(om[:, 0] < 0).to(DEV)].view(torch.int32),
+                                       csc[~torch.from_numpy(om[:, 0] < 0).to(DEV)].view(torch.int32))
+            torch.cuda.synchronize()
+
+    if w.backward:
+        say("backward", w.name)
+        g = synth.gen_grad_out(w)
+        gd = dev_bf16(g)
+        gy, _ = ep.dispatch_cached(h, gd, zero_padding=w.zero_padding)
+        check_payload_rows(gy, gd, lay, False)
+        gx = ep.combine(h, gy, wd)
+        torch.cuda.synchronize()
+        toks = np.arange(0, w.T, 8)
+        got = host_u16(gather_rows(gx, toks))
+        exp = np.concatenate([oracle.combine_identity(w.K, w.H, False, topk, g, wt, u, u + 1) for u in toks])
+        np.testing.assert_array_equal(got, exp)
+    h.free()
+    del rx, sc, rw, rm, xd
+    torch.cuda.empty_cache()
