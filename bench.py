@@ -1,0 +1,266 @@
+"""Throughput of the MoE dispatch/combine hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic tokens:
+fresh layout of the routing (ep_relayout: counts, scans, stable ranks, the
+one D->H read of the window sizes), fresh dispatch of x into the expanded
+expert-grouped layout (bf16, with zero padding), identity experts, and the
+weighted combine back to token order.  Inputs are resident in HBM before the
+timed region; the handle and the expanded tensors are long-lived buffers
+reused every step, as the pages recommend for the EP buffer.
+
+Prints ONE JSON line.  Usage:
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dispatch & combine payload GB/s + tokens/s on 1 MI355X; % HBM roofline"
+DEFAULT_WORKLOAD = "dsv3-bf16-p8-s4096-e256-k8-h7168"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+KERNEL_SOURCES = ["combine_topk_idx_expert_amd/csrc/ep_dispatch.hpp",
+                  "combine_topk_idx_expert_amd/csrc/ep_device.hpp"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic byte ledger (what the method must move, not hardware traffic)
+# ---------------------------------------------------------------------------
+
+def ledger(T: int, K: int, H: int, rows: int, pad: int, fp8: bool, zero_padding: bool) -> dict:
+    """Bytes read / written per call.
+
+    rows = valid slots (expanded rows carrying a token), pad = alignment padding rows.
+    dispatch: read x (T*H*2) + per slot its weight and destination row (8 B);
+              write rows*(H*b + sf) payload, (rows+pad)*12 B of row metadata
+              (weight + source (u, j)), and pad*(H*b + sf) zeros when zero padding.
+    combine:  read rows*H*2 expert outputs + per slot weight and row (8 B);
+              write T*H*2.
+    """
+    b = 1 if fp8 else 2
+    sf = 4 * (H // 128) if fp8 else 0
+    d_read = T * H * 2 + 8 * T * K
+    d_write = rows * (H * b + sf) + (rows + pad) * 12 + (pad * (H * b + sf) if zero_padding else 0)
+    c_read = rows * H * 2 + 8 * T * K
+    c_write = T * H * 2
+    return dict(dispatch_read=d_read, dispatch_write=d_write, dispatch=d_read + d_write,
+                combine_read=c_read, combine_write=c_write, combine=c_read + c_write)
+
+
+def page_style_payload(num_recv_total: int, T: int, K: int, H: int, fp8: bool) -> float:
+    """The pages' bandwidth numerator: received tokens x logical bytes per token
+    (x, topk_idx, topk_weights), no padding ("Measure time and bytes correctly first";
+    tutorial section 7.4)."""
+    per_tok = (H * (1 if fp8 else 2) + (4 * (H // 128) if fp8 else 0)) + 8 * K + 4 * K
+    return float(num_recv_total) * per_tok
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, topk, x, wt, budget_s: float = 25.0) -> dict:
+    import numpy as np
+
+    import oracle
+
+    T = w.T
+    t0 = time.perf_counter()
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    t_layout = time.perf_counter() - t0
+    # dispatch of the first window(s) and combine of the matching share of tokens,
+    # scaled to the whole step by the fraction of rows / tokens covered
+    nwin = 1
+    r0, r1 = 0, int(lay.window_row_base[nwin])
+    t0 = time.perf_counter()
+    rx, _, _, _ = oracle.dispatch(lay, w.H, x, wt, False, w.zero_padding, r0, r1)
+    t_disp = time.perf_counter() - t0
+    frac_rows = (r1 - r0) / max(1, lay.total_rows)
+    ntok = max(1, T // w.P)
+    # combine input: identity experts, so every row of token u is x[u]; only the rows of
+    # the sampled tokens are filled (outside the timing)
+    El = w.E // w.P
+    y = np.zeros((lay.total_rows, w.H), np.uint16)
+    tk = topk[:ntok]
+    rows = np.where(tk >= 0, lay.window_row_base[np.where(tk >= 0, tk // El, 0)] + lay.dst_slot[:ntok], -1)
+    for j in range(w.K):
+        m = rows[:, j] >= 0
+        y[rows[m, j]] = x[:ntok][m]
+    t0 = time.perf_counter()
+    oracle.combine(lay, w.H, y, wt, 0, ntok)
+    t_comb = time.perf_counter() - t0
+    step = t_layout + t_disp / frac_rows + t_comb * (T / ntok)
+    return {"value": T / step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"full layout of all {T} tokens; dispatch of window 0 ({r1 - r0} of {lay.total_rows} "
+                       f"expanded rows); combine of {ntok} of {T} tokens; each part scaled to the whole "
+                       f"step by the share it covered; single thread"),
+            "seconds": {"layout": t_layout, "dispatch_sample": t_disp, "combine_sample": t_comb,
+                        "step_estimate": step}}
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the P "
+              "expert-parallel ranks are virtual windows in one GPU's HBM.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import combine_topk_idx_expert_amd as ep
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.CONFIGS[args.workload]
+    T, K, H = w.T, w.K, w.H
+
+    log("generating inputs", w.name)
+    topk = synth.gen_routing(w)
+    x = synth.gen_x(w)
+    wt = synth.gen_weights(w)
+    topk_d = torch.from_numpy(topk).to(dev)
+    x_d = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    w_d = torch.from_numpy(wt).to(dev)
+
+    h = ep.get_layout(ep.Config(w.P, w.S, H, K, w.E, w.A), topk_d)
+    R = h.total_rows
+    _, num_recv, _ = h.counts()
+    rows_valid = int((topk >= 0).sum())
+    pad = R - rows_valid
+    recv_x = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    recv_w = torch.empty(R, dtype=torch.float32, device=dev)
+    recv_m = torch.empty((R, 2), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        ep.relayout(h, topk_d)
+        if ev is not None:
+            ev[0].record(stream)
+        ep.dispatch(h, x_d, w_d, fp8=False, zero_padding=w.zero_padding, out=(recv_x, None, recv_w, recv_m))
+        if ev is not None:
+            ev[1].record(stream)
+        ep.combine(h, recv_x, w_d, out=out)  # identity experts: y = recv_x
+        if ev is not None:
+            ev[2].record(stream)
+
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log("timing", args.steps, "steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    d_ms = [e[0].elapsed_time(e[1]) for e in events]
+    c_ms = [e[1].elapsed_time(e[2]) for e in events]
+
+    ms_step = elapsed * 1e3 / args.steps
+    led = ledger(T, K, H, rows_valid, pad, False, w.zero_padding)
+    d_us = 1e3 * sum(d_ms) / len(d_ms)
+    c_us = 1e3 * sum(c_ms) / len(c_ms)
+    d_gbps = led["dispatch"] / (d_us * 1e3)
+    c_gbps = led["combine"] / (c_us * 1e3)
+    layout_us = ms_step * 1e3 - d_us - c_us
+    dominant = "dispatch" if d_us >= c_us else "combine"
+    dom_kernel = "dispatch_kernel" if dominant == "dispatch" else "combine_kernel"
+    dom_bytes = led[dominant]
+    dom_us = d_us if dominant == "dispatch" else c_us
+    achieved = dom_bytes / (dom_us * 1e3)
+    traffic = traffic_from_profiles(dom_kernel, w.name)
+    payload = page_style_payload(int(num_recv.sum()), T, K, H, False)
+
+    result = {
+        "metric": METRIC,
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "P": w.P, "S": w.S, "T": T, "E": w.E, "K": K, "H": H, "A": w.A,
+                   "routing": w.routing, "zero_padding": w.zero_padding, "seed": w.seed,
+                   "step": "relayout + dispatch(bf16) + identity + combine(fp32 acc)"},
+        "roofline": {"bound": "hbm", "kernel": dom_kernel, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": dom_us},
+        "calls": {
+            "layout_us_incl_host_sync": layout_us,
+            "dispatch_us": d_us, "combine_us": c_us,
+            "dispatch_GBps": d_gbps, "combine_GBps": c_gbps,
+            "dispatch_frac_hbm": d_gbps / HBM_PEAK_GBPS, "combine_frac_hbm": c_gbps / HBM_PEAK_GBPS,
+            "dispatch_bytes": led["dispatch"], "combine_bytes": led["combine"],
+            "dispatch_tokens_per_s": T / (d_us * 1e-6), "combine_tokens_per_s": T / (c_us * 1e-6),
+            "page_style_payload_GBps_dispatch": payload / (d_us * 1e3),
+            "expanded_rows": R, "padding_rows": pad,
+        },
+    }
+
+    if not args.no_cpu:
+        log("cpu baseline (oracle, one thread)")
+        result["cpu_baseline"] = cpu_baseline(w, topk, x, wt)
+    h.free()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
