@@ -29,7 +29,8 @@ METRIC = "dispatch & combine payload GB/s + tokens/s on 1 MI355X; % HBM roofline
 DEFAULT_WORKLOAD = "dsv3-bf16-p8-s4096-e256-k8-h7168"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 KERNEL_SOURCES = ["combine_topk_idx_expert_amd/csrc/ep_dispatch.hpp",
-                  "combine_topk_idx_expert_amd/csrc/ep_device.hpp"]
+                  "combine_topk_idx_expert_amd/csrc/ep_device.hpp",
+                  "combine_topk_idx_expert_amd/csrc/ep_api.hip"]
 
 
 def log(*a):
@@ -143,6 +144,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="first run a plain torch copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -162,6 +165,14 @@ def main() -> int:
     w = synth.CONFIGS[args.workload]
     T, K, H = w.T, w.K, w.H
 
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        a_ = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b_ = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        b_.copy_(a_)  # the plain copy kernel the hardware counters are scaled against
+        torch.cuda.synchronize()
+        del a_, b_
     log("generating inputs", w.name)
     topk = synth.gen_routing(w)
     x = synth.gen_x(w)

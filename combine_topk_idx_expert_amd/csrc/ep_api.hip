@@ -225,26 +225,47 @@ ep_status check_handle(const ep_handle* h) {
   return EP_OK;
 }
 
-// Largest column tile that still fits: 16-byte chunks per lane.
-int chunks_per_lane(int H) {
-  const int nchunk = H / 8;
-  return (nchunk + kWave - 1) / kWave;
+// Column part per wave, in 16-byte chunks per lane (tunable at build time;
+// the defaults are the fastest of a sweep on MI355X at hidden 7168 and 4096:
+// bf16 dispatch 1 KiB per wave, fp8 dispatch 2 KiB of bf16 input per wave,
+// combine 1 KiB per wave with all K <= 8 row loads in flight).
+#ifndef EP_DISPATCH_NC_BF16
+#define EP_DISPATCH_NC_BF16 1
+#endif
+#ifndef EP_DISPATCH_NC_FP8
+#define EP_DISPATCH_NC_FP8 2
+#endif
+#ifndef EP_COMBINE_NCT
+#define EP_COMBINE_NCT 1
+#endif
+#ifndef EP_COMBINE_G
+#define EP_COMBINE_G 8
+#endif
+
+// Largest instantiated chunk count <= want that the row still needs.
+int pick_nc(int H, int want) {
+  const int need = ((H >> 3) + kWave - 1) / kWave;  // chunks per lane for the whole row
+  const int nc = std::min(want, need);
+  return nc >= 14 ? 14 : nc >= 8 ? 8 : nc >= 7 ? 7 : nc >= 4 ? 4 : nc >= 2 ? 2 : 1;
 }
 
+int parts_per_row(int H, int nc) { return ((H >> 3) + nc * kWave - 1) / (nc * kWave); }
+
 template <bool FP8, bool META>
-ep_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
-  const int64_t waves = (int64_t)a.T + a.total_pad;
+ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
+  const int nc = pick_nc(a.H, FP8 ? EP_DISPATCH_NC_FP8 : EP_DISPATCH_NC_BF16);
+  a.split = parts_per_row(a.H, nc);
+  const int64_t waves = ((int64_t)a.T + a.total_pad) * a.split;
   if (waves == 0) return EP_OK;
+  if (waves >= ((int64_t)1 << 31) / kWave) return fail(EP_ERR_OVERFLOW, "dispatch grid too large (%lld waves)", (long long)waves);
   const int blocks = (int)((waves + kRowWaves - 1) / kRowWaves);
-  const int nc = chunks_per_lane(a.H);
-  const int tile = nc <= 1 ? 1 : nc <= 2 ? 2 : nc <= 4 ? 4 : nc <= 8 ? 8 : nc <= 14 ? 14 : 16;
-  switch (tile) {
+  switch (nc) {
     case 1: dispatch_kernel<1, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
     case 2: dispatch_kernel<2, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
     case 4: dispatch_kernel<4, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
+    case 7: dispatch_kernel<7, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
     case 8: dispatch_kernel<8, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
-    case 14: dispatch_kernel<14, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
-    default: dispatch_kernel<16, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
+    default: dispatch_kernel<14, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
   }
   EP_LAUNCHED("dispatch_kernel");
   return EP_OK;
@@ -349,17 +370,18 @@ ep_status ep_combine(const ep_handle* h, const void* y, const float* topk_weight
   if (h->total_rows > 0 && !y) return fail(EP_ERR_NULL, "y is NULL");
   if (misaligned(y, 16) || misaligned(out, 16) || misaligned(topk_weights, 4))
     return fail(EP_ERR_SHAPE, "y / out must be 16-byte aligned, topk_weights 4-byte aligned");
+  const int nct = std::min(pick_nc(h->cfg.hidden, EP_COMBINE_NCT), 4);
   CombineArgs a{(const uint16_t*)y, topk_weights, h->dst_row, (uint16_t*)out, (int)h->T, h->dims.K,
-                h->cfg.hidden};
-  const int blocks = (int)((h->T + kRowWaves - 1) / kRowWaves);
+                h->cfg.hidden, parts_per_row(h->cfg.hidden, nct)};
+  const int64_t waves = h->T * a.split;
+  if (waves >= ((int64_t)1 << 31) / kWave) return fail(EP_ERR_OVERFLOW, "combine grid too large (%lld waves)", (long long)waves);
+  const int blocks = (int)((waves + kRowWaves - 1) / kRowWaves);
   hipStream_t s = (hipStream_t)stream;
-  const int nc = chunks_per_lane(a.H);
-  if (nc <= 1)
-    combine_kernel<1, 4><<<blocks, kRowThreads, 0, s>>>(a);
-  else if (nc <= 2)
-    combine_kernel<2, 4><<<blocks, kRowThreads, 0, s>>>(a);
-  else
-    combine_kernel<4, 4><<<blocks, kRowThreads, 0, s>>>(a);
+  switch (nct) {
+    case 1: combine_kernel<1, EP_COMBINE_G><<<blocks, kRowThreads, 0, s>>>(a); break;
+    case 2: combine_kernel<2, EP_COMBINE_G><<<blocks, kRowThreads, 0, s>>>(a); break;
+    default: combine_kernel<4, EP_COMBINE_G><<<blocks, kRowThreads, 0, s>>>(a); break;
+  }
   EP_LAUNCHED("combine_kernel");
   return EP_OK;
 }

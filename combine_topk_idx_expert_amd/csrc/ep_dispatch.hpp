@@ -10,9 +10,10 @@
 // Combine: every token gathers its K expert rows and reduces them in a fixed
 // slot order in fp32, then rounds to bf16 (section 4.5).
 //
-// Work split: one wave per token (source-token partitioning keeps skewed
-// routing balanced: a hot expert means more rows written, not a longer wave).
-// A lane moves 16-byte vectors; a wave step covers 64 x 16 B = 1 KiB of a row.
+// Work split: one wave per (source token, column part).  Partitioning by source
+// token keeps skewed routing balanced: a hot expert means more rows written,
+// not a longer wave.  A lane moves 16-byte vectors; 64 lanes cover 1 KiB of a
+// bf16 row per vector.
 #pragma once
 
 #include "ep_device.hpp"
@@ -22,6 +23,10 @@ namespace ep {
 constexpr int kRowThreads = 256;  // 4 waves per workgroup
 constexpr int kRowWaves = kRowThreads / kWave;
 
+// Rows are split into column parts of NC 16-byte chunks per lane (NC KiB of
+// bf16 per wave); a wave handles one (row, part).  Short-lived waves that
+// each move a few KiB keep more of HBM's write bandwidth than long-lived
+// waves that move whole rows (measured on MI355X).
 struct DispatchArgs {
   const uint16_t* x;        // [T][H] bf16
   const float* w;           // [T][K]           (fresh only)
@@ -32,6 +37,7 @@ struct DispatchArgs {
   float* recv_weights;      // [rows]           (fresh only)
   int32_t* recv_meta;       // [rows][2]        (fresh only)
   int T, K, H, total_pad;
+  int split;                // parts per row = ceil((H / 8) / (64 * NC))
   int zero_pad;
 };
 
@@ -60,7 +66,7 @@ __device__ __forceinline__ u32x2 quantize8(u32x4 v, float scale, bool zero_block
   return out;
 }
 
-// NC: 16-byte chunks per lane per column tile (a tile is NC * 1 KiB of bf16).
+// NC: 16-byte chunks per lane per wave (the column part is 64 * NC chunks).
 template <int NC, bool FP8, bool META>
 __global__ __launch_bounds__(kRowThreads) void dispatch_kernel(DispatchArgs a) {
   const int gw = wave_index();
@@ -68,60 +74,61 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_kernel(DispatchArgs a) {
   const int nchunk = a.H >> 3;  // 16-byte bf16 chunks per row
   const int64_t out_row_bytes = FP8 ? (int64_t)a.H : (int64_t)a.H * 2;
   uint8_t* recv = (uint8_t*)a.recv_x;
+  const int token_waves = a.T * a.split;
 
-  if (gw < a.T) {
-    const int u = gw;
+  if (gw < token_waves) {
+    const int u = gw / a.split;
+    const int part = gw - u * a.split;
+    const int tile = part * NC * kWave;
     const u32x4* src = (const u32x4*)(a.x + (int64_t)u * a.H);
     const int32_t* rows = a.dst_row + (int64_t)u * a.K;
-    for (int tile = 0; tile < nchunk; tile += NC * kWave) {
-      u32x4 v[NC];
+    u32x4 v[NC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int q = tile + c * kWave + lane;
-        v[c] = q < nchunk ? __builtin_nontemporal_load(src + q) : u32x4{0, 0, 0, 0};
-      }
-      if constexpr (!FP8) {
-        for (int j = 0; j < a.K; ++j) {
-          const int row = rows[j];
-          if (row < 0) continue;
-          u32x4* dst = (u32x4*)(recv + (int64_t)row * out_row_bytes);
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const int q = tile + c * kWave + lane;
-            if (q < nchunk) dst[q] = v[c];
-          }
-        }
-      } else {
-        u32x2 codes[NC];
-        float scale[NC];
+    for (int c = 0; c < NC; ++c) {
+      const int q = tile + c * kWave + lane;
+      v[c] = q < nchunk ? __builtin_nontemporal_load(src + q) : u32x4{0, 0, 0, 0};
+    }
+    if constexpr (!FP8) {
+      for (int j = 0; j < a.K; ++j) {
+        const int row = rows[j];
+        if (row < 0) continue;
+        u32x4* dst = (u32x4*)(recv + (int64_t)row * out_row_bytes);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          uint32_t m = 0;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) m = max(m, max(v[c][k] & 0x7FFFu, (v[c][k] >> 16) & 0x7FFFu));
-          m = row16_max_u32(m);  // one DPP row = 16 lanes = one 128-channel block
-          scale[c] = __uint_as_float(m << 16) / 448.0f;
-          codes[c] = quantize8(v[c], scale[c], m == 0);
+          const int q = tile + c * kWave + lane;
+          if (q < nchunk) dst[q] = v[c];
         }
-        const int nblk = a.H >> 7;
-        for (int j = 0; j < a.K; ++j) {
-          const int row = rows[j];
-          if (row < 0) continue;
-          u32x2* dst = (u32x2*)(recv + (int64_t)row * out_row_bytes);
-          float* srow = a.recv_scales + (int64_t)row * nblk;
+      }
+    } else {
+      u32x2 codes[NC];
+      float scale[NC];
 #pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const int q = tile + c * kWave + lane;
-            if (q < nchunk) {
-              dst[q] = codes[c];
-              if ((lane & 15) == 0) srow[q >> 4] = scale[c];
-            }
+      for (int c = 0; c < NC; ++c) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m = max(m, max(v[c][k] & 0x7FFFu, (v[c][k] >> 16) & 0x7FFFu));
+        m = row16_max_u32(m);  // one DPP row = 16 lanes = one 128-channel block
+        scale[c] = __uint_as_float(m << 16) / 448.0f;
+        codes[c] = quantize8(v[c], scale[c], m == 0);
+      }
+      const int nblk = a.H >> 7;
+      for (int j = 0; j < a.K; ++j) {
+        const int row = rows[j];
+        if (row < 0) continue;
+        u32x2* dst = (u32x2*)(recv + (int64_t)row * out_row_bytes);
+        float* srow = a.recv_scales + (int64_t)row * nblk;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int q = tile + c * kWave + lane;
+          if (q < nchunk) {
+            dst[q] = codes[c];
+            if ((lane & 15) == 0) srow[q >> 4] = scale[c];
           }
         }
       }
     }
     if constexpr (META) {
-      if (lane < a.K) {
+      if (part == 0 && lane < a.K) {
         const int row = rows[lane];
         if (row >= 0) {
           a.recv_weights[row] = a.w[(int64_t)u * a.K + lane];
@@ -130,10 +137,12 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_kernel(DispatchArgs a) {
         }
       }
     }
-  } else if (gw < a.T + a.total_pad) {
-    const int row = a.pad_rows[gw - a.T];
+  } else if (gw < token_waves + a.total_pad * a.split) {
+    const int p = (gw - token_waves) / a.split;
+    const int part = (gw - token_waves) - p * a.split;
+    const int row = a.pad_rows[p];
     if constexpr (META) {
-      if (lane == 0) {
+      if (part == 0 && lane == 0) {
         a.recv_weights[row] = 0.0f;
         a.recv_meta[2 * (int64_t)row] = -1;
         a.recv_meta[2 * (int64_t)row + 1] = -1;
@@ -141,11 +150,18 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_kernel(DispatchArgs a) {
     }
     if (a.zero_pad) {
       uint8_t* dst = recv + (int64_t)row * out_row_bytes;
-      const int n16 = (int)(out_row_bytes >> 4);  // H % 8 == 0 -> whole 16-byte chunks
-      for (int q = lane; q < n16; q += kWave) ((u32x4*)dst)[q] = u32x4{0, 0, 0, 0};
-      if constexpr (FP8) {
-        const int nblk = a.H >> 7;
-        for (int b = lane; b < nblk; b += kWave) a.recv_scales[(int64_t)row * nblk + b] = 0.0f;
+      const int tile = part * NC * kWave;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int q = tile + c * kWave + lane;  // 16-byte bf16 chunk index
+        if (q < nchunk) {
+          if constexpr (FP8)
+            ((u32x2*)dst)[q] = u32x2{0, 0};
+          else
+            ((u32x4*)dst)[q] = u32x4{0, 0, 0, 0};
+          if constexpr (FP8)
+            if ((lane & 15) == 0) a.recv_scales[(int64_t)row * (a.H >> 7) + (q >> 4)] = 0.0f;
+        }
       }
     }
   }
@@ -160,69 +176,72 @@ struct CombineArgs {
   const int32_t* dst_row;  // [T][K]
   uint16_t* out;           // [T][H] bf16
   int T, K, H;
+  int split;               // parts per row = ceil((H / 8) / (64 * NCT))
 };
 
-// NCT: 16-byte chunks per lane per column tile; G: slots whose loads are in
-// flight together.  Accumulation order is always j = 0..K-1.
+// NCT: 16-byte chunks per lane (the wave's column part is 64 * NCT chunks);
+// G: slots whose loads are in flight together.  Accumulation order is always
+// j = 0..K-1.
 template <int NCT, int G>
 __global__ __launch_bounds__(kRowThreads) void combine_kernel(CombineArgs a) {
 #pragma clang fp contract(off)
-  const int u = wave_index();
-  if (u >= a.T) return;
+  const int gw = wave_index();
+  if (gw >= a.T * a.split) return;
+  const int u = gw / a.split;
+  const int part = gw - u * a.split;
+  const int tile = part * NCT * kWave;
   const int lane = lane_id();
   const int nchunk = a.H >> 3;
   const int32_t* rows = a.dst_row + (int64_t)u * a.K;
   const float* wrow = a.w ? a.w + (int64_t)u * a.K : nullptr;
   u32x4* dst = (u32x4*)(a.out + (int64_t)u * a.H);
 
-  for (int tile = 0; tile < nchunk; tile += NCT * kWave) {
-    float acc[NCT][8];
+  float acc[NCT][8];
 #pragma unroll
-    for (int c = 0; c < NCT; ++c)
+  for (int c = 0; c < NCT; ++c)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[c][k] = 0.0f;
+    for (int k = 0; k < 8; ++k) acc[c][k] = 0.0f;
 
-    for (int j0 = 0; j0 < a.K; j0 += G) {
-      u32x4 v[G][NCT];
-      int row[G];
-      float wj[G];
+  for (int j0 = 0; j0 < a.K; j0 += G) {
+    u32x4 v[G][NCT];
+    int row[G];
+    float wj[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const int j = j0 + g;
-        row[g] = j < a.K ? rows[j] : -1;
-        wj[g] = (j < a.K && wrow) ? wrow[j] : 1.0f;
-        if (row[g] >= 0) {
-          const u32x4* src = (const u32x4*)(a.y + (int64_t)row[g] * a.H);
+    for (int g = 0; g < G; ++g) {
+      const int j = j0 + g;
+      row[g] = j < a.K ? rows[j] : -1;
+      wj[g] = (j < a.K && wrow) ? wrow[j] : 1.0f;
+      if (row[g] >= 0) {
+        const u32x4* src = (const u32x4*)(a.y + (int64_t)row[g] * a.H);
 #pragma unroll
-          for (int c = 0; c < NCT; ++c) {
-            const int q = tile + c * kWave + lane;
-            v[g][c] = q < nchunk ? __builtin_nontemporal_load(src + q) : u32x4{0, 0, 0, 0};
-          }
+        for (int c = 0; c < NCT; ++c) {
+          const int q = tile + c * kWave + lane;
+          v[g][c] = q < nchunk ? __builtin_nontemporal_load(src + q) : u32x4{0, 0, 0, 0};
         }
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        if (row[g] < 0) continue;
-#pragma unroll
-        for (int c = 0; c < NCT; ++c)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float p0 = wj[g] * bf16_lo(v[g][c][k]);
-            const float p1 = wj[g] * bf16_hi(v[g][c][k]);
-            acc[c][2 * k] = acc[c][2 * k] + p0;
-            acc[c][2 * k + 1] = acc[c][2 * k + 1] + p1;
-          }
       }
     }
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-      const int q = tile + c * kWave + lane;
-      if (q < nchunk) {
-        u32x4 o;
+    for (int g = 0; g < G; ++g) {
+      if (row[g] < 0) continue;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(acc[c][2 * k], acc[c][2 * k + 1]);
-        dst[q] = o;
-      }
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float p0 = wj[g] * bf16_lo(v[g][c][k]);
+          const float p1 = wj[g] * bf16_hi(v[g][c][k]);
+          acc[c][2 * k] = acc[c][2 * k] + p0;
+          acc[c][2 * k + 1] = acc[c][2 * k + 1] + p1;
+        }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    const int q = tile + c * kWave + lane;
+    if (q < nchunk) {
+      u32x4 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(acc[c][2 * k], acc[c][2 * k + 1]);
+      dst[q] = o;
     }
   }
 }
