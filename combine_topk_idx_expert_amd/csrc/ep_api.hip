@@ -59,7 +59,7 @@ struct ep_handle {
   int64_t T;
   int device;
   // read back by the layout
-  int64_t total_rows = 0, total_pad = 0, sum_recv = 0;
+  int64_t total_rows = 0, total_pad = 0, sum_recv = 0, sum_expanded = 0;
   bool valid = false;
   // device arena and the arrays inside it
   void* arena = nullptr;
@@ -68,7 +68,9 @@ struct ep_handle {
   int32_t *num_tokens_per_rank, *num_tokens_per_expert, *rank_prefix_matrix, *num_recv, *n_e;
   int64_t *expert_offset, *num_expanded, *window_row_base, *recv_src_base;
   int32_t *dst_slot, *dst_row, *send_head, *recv_src_idx;
-  int32_t *pad_base, *pad_rows, *chunk_hist, *col_total;
+  int32_t *pad_base, *pad_rows, *chunk_hist, *col_total, *row_slot;
+  int64_t* packed_base;
+  float* tok_scales = nullptr;  // fp8 per-token scales (H % 128 == 0 only)
   int64_t* summary_dev;
   int64_t* summary_host = nullptr;  // pinned
   hipEvent_t done = nullptr;        // end of the last layout's work
@@ -146,6 +148,9 @@ ep_status allocate(ep_handle* h) {
       {(void**)&h->chunk_hist, (size_t)((int64_t)d.ncols * d.num_chunks * 4)},
       {(void**)&h->col_total, (size_t)(d.ncols * 4)},
       {(void**)&h->summary_dev, (size_t)((kSummaryHeader + 3 * P + 1) * 8)},
+      {(void**)&h->row_slot, (size_t)((T * K + max_pad) * 4)},
+      {(void**)&h->packed_base, (size_t)((P + 1) * 8)},
+      {(void**)&h->tok_scales, (size_t)(h->cfg.hidden % 128 == 0 ? T * (h->cfg.hidden / 128) * 4 : 0)},
   };
   size_t total = 0;
   for (const Item& it : items) total += align_up(std::max<size_t>(it.bytes, 1));
@@ -194,15 +199,16 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
       h->rank_prefix_matrix);
   EP_LAUNCHED("layout_scan_kernel");
   FinalizeOut fo{h->n_e, h->expert_offset, h->num_expanded, h->window_row_base, h->num_recv,
-                 h->recv_src_base, h->pad_base, h->pad_rows, h->summary_dev};
+                 h->recv_src_base, h->pad_base, h->pad_rows, h->packed_base, h->row_slot, h->summary_dev};
   layout_finalize_kernel<<<1, kFinalizeThreads, h->lds_finalize, s>>>(d, h->col_total, fo);
   EP_LAUNCHED("layout_finalize_kernel");
   EP_HIP(hipMemcpyAsync(h->summary_host, h->summary_dev, (size_t)(kSummaryHeader + 3 * d.P + 1) * 8,
                         hipMemcpyDeviceToHost, s));
   if (d.num_chunks > 0) {
-    RankOut ro{h->dst_slot, h->dst_row, h->send_head, h->recv_src_idx};
+    RankOut ro{h->dst_slot, h->dst_row, h->row_slot, h->send_head, h->recv_src_idx};
     layout_rank_kernel<<<d.num_chunks, kWave, h->lds_rank, s>>>(d, topk_idx, h->chunk_hist, h->expert_offset,
-                                                                 h->window_row_base, h->recv_src_base, ro);
+                                                                 h->window_row_base, h->packed_base,
+                                                                 h->recv_src_base, ro);
     EP_LAUNCHED("layout_rank_kernel");
   }
   EP_HIP(hipEventRecord(h->done, s));
@@ -213,6 +219,8 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
     return fail(EP_ERR_OVERFLOW, "expanded rows %lld reach 2^31 (symmetric windows)", (long long)sm[0]);
   h->total_rows = sm[0];
   h->total_pad = sm[1];
+  h->sum_expanded = 0;
+  for (int r = 0; r < d.P; ++r) h->sum_expanded += sm[kSummaryHeader + r];
   h->sum_recv = sm[3];
   h->valid = true;
   if (total_rows) *total_rows = h->total_rows;
@@ -235,6 +243,9 @@ ep_status check_handle(const ep_handle* h) {
 #ifndef EP_DISPATCH_NC_FP8
 #define EP_DISPATCH_NC_FP8 2
 #endif
+#ifndef EP_ROW_BLOCK_WAVES
+#define EP_ROW_BLOCK_WAVES 4  // waves per workgroup of the row kernels
+#endif
 #ifndef EP_COMBINE_NCT
 #define EP_COMBINE_NCT 1
 #endif
@@ -255,19 +266,30 @@ template <bool FP8, bool META>
 ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
   const int nc = pick_nc(a.H, FP8 ? EP_DISPATCH_NC_FP8 : EP_DISPATCH_NC_BF16);
   a.split = parts_per_row(a.H, nc);
-  const int64_t waves = ((int64_t)a.T + a.total_pad) * a.split;
-  if (waves == 0) return EP_OK;
+  const int64_t meta_items = META ? ((int64_t)a.sum_expanded + kWave - 1) / kWave : 0;
+  const int64_t waves = ((int64_t)a.T + (a.zero_pad ? a.total_pad : 0)) * a.split + meta_items;
   if (waves >= ((int64_t)1 << 31) / kWave) return fail(EP_ERR_OVERFLOW, "dispatch grid too large (%lld waves)", (long long)waves);
-  const int blocks = (int)((waves + kRowWaves - 1) / kRowWaves);
-  switch (nc) {
-    case 1: dispatch_kernel<1, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
-    case 2: dispatch_kernel<2, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
-    case 4: dispatch_kernel<4, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
-    case 7: dispatch_kernel<7, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
-    case 8: dispatch_kernel<8, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
-    default: dispatch_kernel<14, FP8, META><<<blocks, kRowThreads, 0, s>>>(a); break;
+  if (waves > 0) {
+    const int threads = EP_ROW_BLOCK_WAVES * kWave;
+    const int blocks = (int)((waves + EP_ROW_BLOCK_WAVES - 1) / EP_ROW_BLOCK_WAVES);
+    switch (nc) {
+      case 1: dispatch_kernel<1, FP8, META><<<blocks, threads, 0, s>>>(a); break;
+      case 2: dispatch_kernel<2, FP8, META><<<blocks, threads, 0, s>>>(a); break;
+      case 4: dispatch_kernel<4, FP8, META><<<blocks, threads, 0, s>>>(a); break;
+      case 7: dispatch_kernel<7, FP8, META><<<blocks, threads, 0, s>>>(a); break;
+      case 8: dispatch_kernel<8, FP8, META><<<blocks, threads, 0, s>>>(a); break;
+      default: dispatch_kernel<14, FP8, META><<<blocks, threads, 0, s>>>(a); break;
+    }
+    EP_LAUNCHED("dispatch_kernel");
   }
-  EP_LAUNCHED("dispatch_kernel");
+  if constexpr (FP8) {
+    const int64_t n = (int64_t)a.sum_expanded * (a.H >> 7);
+    if (n > 0) {
+      if (n >= ((int64_t)1 << 31)) return fail(EP_ERR_OVERFLOW, "scale grid too large");
+      dispatch_scales_kernel<<<(int)((n + 255) / 256), 256, 0, s>>>(a);
+      EP_LAUNCHED("dispatch_scales_kernel");
+    }
+  }
   return EP_OK;
 }
 
@@ -296,15 +318,23 @@ ep_status dispatch_common(const ep_handle* h, uint32_t flags, const void* x, con
   a.w = w;
   a.dst_row = h->dst_row;
   a.pad_rows = h->pad_rows;
+  a.row_slot = h->row_slot;
+  a.packed_base = h->packed_base;
+  a.window_row_base = h->window_row_base;
   a.recv_x = recv_x;
   a.recv_scales = recv_scales;
+  a.tok_scales = h->tok_scales;
   a.recv_weights = recv_weights;
   a.recv_meta = recv_meta;
   a.T = (int)h->T;
   a.K = h->dims.K;
   a.H = h->cfg.hidden;
-  a.total_pad = (meta || zero_pad) ? (int)h->total_pad : 0;
+  a.P = h->dims.P;
+  a.total_pad = (int)h->total_pad;
+  a.sum_expanded = (int)h->sum_expanded;
+  a.split = 1;
   a.zero_pad = zero_pad ? 1 : 0;
+  a.symmetric = h->dims.symmetric;
   if (fp8) return meta ? launch_dispatch<true, true>(a, s) : launch_dispatch<true, false>(a, s);
   return meta ? launch_dispatch<false, true>(a, s) : launch_dispatch<false, false>(a, s);
 }
@@ -375,12 +405,13 @@ ep_status ep_combine(const ep_handle* h, const void* y, const float* topk_weight
                 h->cfg.hidden, parts_per_row(h->cfg.hidden, nct)};
   const int64_t waves = h->T * a.split;
   if (waves >= ((int64_t)1 << 31) / kWave) return fail(EP_ERR_OVERFLOW, "combine grid too large (%lld waves)", (long long)waves);
-  const int blocks = (int)((waves + kRowWaves - 1) / kRowWaves);
+  const int threads = EP_ROW_BLOCK_WAVES * kWave;
+  const int blocks = (int)((waves + EP_ROW_BLOCK_WAVES - 1) / EP_ROW_BLOCK_WAVES);
   hipStream_t s = (hipStream_t)stream;
   switch (nct) {
-    case 1: combine_kernel<1, EP_COMBINE_G><<<blocks, kRowThreads, 0, s>>>(a); break;
-    case 2: combine_kernel<2, EP_COMBINE_G><<<blocks, kRowThreads, 0, s>>>(a); break;
-    default: combine_kernel<4, EP_COMBINE_G><<<blocks, kRowThreads, 0, s>>>(a); break;
+    case 1: combine_kernel<1, EP_COMBINE_G><<<blocks, threads, 0, s>>>(a); break;
+    case 2: combine_kernel<2, EP_COMBINE_G><<<blocks, threads, 0, s>>>(a); break;
+    default: combine_kernel<4, EP_COMBINE_G><<<blocks, threads, 0, s>>>(a); break;
   }
   EP_LAUNCHED("combine_kernel");
   return EP_OK;

@@ -27,23 +27,44 @@ constexpr int kRowWaves = kRowThreads / kWave;
 // bf16 per wave); a wave handles one (row, part).  Short-lived waves that
 // each move a few KiB keep more of HBM's write bandwidth than long-lived
 // waves that move whole rows (measured on MI355X).
+//
+// Row metadata (weights, source slot, fp8 scales) is written in row order by
+// waves that each own 64 consecutive expanded rows, so every store is
+// coalesced; scattering it per token would issue millions of partial-line
+// writes.
 struct DispatchArgs {
-  const uint16_t* x;        // [T][H] bf16
-  const float* w;           // [T][K]           (fresh only)
-  const int32_t* dst_row;   // [T][K] global row, -1 unused
-  const int32_t* pad_rows;  // [total_pad] global rows
-  void* recv_x;             // [rows][H] bf16 | u8
-  float* recv_scales;       // [rows][H/128]    (fp8)
-  float* recv_weights;      // [rows]           (fresh only)
-  int32_t* recv_meta;       // [rows][2]        (fresh only)
-  int T, K, H, total_pad;
-  int split;                // parts per row = ceil((H / 8) / (64 * NC))
-  int zero_pad;
+  const uint16_t* x;             // [T][H] bf16
+  const float* w;                // [T][K]           (fresh only)
+  const int32_t* dst_row;        // [T][K] global row, -1 unused
+  const int32_t* pad_rows;       // [total_pad] global rows
+  const int32_t* row_slot;       // [sum_expanded] source slot u*K+j, -1 padding (packed order)
+  const int64_t* packed_base;    // [P+1] packed start of each window
+  const int64_t* window_row_base;  // [P+1] global start of each window
+  void* recv_x;                  // [rows][H] bf16 | u8
+  float* recv_scales;            // [rows][H/128]    (fp8)
+  float* tok_scales;             // [T][H/128]       (fp8 scratch: scales per token)
+  float* recv_weights;           // [rows]           (fresh only)
+  int32_t* recv_meta;            // [rows][2]        (fresh only)
+  int T, K, H, P;
+  int total_pad, sum_expanded;
+  int split;                     // parts per row = ceil((H / 8) / (64 * NC))
+  int zero_pad, symmetric;
 };
 
 // Wave-uniform global wave index of the calling lane.
 __device__ __forceinline__ int wave_index() {
-  return uniform((int)(blockIdx.x * kRowWaves + (threadIdx.x >> 6)));
+  return uniform((int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
+}
+
+// Global row of the p-th row when the windows are laid end to end.
+__device__ __forceinline__ int64_t packed_to_row(const DispatchArgs& a, int64_t p) {
+  if (!a.symmetric) return p;  // packed windows: the same numbering
+  int lo = 0, hi = a.P;        // last window with packed_base <= p
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.packed_base[mid] <= p) lo = mid; else hi = mid;
+  }
+  return a.window_row_base[lo] + (p - a.packed_base[lo]);
 }
 
 // E4M3 codes of 8 bf16 values (packed in v) for one 128-channel block whose
@@ -66,17 +87,22 @@ __device__ __forceinline__ u32x2 quantize8(u32x4 v, float scale, bool zero_block
   return out;
 }
 
+// Work items, in grid order:
+//   [0, T*split)                      payload of (token, part)
+//   [.., + total_pad*split)           zero payload of (padding row, part)   if zero_pad
+//   [.., + ceil(sum_expanded / 64))   row metadata of 64 rows               if META
 // NC: 16-byte chunks per lane per wave (the column part is 64 * NC chunks).
 template <int NC, bool FP8, bool META>
-__global__ __launch_bounds__(kRowThreads) void dispatch_kernel(DispatchArgs a) {
+__global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
   const int gw = wave_index();
   const int lane = lane_id();
   const int nchunk = a.H >> 3;  // 16-byte bf16 chunks per row
   const int64_t out_row_bytes = FP8 ? (int64_t)a.H : (int64_t)a.H * 2;
   uint8_t* recv = (uint8_t*)a.recv_x;
-  const int token_waves = a.T * a.split;
+  const int token_items = a.T * a.split;
+  const int pad_items = a.zero_pad ? a.total_pad * a.split : 0;
 
-  if (gw < token_waves) {
+  if (gw < token_items) {
     const int u = gw / a.split;
     const int part = gw - u * a.split;
     const int tile = part * NC * kWave;
@@ -101,70 +127,70 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_kernel(DispatchArgs a) {
       }
     } else {
       u32x2 codes[NC];
-      float scale[NC];
+      const int nblk = a.H >> 7;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         uint32_t m = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) m = max(m, max(v[c][k] & 0x7FFFu, (v[c][k] >> 16) & 0x7FFFu));
         m = row16_max_u32(m);  // one DPP row = 16 lanes = one 128-channel block
-        scale[c] = __uint_as_float(m << 16) / 448.0f;
-        codes[c] = quantize8(v[c], scale[c], m == 0);
+        const float scale = __uint_as_float(m << 16) / 448.0f;
+        codes[c] = quantize8(v[c], scale, m == 0);
+        const int q = tile + c * kWave + lane;
+        if ((lane & 15) == 0 && q < nchunk) a.tok_scales[(int64_t)u * nblk + (q >> 4)] = scale;
       }
-      const int nblk = a.H >> 7;
       for (int j = 0; j < a.K; ++j) {
         const int row = rows[j];
         if (row < 0) continue;
         u32x2* dst = (u32x2*)(recv + (int64_t)row * out_row_bytes);
-        float* srow = a.recv_scales + (int64_t)row * nblk;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const int q = tile + c * kWave + lane;
-          if (q < nchunk) {
-            dst[q] = codes[c];
-            if ((lane & 15) == 0) srow[q >> 4] = scale[c];
-          }
+          if (q < nchunk) dst[q] = codes[c];
         }
       }
     }
-    if constexpr (META) {
-      if (part == 0 && lane < a.K) {
-        const int row = rows[lane];
-        if (row >= 0) {
-          a.recv_weights[row] = a.w[(int64_t)u * a.K + lane];
-          a.recv_meta[2 * (int64_t)row] = u;
-          a.recv_meta[2 * (int64_t)row + 1] = lane;
-        }
-      }
-    }
-  } else if (gw < token_waves + a.total_pad * a.split) {
-    const int p = (gw - token_waves) / a.split;
-    const int part = (gw - token_waves) - p * a.split;
-    const int row = a.pad_rows[p];
-    if constexpr (META) {
-      if (part == 0 && lane == 0) {
-        a.recv_weights[row] = 0.0f;
-        a.recv_meta[2 * (int64_t)row] = -1;
-        a.recv_meta[2 * (int64_t)row + 1] = -1;
-      }
-    }
-    if (a.zero_pad) {
-      uint8_t* dst = recv + (int64_t)row * out_row_bytes;
-      const int tile = part * NC * kWave;
+  } else if (gw < token_items + pad_items) {
+    const int p = (gw - token_items) / a.split;
+    const int part = (gw - token_items) - p * a.split;
+    uint8_t* dst = recv + (int64_t)a.pad_rows[p] * out_row_bytes;
+    const int tile = part * NC * kWave;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int q = tile + c * kWave + lane;  // 16-byte bf16 chunk index
-        if (q < nchunk) {
-          if constexpr (FP8)
-            ((u32x2*)dst)[q] = u32x2{0, 0};
-          else
-            ((u32x4*)dst)[q] = u32x4{0, 0, 0, 0};
-          if constexpr (FP8)
-            if ((lane & 15) == 0) a.recv_scales[(int64_t)row * (a.H >> 7) + (q >> 4)] = 0.0f;
-        }
+    for (int c = 0; c < NC; ++c) {
+      const int q = tile + c * kWave + lane;  // 16-byte bf16 chunk index
+      if (q < nchunk) {
+        if constexpr (FP8)
+          ((u32x2*)dst)[q] = u32x2{0, 0};
+        else
+          ((u32x4*)dst)[q] = u32x4{0, 0, 0, 0};
       }
+    }
+  } else if (META) {
+    const int64_t pr = (int64_t)(gw - token_items - pad_items) * kWave + lane;
+    if (pr < a.sum_expanded) {
+      const int slot = a.row_slot[pr];
+      const int64_t row = packed_to_row(a, pr);
+      const int u = slot >= 0 ? slot / a.K : -1;
+      a.recv_weights[row] = slot >= 0 ? a.w[slot] : 0.0f;
+      ((int2*)a.recv_meta)[row] = make_int2(u, slot >= 0 ? slot - u * a.K : -1);
     }
   }
+}
+
+// fp8 row scales in row order: recv_scales[row][b] = scale of the row's
+// source token (0 for padding rows with zero padding; otherwise untouched).
+__global__ __launch_bounds__(256) void dispatch_scales_kernel(DispatchArgs a) {
+  const int nblk = a.H >> 7;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.sum_expanded * nblk) return;
+  const int64_t pr = i / nblk;
+  const int b = (int)(i - pr * nblk);
+  const int slot = a.row_slot[pr];
+  const int64_t row = packed_to_row(a, pr);
+  if (slot >= 0)
+    a.recv_scales[row * nblk + b] = a.tok_scales[(int64_t)(slot / a.K) * nblk + b];
+  else if (a.zero_pad)
+    a.recv_scales[row * nblk + b] = 0.0f;
 }
 
 // --------------------------------------------------------------------------
@@ -183,7 +209,7 @@ struct CombineArgs {
 // G: slots whose loads are in flight together.  Accumulation order is always
 // j = 0..K-1.
 template <int NCT, int G>
-__global__ __launch_bounds__(kRowThreads) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
 #pragma clang fp contract(off)
   const int gw = wave_index();
   if (gw >= a.T * a.split) return;

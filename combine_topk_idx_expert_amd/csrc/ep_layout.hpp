@@ -242,6 +242,8 @@ struct FinalizeOut {
   int64_t* recv_src_base;   // [P+1]
   int32_t* pad_base;        // [E+1]
   int32_t* pad_rows;        // [E*(A-1)] capacity
+  int64_t* packed_base;     // [P+1] windows laid end to end (row_slot index space)
+  int32_t* row_slot;        // [sum num_expanded] source slot u*K+j of each row, -1 padding
   int64_t* summary;         // host summary, see above
 };
 
@@ -300,6 +302,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
   for (int r = tid; r <= d.P; r += kFinalizeThreads) {
     const int64_t base = d.symmetric ? (int64_t)r * wmax : g[min(r, d.P) * d.El];
     o.window_row_base[r] = base;
+    o.packed_base[r] = g[r * d.El];
     o.summary[kSummaryHeader + 2 * d.P + r] = base;
   }
   for (int x = tid; x < d.P * (d.El + 1); x += kFinalizeThreads) {
@@ -341,6 +344,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
     const int64_t first_pad = (d.symmetric ? (int64_t)r * wmax : g[r * d.El]) + (g[e] - g[r * d.El]) +
                               col_total[e];
     o.pad_rows[i] = (int32_t)(first_pad + (i - pb[e]));
+    o.row_slot[g[e] + col_total[e] + (i - pb[e])] = -1;
   }
 }
 
@@ -350,6 +354,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
 struct RankOut {
   int32_t* dst_slot;      // [T][K]
   int32_t* dst_row;       // [T][K]
+  int32_t* row_slot;      // [sum num_expanded], packed window order
   int32_t* send_head;     // [T][P]
   int32_t* recv_src_idx;  // [sum num_recv]
 };
@@ -358,7 +363,7 @@ struct RankOut {
 __global__ __launch_bounds__(64) void layout_rank_kernel(
     LayoutDims d, const int64_t* __restrict__ topk_idx, const int32_t* __restrict__ chunk_excl,
     const int64_t* __restrict__ expert_offset, const int64_t* __restrict__ window_row_base,
-    const int64_t* __restrict__ recv_src_base, RankOut o) {
+    const int64_t* __restrict__ packed_base, const int64_t* __restrict__ recv_src_base, RankOut o) {
   extern __shared__ int32_t lds[];
   int32_t* cnt_e = lds;
   int32_t* cnt_r = lds + d.E + 1;
@@ -406,6 +411,7 @@ __global__ __launch_bounds__(64) void layout_rank_kernel(
         const int64_t slot = expert_offset[(int64_t)r * (d.El + 1) + (e - r * d.El)] + be + count_below(pe);
         o.dst_slot[u * d.K + j] = (int32_t)slot;
         o.dst_row[u * d.K + j] = (int32_t)(window_row_base[r] + slot);
+        o.row_slot[packed_base[r] + slot] = (int32_t)(u * d.K + j);
       } else {
         o.dst_slot[u * d.K + j] = -1;
         o.dst_row[u * d.K + j] = -1;
