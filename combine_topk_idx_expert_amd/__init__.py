@@ -26,6 +26,7 @@ from ._native import (  # noqa: F401
     Status,
     TENSORS,
     combine,
+    debug_e4m3_encode,
     dispatch,
     dispatch_cached,
     get_layout,

@@ -125,6 +125,8 @@ def lib() -> ctypes.CDLL:
         for fn in ("ep_get_layout", "ep_relayout", "ep_dispatch", "ep_dispatch_cached", "ep_combine",
                    "ep_handle_config", "ep_handle_check", "ep_handle_counts", "ep_handle_tensor"):
             getattr(L, fn).restype = i32
+        L.ep_debug_e4m3_encode.argtypes = [vp, vp, i64, vp]
+        L.ep_debug_e4m3_encode.restype = i32
         L.ep_last_error.argtypes = []
         L.ep_last_error.restype = ctypes.c_char_p
         L.ep_abi_version.argtypes = []
@@ -315,4 +317,15 @@ def combine(h: Handle, y, topk_weights=None, out=None):
     if out is None:
         out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=y.device)
     _check(lib().ep_combine(h.ptr, _ptr(y), _ptr(topk_weights), _ptr(out), _stream(y.device)))
+    return out
+
+
+def debug_e4m3_encode(q):
+    """The fp8 dispatch kernel's float -> E4M3FN conversion on a float32 device tensor."""
+    import torch
+
+    if q.dtype != torch.float32 or not q.is_cuda or not q.is_contiguous():
+        raise TypeError("q must be a contiguous float32 device tensor")
+    out = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+    _check(lib().ep_debug_e4m3_encode(_ptr(q), _ptr(out), q.numel(), _stream(q.device)))
     return out

@@ -234,17 +234,20 @@ ep_status check_handle(const ep_handle* h) {
 }
 
 // Column part per wave, in 16-byte chunks per lane (tunable at build time;
-// the defaults are the fastest of a sweep on MI355X at hidden 7168 and 4096:
-// bf16 dispatch 1 KiB per wave, fp8 dispatch 2 KiB of bf16 input per wave,
-// combine 1 KiB per wave with all K <= 8 row loads in flight).
+// the defaults are the fastest of sweeps on MI355X at hidden 7168 and 4096:
+// dispatch 1 KiB of bf16 input per wave for bf16 and fp8 output, combine
+// 1 KiB per wave with all K <= 8 row loads in flight).
 #ifndef EP_DISPATCH_NC_BF16
 #define EP_DISPATCH_NC_BF16 1
 #endif
 #ifndef EP_DISPATCH_NC_FP8
-#define EP_DISPATCH_NC_FP8 2
+#define EP_DISPATCH_NC_FP8 1
 #endif
 #ifndef EP_ROW_BLOCK_WAVES
 #define EP_ROW_BLOCK_WAVES 4  // waves per workgroup of the row kernels
+#endif
+#ifndef EP_DISPATCH_LDS_BYTES
+#define EP_DISPATCH_LDS_BYTES 0
 #endif
 #ifndef EP_COMBINE_NCT
 #define EP_COMBINE_NCT 1
@@ -272,13 +275,14 @@ ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
   if (waves > 0) {
     const int threads = EP_ROW_BLOCK_WAVES * kWave;
     const int blocks = (int)((waves + EP_ROW_BLOCK_WAVES - 1) / EP_ROW_BLOCK_WAVES);
+    const size_t lds = EP_DISPATCH_LDS_BYTES;  // > 0 caps workgroups per CU (occupancy)
     switch (nc) {
-      case 1: dispatch_kernel<1, FP8, META><<<blocks, threads, 0, s>>>(a); break;
-      case 2: dispatch_kernel<2, FP8, META><<<blocks, threads, 0, s>>>(a); break;
-      case 4: dispatch_kernel<4, FP8, META><<<blocks, threads, 0, s>>>(a); break;
-      case 7: dispatch_kernel<7, FP8, META><<<blocks, threads, 0, s>>>(a); break;
-      case 8: dispatch_kernel<8, FP8, META><<<blocks, threads, 0, s>>>(a); break;
-      default: dispatch_kernel<14, FP8, META><<<blocks, threads, 0, s>>>(a); break;
+      case 1: dispatch_kernel<1, FP8, META><<<blocks, threads, lds, s>>>(a); break;
+      case 2: dispatch_kernel<2, FP8, META><<<blocks, threads, lds, s>>>(a); break;
+      case 4: dispatch_kernel<4, FP8, META><<<blocks, threads, lds, s>>>(a); break;
+      case 7: dispatch_kernel<7, FP8, META><<<blocks, threads, lds, s>>>(a); break;
+      case 8: dispatch_kernel<8, FP8, META><<<blocks, threads, lds, s>>>(a); break;
+      default: dispatch_kernel<14, FP8, META><<<blocks, threads, lds, s>>>(a); break;
     }
     EP_LAUNCHED("dispatch_kernel");
   }
@@ -480,6 +484,17 @@ ep_status ep_handle_tensor(const ep_handle* h, int32_t which, const void** dev_p
   *dev_ptr = p;
   *numel = n;
   *elem_bytes = b;
+  return EP_OK;
+}
+
+ep_status ep_debug_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
+  if (n < 0) return fail(EP_ERR_SHAPE, "n < 0");
+  if (n == 0) return EP_OK;
+  if (!in || !out) return fail(EP_ERR_NULL, "NULL argument");
+  const int64_t threads = (n + 3) / 4;
+  if ((threads + 255) / 256 >= ((int64_t)1 << 31)) return fail(EP_ERR_OVERFLOW, "n too large");
+  e4m3_encode_kernel<<<(int)((threads + 255) / 256), 256, 0, (hipStream_t)stream>>>(in, out, n);
+  EP_LAUNCHED("e4m3_encode_kernel");
   return EP_OK;
 }
 

@@ -89,4 +89,14 @@ __device__ __forceinline__ uint32_t e4m3_rne(float q) {
   return sign | (a >= 0x3C800000u ? nrm : sub);
 }
 
+// The same encoding with gfx950's v_cvt_pk_fp8_f32 (OCP E4M3FN, round to
+// nearest even), two values per instruction.  An exhaustive comparison with
+// e4m3_rne over every fp32 pattern of magnitude <= 464 found no difference;
+// larger magnitudes (never produced by x / (amax / 448)) are not used.
+__device__ __forceinline__ uint32_t e4m3x4_hw(float q0, float q1, float q2, float q3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
+  return (uint32_t)w;
+}
+
 }  // namespace ep

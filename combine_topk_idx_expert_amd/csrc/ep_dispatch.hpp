@@ -67,22 +67,21 @@ __device__ __forceinline__ int64_t packed_to_row(const DispatchArgs& a, int64_t 
   return a.window_row_base[lo] + (p - a.packed_base[lo]);
 }
 
-// E4M3 codes of 8 bf16 values (packed in v) for one 128-channel block whose
-// scale is `scale` (> 0), little-endian bytes in two words.
+// E4M3 codes of 8 bf16 values (packed in v) for one 128-channel block with
+// scale `scale`: code = E4M3FN_RNE(x / scale) with IEEE fp32 division; a block
+// whose amax is 0 has scale 0 and gets the signed zero of each input.
+// Little-endian bytes in two words.
 __device__ __forceinline__ u32x2 quantize8(u32x4 v, float scale, bool zero_block) {
   u32x2 out;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t pair = v[2 * h + (k >> 1)];
-      const float xf = (k & 1) ? bf16_hi(pair) : bf16_lo(pair);
-      const uint32_t sign = (__float_as_uint(xf) >> 24) & 0x80u;
-      const uint32_t code = zero_block ? sign : e4m3_rne(xf / scale);
-      word |= code << (8 * k);
+    const uint32_t p0 = v[2 * h], p1 = v[2 * h + 1];
+    if (!zero_block) {
+      out[h] = e4m3x4_hw(bf16_lo(p0) / scale, bf16_hi(p0) / scale, bf16_lo(p1) / scale, bf16_hi(p1) / scale);
+    } else {
+      out[h] = ((p0 >> 8) & 0x80u) | ((p0 >> 16) & 0x8000u) | (((p1 >> 8) & 0x80u) << 16) |
+               ((p1 & 0x80000000u));
     }
-    out[h] = word;
   }
   return out;
 }
@@ -92,6 +91,22 @@ __device__ __forceinline__ u32x2 quantize8(u32x4 v, float scale, bool zero_block
 //   [.., + total_pad*split)           zero payload of (padding row, part)   if zero_pad
 //   [.., + ceil(sum_expanded / 64))   row metadata of 64 rows               if META
 // NC: 16-byte chunks per lane per wave (the column part is 64 * NC chunks).
+// Store pacing: after each destination row, wait until at most
+// EP_DISPATCH_ROWS_IN_FLIGHT - 1 earlier rows' stores of this wave are still
+// outstanding.  Fewer scattered writes in flight keep HBM more efficient than
+// letting every wave burst all K rows (measured on MI355X); 0 disables.
+#ifndef EP_DISPATCH_ROWS_IN_FLIGHT
+#define EP_DISPATCH_ROWS_IN_FLIGHT 1
+#endif
+template <int NC>
+__device__ __forceinline__ void store_pacing() {
+  if constexpr (EP_DISPATCH_ROWS_IN_FLIGHT > 0) {
+    constexpr int want = NC * (EP_DISPATCH_ROWS_IN_FLIGHT - 1);
+    constexpr int allow = want < 15 ? want : 15;  // the vmcnt field holds 0..15 here
+    __builtin_amdgcn_s_waitcnt(0x0F70 | allow);  // vmcnt(allow), expcnt/lgkmcnt unchanged
+  }
+}
+
 template <int NC, bool FP8, bool META>
 __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
   const int gw = wave_index();
@@ -107,7 +122,10 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
     const int part = gw - u * a.split;
     const int tile = part * NC * kWave;
     const u32x4* src = (const u32x4*)(a.x + (int64_t)u * a.H);
-    const int32_t* rows = a.dst_row + (int64_t)u * a.K;
+    // All K destination rows in one vector load (lane j holds row j), issued
+    // before any store: the stores could alias the table as far as the compiler
+    // knows, so per-slot loads inside the store loop would each wait for memory.
+    const int my_row = lane < a.K ? a.dst_row[(int64_t)u * a.K + lane] : -1;
     u32x4 v[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -116,7 +134,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
     }
     if constexpr (!FP8) {
       for (int j = 0; j < a.K; ++j) {
-        const int row = rows[j];
+        const int row = __builtin_amdgcn_readlane(my_row, j);
         if (row < 0) continue;
         u32x4* dst = (u32x4*)(recv + (int64_t)row * out_row_bytes);
 #pragma unroll
@@ -124,6 +142,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
           const int q = tile + c * kWave + lane;
           if (q < nchunk) dst[q] = v[c];
         }
+        store_pacing<NC>();
       }
     } else {
       u32x2 codes[NC];
@@ -140,7 +159,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
         if ((lane & 15) == 0 && q < nchunk) a.tok_scales[(int64_t)u * nblk + (q >> 4)] = scale;
       }
       for (int j = 0; j < a.K; ++j) {
-        const int row = rows[j];
+        const int row = __builtin_amdgcn_readlane(my_row, j);
         if (row < 0) continue;
         u32x2* dst = (u32x2*)(recv + (int64_t)row * out_row_bytes);
 #pragma unroll
@@ -148,6 +167,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
           const int q = tile + c * kWave + lane;
           if (q < nchunk) dst[q] = codes[c];
         }
+        store_pacing<NC>();
       }
     }
   } else if (gw < token_items + pad_items) {
@@ -193,6 +213,21 @@ __global__ __launch_bounds__(256) void dispatch_scales_kernel(DispatchArgs a) {
     a.recv_scales[row * nblk + b] = 0.0f;
 }
 
+// Test hook: the dispatch kernel's float -> E4M3 conversion applied to an
+// array (four values per thread, the tail padded with zeros).
+__global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* __restrict__ in, uint8_t* __restrict__ out,
+                                                          int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float f[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) f[k] = i + k < n ? in[i + k] : 0.0f;
+  const uint32_t w = e4m3x4_hw(f[0], f[1], f[2], f[3]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (i + k < n) out[i + k] = (uint8_t)(w >> (8 * k));
+}
+
 // --------------------------------------------------------------------------
 // combine
 // --------------------------------------------------------------------------
@@ -218,8 +253,9 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
   const int tile = part * NCT * kWave;
   const int lane = lane_id();
   const int nchunk = a.H >> 3;
-  const int32_t* rows = a.dst_row + (int64_t)u * a.K;
-  const float* wrow = a.w ? a.w + (int64_t)u * a.K : nullptr;
+  // the token's K rows and weights, one vector load each (lane j holds slot j)
+  const int my_row = lane < a.K ? a.dst_row[(int64_t)u * a.K + lane] : -1;
+  const float my_w = (lane < a.K && a.w) ? a.w[(int64_t)u * a.K + lane] : 1.0f;
   u32x4* dst = (u32x4*)(a.out + (int64_t)u * a.H);
 
   float acc[NCT][8];
@@ -235,8 +271,8 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int j = j0 + g;
-      row[g] = j < a.K ? rows[j] : -1;
-      wj[g] = (j < a.K && wrow) ? wrow[j] : 1.0f;
+      row[g] = j < a.K ? __builtin_amdgcn_readlane(my_row, j) : -1;
+      wj[g] = j < a.K ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j)) : 1.0f;
       if (row[g] >= 0) {
         const u32x4* src = (const u32x4*)(a.y + (int64_t)row[g] * a.H);
 #pragma unroll

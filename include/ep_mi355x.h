@@ -219,6 +219,12 @@ enum {
 ep_status ep_handle_tensor(const ep_handle *h, int32_t which, const void **dev_ptr, int64_t *numel,
                            int32_t *elem_bytes);
 
+/* Test hook, not part of the method: converts n floats (device) to OCP E4M3FN
+ * bytes (device) with the same device conversion that fp8 dispatch applies to
+ * x / scale, so that it can be compared with a reference encoder.  Async on
+ * `stream`.  Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_OVERFLOW, EP_ERR_HIP. */
+ep_status ep_debug_e4m3_encode(const float *in, uint8_t *out, int64_t n, void *stream);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char *ep_last_error(void);
 

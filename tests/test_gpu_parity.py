@@ -357,3 +357,18 @@ def test_full_size(w):
     h.free()
     del rx, sc, rw, rm, xd
     torch.cuda.empty_cache()
+
+
+def test_device_e4m3_conversion_matches_oracle():
+    """The device fp32 -> E4M3FN conversion used by fp8 dispatch, on every 53rd fp32 pattern of
+    magnitude <= 464 plus +-3 ulp around every rounding midpoint, both signs, against the oracle."""
+    pats = np.arange(0, 0x43E80001, 53, dtype=np.uint32)
+    codes = np.arange(0x7F, dtype=np.uint8)
+    vals = np.sort(oracle.e4m3_decode(codes).astype(np.float64))
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32).view(np.uint32)
+    near = (mids[:, None].astype(np.int64) + np.arange(-3, 4)[None, :]).ravel().astype(np.uint32)
+    q = np.concatenate([pats, near]).view(np.float32)
+    q = np.concatenate([q, -q])
+    say("device e4m3 conversion on", q.size, "values")
+    got = ep.debug_e4m3_encode(torch.from_numpy(q).to(DEV)).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.e4m3_encode(q))
