@@ -68,7 +68,7 @@ struct ep_handle {
   int32_t *num_tokens_per_rank, *num_tokens_per_expert, *rank_prefix_matrix, *num_recv, *n_e;
   int64_t *expert_offset, *num_expanded, *window_row_base, *recv_src_base;
   int32_t *dst_slot, *dst_row, *send_head, *recv_src_idx;
-  int32_t *pad_base, *pad_rows, *chunk_hist, *col_total, *row_slot;
+  int32_t *pad_base, *pad_rows, *chunk_hist, *chunk_excl_t, *col_total, *row_slot;
   int64_t* packed_base;
   float* tok_scales = nullptr;  // fp8 per-token scales (H % 128 == 0 only)
   int64_t* summary_dev;
@@ -146,6 +146,7 @@ ep_status allocate(ep_handle* h) {
       {(void**)&h->pad_base, (size_t)((E + 1) * 4)},
       {(void**)&h->pad_rows, (size_t)(std::max<int64_t>(max_pad, 1) * 4)},
       {(void**)&h->chunk_hist, (size_t)((int64_t)d.ncols * d.num_chunks * 4)},
+      {(void**)&h->chunk_excl_t, (size_t)((int64_t)d.ncols * d.num_chunks * 4)},
       {(void**)&h->col_total, (size_t)(d.ncols * 4)},
       {(void**)&h->summary_dev, (size_t)((kSummaryHeader + 3 * P + 1) * 8)},
       {(void**)&h->row_slot, (size_t)((T * K + max_pad) * 4)},
@@ -169,7 +170,7 @@ ep_status allocate(ep_handle* h) {
 
   h->lds_count = (size_t)(d.ncols + kChunk * ((d.P + 31) / 32) + kChunk * d.K) * 4;
   h->lds_scan = (size_t)(((d.P + 1) & ~1) * 4 + (kScanThreads / 64) * 8);
-  h->lds_finalize = (size_t)((d.E + 1) + ((d.E + 2) / 2) + 1 + kFinalizeThreads / 64) * 8;
+  h->lds_finalize = (size_t)((d.E + 1) + ((d.E + 2) / 2) + 1 + kFinalizeThreads / 64) * 8 + (size_t)d.ncols * 4;
   h->lds_rank = (size_t)((d.E + 1) + (d.P + 1) + 2 * kChunk * d.K) * 4;
   return EP_OK;
 }
@@ -195,7 +196,7 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
     EP_LAUNCHED("layout_count_kernel");
   }
   layout_scan_kernel<<<d.ncols, kScanThreads, h->lds_scan, s>>>(
-      d, h->chunk_hist, h->col_total, h->num_tokens_per_expert, h->num_tokens_per_rank,
+      d, h->chunk_hist, h->chunk_excl_t, h->col_total, h->num_tokens_per_expert, h->num_tokens_per_rank,
       h->rank_prefix_matrix);
   EP_LAUNCHED("layout_scan_kernel");
   FinalizeOut fo{h->n_e, h->expert_offset, h->num_expanded, h->window_row_base, h->num_recv,
@@ -204,11 +205,12 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
   EP_LAUNCHED("layout_finalize_kernel");
   EP_HIP(hipMemcpyAsync(h->summary_host, h->summary_dev, (size_t)(kSummaryHeader + 3 * d.P + 1) * 8,
                         hipMemcpyDeviceToHost, s));
-  if (d.num_chunks > 0) {
-    RankOut ro{h->dst_slot, h->dst_row, h->row_slot, h->send_head, h->recv_src_idx};
-    layout_rank_kernel<<<d.num_chunks, kWave, h->lds_rank, s>>>(d, topk_idx, h->chunk_hist, h->expert_offset,
-                                                                 h->window_row_base, h->packed_base,
-                                                                 h->recv_src_base, ro);
+  {
+    // at least one workgroup per expert, so that the padding rows are written even when T = 0
+    RankOut ro{h->dst_slot, h->dst_row, h->row_slot, h->send_head, h->recv_src_idx, h->pad_rows};
+    RankIn ri{h->chunk_excl_t, h->n_e, h->pad_base, h->expert_offset, h->window_row_base, h->packed_base,
+              h->recv_src_base};
+    layout_rank_kernel<<<std::max(d.num_chunks, 1), kWave, h->lds_rank, s>>>(d, topk_idx, ri, ro);
     EP_LAUNCHED("layout_rank_kernel");
   }
   EP_HIP(hipEventRecord(h->done, s));

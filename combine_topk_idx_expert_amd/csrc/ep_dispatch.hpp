@@ -95,6 +95,13 @@ __device__ __forceinline__ u32x2 quantize8(u32x4 v, float scale, bool zero_block
 // EP_DISPATCH_ROWS_IN_FLIGHT - 1 earlier rows' stores of this wave are still
 // outstanding.  Fewer scattered writes in flight keep HBM more efficient than
 // letting every wave burst all K rows (measured on MI355X); 0 disables.
+// Payload stores of dispatch are nontemporal: the expanded rows are consumed by
+// a later kernel, and streaming them past the caches measured slightly faster.
+template <typename V>
+__device__ __forceinline__ void stream_store(V* p, V v) {
+  __builtin_nontemporal_store(v, p);
+}
+
 #ifndef EP_DISPATCH_ROWS_IN_FLIGHT
 #define EP_DISPATCH_ROWS_IN_FLIGHT 1
 #endif
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const int q = tile + c * kWave + lane;
-          if (q < nchunk) dst[q] = v[c];
+          if (q < nchunk) stream_store(dst + q, v[c]);
         }
         store_pacing<NC>();
       }
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const int q = tile + c * kWave + lane;
-          if (q < nchunk) dst[q] = codes[c];
+          if (q < nchunk) stream_store(dst + q, codes[c]);
         }
         store_pacing<NC>();
       }
@@ -180,9 +187,9 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
       const int q = tile + c * kWave + lane;  // 16-byte bf16 chunk index
       if (q < nchunk) {
         if constexpr (FP8)
-          ((u32x2*)dst)[q] = u32x2{0, 0};
+          stream_store((u32x2*)dst + q, u32x2{0, 0});
         else
-          ((u32x4*)dst)[q] = u32x4{0, 0, 0, 0};
+          stream_store((u32x4*)dst + q, u32x4{0, 0, 0, 0});
       }
     }
   } else if (META) {
@@ -248,8 +255,8 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
 #pragma clang fp contract(off)
   const int gw = wave_index();
   if (gw >= a.T * a.split) return;
-  const int u = gw / a.split;
-  const int part = gw - u * a.split;
+  const int u = gw / a.split;  // ascending tokens: measured faster than descending
+  const int part = gw % a.split;
   const int tile = part * NCT * kWave;
   const int lane = lane_id();
   const int nchunk = a.H >> 3;

@@ -158,17 +158,19 @@ __global__ __launch_bounds__(64) void layout_count_kernel(LayoutDims d,
 // --------------------------------------------------------------------------
 // 2. column scans
 // --------------------------------------------------------------------------
-// One workgroup (256 threads) per column.  chunk_hist[col][chunk] becomes the
-// exclusive prefix over chunks.  Per-source-rank sums give
+// One workgroup (256 threads) per column: exclusive prefix over chunks of
+// chunk_hist[col][chunk].  Per-source-rank sums give
 // num_tokens_per_expert[s][e], num_tokens_per_rank[s][d] and
 // rank_prefix_matrix[s][d] (inclusive over s).
 // LDS: rank_sum[P] | wave sums (int64) [4]
 constexpr int kScanThreads = 256;
 
+// chunk_excl_t[chunk][col] receives the same offsets chunk-major, so that the
+// rank kernel reads its chunk's E + P offsets contiguously.
 __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
-    LayoutDims d, int32_t* __restrict__ chunk_hist, int32_t* __restrict__ col_total,
-    int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ num_tokens_per_rank,
-    int32_t* __restrict__ rank_prefix_matrix) {
+    LayoutDims d, int32_t* __restrict__ chunk_hist, int32_t* __restrict__ chunk_excl_t,
+    int32_t* __restrict__ col_total, int32_t* __restrict__ num_tokens_per_expert,
+    int32_t* __restrict__ num_tokens_per_rank, int32_t* __restrict__ rank_prefix_matrix) {
   extern __shared__ int32_t lds[];
   int32_t* rank_sum = lds;
   int64_t* wsum = (int64_t*)(lds + ((d.P + 1) & ~1));
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = base + tid * 4 + q;
-      if (i < nc) v[i] = (int32_t)run;
+      if (i < nc) chunk_excl_t[(int64_t)i * d.ncols + col] = (int32_t)run;
       run += x[q];
     }
     carry += tile_total;
@@ -247,14 +249,18 @@ struct FinalizeOut {
   int64_t* summary;         // host summary, see above
 };
 
-// LDS: g[E+1] int64 (global prefix of aligned sizes) | pad_base[E+1] int32 | wave sums
+// LDS: g[E+1] int64 (global prefix of aligned sizes) | pad_base[E+1] int32 |
+//      wave sums [16] int64 | column totals [E+P+1] int32
 __global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
-    LayoutDims d, const int32_t* __restrict__ col_total, FinalizeOut o) {
+    LayoutDims d, const int32_t* __restrict__ col_total_g, FinalizeOut o) {
   extern __shared__ int64_t lds64[];
   int64_t* g = lds64;
   int32_t* pb = (int32_t*)(lds64 + d.E + 1);
   int64_t* wsum = lds64 + d.E + 1 + ((d.E + 2) >> 1) + 1;
+  int32_t* col_total = (int32_t*)(wsum + kFinalizeThreads / 64);
   const int tid = threadIdx.x;
+  for (int i = tid; i < d.ncols; i += kFinalizeThreads) col_total[i] = col_total_g[i];
+  __syncthreads();
 
   // aligned sizes p_e = ceil(n_e / A) * A and padding p_e - n_e, scanned over e
   int64_t carry_g = 0, carry_p = 0;
@@ -332,20 +338,6 @@ __global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
     o.summary[3] = carry_r;
   }
 
-  // padding rows, as global row indices, expert-major
-  const int total_pad = pb[d.E];
-  for (int i = tid; i < total_pad; i += kFinalizeThreads) {
-    int lo = 0, hi = d.E;  // last e with pb[e] <= i
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pb[mid] <= i) lo = mid; else hi = mid;
-    }
-    const int e = lo, r = e / d.El;
-    const int64_t first_pad = (d.symmetric ? (int64_t)r * wmax : g[r * d.El]) + (g[e] - g[r * d.El]) +
-                              col_total[e];
-    o.pad_rows[i] = (int32_t)(first_pad + (i - pb[e]));
-    o.row_slot[g[e] + col_total[e] + (i - pb[e])] = -1;
-  }
 }
 
 // --------------------------------------------------------------------------
@@ -357,85 +349,114 @@ struct RankOut {
   int32_t* row_slot;      // [sum num_expanded], packed window order
   int32_t* send_head;     // [T][P]
   int32_t* recv_src_idx;  // [sum num_recv]
+  int32_t* pad_rows;      // [total padding] global rows, expert-major
 };
 
+struct RankIn {
+  const int32_t* chunk_excl_t;     // [chunk][E + P + 1]
+  const int32_t* n_e;              // [E]
+  const int32_t* pad_base;         // [E + 1]
+  const int64_t* expert_offset;    // [P][El + 1]
+  const int64_t* window_row_base;  // [P + 1]
+  const int64_t* packed_base;      // [P + 1]
+  const int64_t* recv_src_base;    // [P + 1]
+};
+
+// Also writes the padding rows of experts blockIdx.x, blockIdx.x + grid, ...:
+// pad_rows (global row) and row_slot = -1.
 // LDS: cnt_e[E+1] | cnt_r[P+1] | staged experts [64*K] | send positions [64*K]
-__global__ __launch_bounds__(64) void layout_rank_kernel(
-    LayoutDims d, const int64_t* __restrict__ topk_idx, const int32_t* __restrict__ chunk_excl,
-    const int64_t* __restrict__ expert_offset, const int64_t* __restrict__ window_row_base,
-    const int64_t* __restrict__ packed_base, const int64_t* __restrict__ recv_src_base, RankOut o) {
+__global__ __launch_bounds__(64) void layout_rank_kernel(LayoutDims d, const int64_t* __restrict__ topk_idx,
+                                                         RankIn in, RankOut o) {
   extern __shared__ int32_t lds[];
   int32_t* cnt_e = lds;
   int32_t* cnt_r = lds + d.E + 1;
   int32_t* ex = cnt_r + d.P + 1;
   int32_t* pos = ex + kChunk * d.K;
-  const ChunkPos p = chunk_pos(d);
   const int lane = threadIdx.x;
+  const int64_t* __restrict__ expert_offset = in.expert_offset;
+  const int64_t* __restrict__ window_row_base = in.window_row_base;
+  const int64_t* __restrict__ packed_base = in.packed_base;
+  const int64_t* __restrict__ recv_src_base = in.recv_src_base;
 
-  for (int i = lane; i < d.E; i += kWave) cnt_e[i] = chunk_excl[(int64_t)i * d.num_chunks + p.c];
-  for (int i = lane; i < d.P; i += kWave)
-    cnt_r[i] = chunk_excl[(int64_t)(d.E + i) * d.num_chunks + p.c];
-  if (lane == 0) {
-    cnt_e[d.E] = 0;
-    cnt_r[d.P] = 0;
+  if (blockIdx.x < d.num_chunks) {  // token part: one chunk per workgroup
+    const ChunkPos p = chunk_pos(d);
+    const int32_t* my_excl = in.chunk_excl_t + (int64_t)p.c * d.ncols;
+    for (int i = lane; i < d.E; i += kWave) cnt_e[i] = my_excl[i];
+    for (int i = lane; i < d.P; i += kWave) cnt_r[i] = my_excl[d.E + i];
+    if (lane == 0) {
+      cnt_e[d.E] = 0;
+      cnt_r[d.P] = 0;
+    }
+    stage_chunk_experts(d, p, topk_idx, ex);
+    __syncthreads();
+
+    const int total = p.n * d.K;
+    for (int base = 0; base < total; base += kWave) {  // uniform trip count
+      const int i = base + lane;
+      const bool live = i < total;
+      const int e = live ? ex[i] : -1;
+      const int t = i / d.K, j = i - t * d.K;
+      const int r = e >= 0 ? e / d.El : d.P;
+      bool first = e >= 0;  // first slot of token t on rank r
+      if (e >= 0) {         // (only lanes holding a slot read the token's earlier slots)
+        for (int jj = 0; jj < j; ++jj) {
+          const int e2 = ex[t * d.K + jj];
+          first &= !(e2 >= 0 && e2 / d.El == r);
+        }
+      }
+      const uint32_t key_e = e >= 0 ? (uint32_t)e : (uint32_t)d.E;
+      const uint32_t key_r = first ? (uint32_t)r : (uint32_t)d.P;
+      const uint64_t pe = match_any(key_e, d.ebits);
+      const uint64_t pr = match_any(key_r, d.pbits);
+      const int be = cnt_e[key_e], br = cnt_r[key_r];
+      __builtin_amdgcn_wave_barrier();
+      if (lane == 63 - __builtin_clzll(pe)) cnt_e[key_e] = be + __builtin_popcountll(pe);
+      if (lane == 63 - __builtin_clzll(pr)) cnt_r[key_r] = br + __builtin_popcountll(pr);
+      __builtin_amdgcn_wave_barrier();
+      if (live) {
+        const int64_t u = p.u0 + t;
+        if (e >= 0) {
+          const int64_t slot = expert_offset[(int64_t)r * (d.El + 1) + (e - r * d.El)] + be + count_below(pe);
+          o.dst_slot[u * d.K + j] = (int32_t)slot;
+          o.dst_row[u * d.K + j] = (int32_t)(window_row_base[r] + slot);
+          o.row_slot[packed_base[r] + slot] = (int32_t)(u * d.K + j);
+        } else {
+          o.dst_slot[u * d.K + j] = -1;
+          o.dst_row[u * d.K + j] = -1;
+        }
+        int32_t sh = -1;
+        if (first) {
+          sh = br + count_below(pr);
+          o.recv_src_idx[recv_src_base[r] + sh] = p.t0 + t;
+        }
+        pos[i] = sh;
+      }
+    }
+    __syncthreads();
+
+    // send_head rows of the chunk: one contiguous int32 range, -1 where not sent
+    int32_t* out = o.send_head + p.u0 * d.P;
+    for (int q = lane; q < p.n * d.P; q += kWave) {
+      const int t = q / d.P, r = q - t * d.P;
+      int32_t v = -1;
+      for (int j = 0; j < d.K; ++j) {
+        const int e = ex[t * d.K + j];
+        if (e >= 0 && e / d.El == r && pos[t * d.K + j] >= 0) v = pos[t * d.K + j];
+      }
+      out[q] = v;
+    }
   }
-  stage_chunk_experts(d, p, topk_idx, ex);
-  __syncthreads();
 
-  const int total = p.n * d.K;
-  for (int base = 0; base < total; base += kWave) {  // uniform trip count
-    const int i = base + lane;
-    const bool in = i < total;
-    const int e = in ? ex[i] : -1;
-    const int t = i / d.K, j = i - t * d.K;
-    const int r = e >= 0 ? e / d.El : d.P;
-    bool first = e >= 0;  // first slot of token t on rank r
-    if (e >= 0) {         // (only lanes holding a slot read the token's earlier slots)
-      for (int jj = 0; jj < j; ++jj) {
-        const int e2 = ex[t * d.K + jj];
-        first &= !(e2 >= 0 && e2 / d.El == r);
-      }
+  // padding rows: [first + n_e, first + ceil(n_e / A) * A) of each expert's segment
+  for (int e = blockIdx.x; e < d.E; e += gridDim.x) {
+    const int r = e / d.El, l = e - r * d.El;
+    const int n = in.n_e[e];
+    const int b0 = in.pad_base[e], npad = in.pad_base[e + 1] - b0;
+    const int64_t local = expert_offset[(int64_t)r * (d.El + 1) + l] + n;
+    for (int i = lane; i < npad; i += kWave) {
+      o.pad_rows[b0 + i] = (int32_t)(window_row_base[r] + local + i);
+      o.row_slot[packed_base[r] + local + i] = -1;
     }
-    const uint32_t key_e = e >= 0 ? (uint32_t)e : (uint32_t)d.E;
-    const uint32_t key_r = first ? (uint32_t)r : (uint32_t)d.P;
-    const uint64_t pe = match_any(key_e, d.ebits);
-    const uint64_t pr = match_any(key_r, d.pbits);
-    const int be = cnt_e[key_e], br = cnt_r[key_r];
-    __builtin_amdgcn_wave_barrier();
-    if (lane == 63 - __builtin_clzll(pe)) cnt_e[key_e] = be + __builtin_popcountll(pe);
-    if (lane == 63 - __builtin_clzll(pr)) cnt_r[key_r] = br + __builtin_popcountll(pr);
-    __builtin_amdgcn_wave_barrier();
-    if (in) {
-      const int64_t u = p.u0 + t;
-      if (e >= 0) {
-        const int64_t slot = expert_offset[(int64_t)r * (d.El + 1) + (e - r * d.El)] + be + count_below(pe);
-        o.dst_slot[u * d.K + j] = (int32_t)slot;
-        o.dst_row[u * d.K + j] = (int32_t)(window_row_base[r] + slot);
-        o.row_slot[packed_base[r] + slot] = (int32_t)(u * d.K + j);
-      } else {
-        o.dst_slot[u * d.K + j] = -1;
-        o.dst_row[u * d.K + j] = -1;
-      }
-      int32_t sh = -1;
-      if (first) {
-        sh = br + count_below(pr);
-        o.recv_src_idx[recv_src_base[r] + sh] = p.t0 + t;
-      }
-      pos[i] = sh;
-    }
-  }
-  __syncthreads();
-
-  // send_head rows of the chunk: one contiguous int32 range, -1 where not sent
-  int32_t* out = o.send_head + p.u0 * d.P;
-  for (int q = lane; q < p.n * d.P; q += kWave) {
-    const int t = q / d.P, r = q - t * d.P;
-    int32_t v = -1;
-    for (int j = 0; j < d.K; ++j) {
-      const int e = ex[t * d.K + j];
-      if (e >= 0 && e / d.El == r && pos[t * d.K + j] >= 0) v = pos[t * d.K + j];
-    }
-    out[q] = v;
   }
 }
 
