@@ -315,4 +315,61 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
   }
 }
 
+// Combine through LDS: one workgroup of 8 waves per (token, column part of
+// 64 * NCF chunks); wave j loads slot j's part of the row (all NCF chunks per
+// lane in flight) into LDS, then the workgroup reduces each chunk over the
+// slots in order.  K <= 8.
+template <int NCF>
+__global__ __launch_bounds__(512) void combine_lds_kernel(CombineArgs a) {
+#pragma clang fp contract(off)
+  extern __shared__ u32x4 stage[];  // [K][64 * NCF]
+  constexpr int W = NCF * kWave;
+  const int u = blockIdx.x / a.split;
+  const int tile = (blockIdx.x - u * a.split) * W;
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int nchunk = a.H >> 3;
+  const int my_row = lane < a.K ? a.dst_row[(int64_t)u * a.K + lane] : -1;
+  const float my_w = (lane < a.K && a.w) ? a.w[(int64_t)u * a.K + lane] : 1.0f;
+  if (wv < a.K) {
+    const int row = __builtin_amdgcn_readlane(my_row, wv);
+    if (row >= 0) {
+      const u32x4* src = (const u32x4*)(a.y + (int64_t)row * a.H);
+      u32x4 v[NCF];
+#pragma unroll
+      for (int c = 0; c < NCF; ++c) {
+        const int q = tile + c * kWave + lane;
+        v[c] = q < nchunk ? __builtin_nontemporal_load(src + q) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int c = 0; c < NCF; ++c) stage[wv * W + c * kWave + lane] = v[c];
+    }
+  }
+  __syncthreads();
+  u32x4* dst = (u32x4*)(a.out + (int64_t)u * a.H);
+  for (int i = threadIdx.x; i < W; i += 512) {
+    const int q = tile + i;
+    if (q >= nchunk) break;
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+    for (int j = 0; j < a.K; ++j) {
+      const int row = __builtin_amdgcn_readlane(my_row, j);
+      if (row < 0) continue;
+      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+      const u32x4 v = stage[j * W + i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float p0 = wj * bf16_lo(v[k]);
+        const float p1 = wj * bf16_hi(v[k]);
+        acc[2 * k] = acc[2 * k] + p0;
+        acc[2 * k + 1] = acc[2 * k + 1] + p1;
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(acc[2 * k], acc[2 * k + 1]);
+    dst[q] = o;
+  }
+}
+
 }  // namespace ep
