@@ -54,8 +54,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_layout.restype = i32
         L.oracle_dispatch.argtypes = [i32] * 8 + [P_] * 7 + [i64, i64] + [P_] * 4
         L.oracle_dispatch.restype = i32
+        L.oracle_dispatch_fixed.argtypes = [i32] * 8 + [P_] * 4 + [i64] + [P_] * 2 + [i64, i64] + [P_] * 5
+        L.oracle_dispatch_fixed.restype = i32
         L.oracle_combine.argtypes = [i32] * 5 + [P_] * 5 + [i64, i64, P_]
         L.oracle_combine.restype = i32
+        L.oracle_combine_fixed.argtypes = [i32] * 5 + [P_] * 2 + [i64] + [P_] * 2 + [i64, i64, P_]
+        L.oracle_combine_fixed.restype = i32
         L.oracle_combine_identity.argtypes = [i32] * 3 + [P_] * 3 + [i64, i64, P_]
         L.oracle_combine_identity.restype = i32
         L.oracle_quantize_row.argtypes = [P_, i32, P_, P_]
@@ -175,6 +179,50 @@ def dispatch(lay: Layout, H: int, x: np.ndarray, topk_weights: np.ndarray | None
     if st != OK:
         raise OracleError(st)
     return recv_x, recv_scales, recv_w, recv_meta
+
+
+def dispatch_fixed(lay: Layout, H: int, capacity: int, x: np.ndarray | None,
+                   topk_weights: np.ndarray | None, fp8: bool, zero_padding: bool, row_begin: int = 0,
+                   row_end: int | None = None, with_meta: bool = True, fill: int = 0):
+    """Fixed output length of ``capacity`` rows per window (``oracle_dispatch_fixed``):
+    rows [row_begin, row_end) of the P * capacity output ->
+    (recv_x, recv_scales, recv_weights, recv_src_meta, dropped_rows)."""
+    if row_end is None:
+        row_end = lay.P * capacity
+    n = row_end - row_begin
+    payload = x is not None
+    x = np.zeros((0,), np.uint16) if x is None else np.ascontiguousarray(x, dtype=np.uint16).reshape(lay.T, H)
+    recv_x = np.full((n, H), fill, np.uint8 if fp8 else np.uint16) if payload else None
+    recv_scales = np.zeros((n, H // 128), np.float32) if (fp8 and payload) else None
+    recv_w = np.zeros(n, np.float32) if with_meta else None
+    recv_meta = np.zeros((n, 2), np.int32) if with_meta else None
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    assert w is not None or not with_meta, "row metadata needs topk_weights"
+    dropped = np.zeros(1, np.int64)
+    st = lib().oracle_dispatch_fixed(
+        lay.P, lay.S, lay.E, lay.K, H, lay.A, int(fp8), int(zero_padding), _p(lay.topk_idx),
+        _p(lay.dst_slot), _p(lay.num_tokens_per_expert_total), _p(lay.expert_offset), capacity,
+        _p(x), _p(w), row_begin, row_end, _p(recv_x), _p(recv_scales), _p(recv_w), _p(recv_meta),
+        _p(dropped))
+    if st != OK:
+        raise OracleError(st)
+    return recv_x, recv_scales, recv_w, recv_meta, int(dropped[0])
+
+
+def combine_fixed(lay: Layout, H: int, capacity: int, y: np.ndarray, topk_weights: np.ndarray | None,
+                  tok_begin: int = 0, tok_end: int | None = None) -> np.ndarray:
+    """Combine over fixed-length windows (``oracle_combine_fixed``): y is [P * capacity, H]."""
+    if tok_end is None:
+        tok_end = lay.T
+    y = np.ascontiguousarray(y, dtype=np.uint16)
+    assert y.size >= lay.P * capacity * H
+    out = np.zeros((tok_end - tok_begin, H), np.uint16)
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    st = lib().oracle_combine_fixed(lay.P, lay.S, lay.E, lay.K, H, _p(lay.topk_idx), _p(lay.dst_slot),
+                                    capacity, _p(y), _p(w), tok_begin, tok_end, _p(out))
+    if st != OK:
+        raise OracleError(st)
+    return out
 
 
 def combine(lay: Layout, H: int, y: np.ndarray, topk_weights: np.ndarray | None,

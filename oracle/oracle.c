@@ -25,6 +25,10 @@
  *    signed-zero codes
  *  - combine: acc = +0; for j = 0..K-1: acc = fl(acc + fl(w_j * y_j)) in fp32;
  *    out = bf16 round-to-nearest-even(acc)
+ *  - fixed output length: the fixed row count applies to each rank's window of
+ *    expanded rows; the tail is zeroed whatever the zero-padding flag says;
+ *    rows past the fixed length are dropped and counted, and combine skips the
+ *    slots whose rows were dropped
  *
  * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fno-fast-math
  */
@@ -289,16 +293,22 @@ void oracle_quantize_row(const uint16_t *x, int H, uint8_t *codes, float *scales
  * do_zero_padding).  Without zero_padding their payload is left untouched.
  * Rows not covered (symmetric-window tails) are left untouched.
  *
+ * capacity > 0 is the fixed output length of every window (see
+ * oracle_dispatch_fixed): window d starts at d * capacity, window-local rows
+ * >= capacity are not written, and the rows [num_expanded[d], capacity) of a
+ * window are its tail.
+ *
  * Output arrays hold only rows [row_begin, row_end): element (r, h) is at
  * (r - row_begin) * H + h.  recv_weights / recv_src_meta may be NULL (cached
  * dispatch moves payload only); recv_x may be NULL (metadata only).
  * recv_scales is used only when fp8. */
-int oracle_dispatch(int P, int S, int E, int K, int H, int A, int fp8, int zero_padding,
-                    const int64_t *topk_idx, const int32_t *dst_slot,
-                    const int32_t *num_tokens_per_expert_total, const int64_t *expert_offset,
-                    const int64_t *window_row_base, const uint16_t *x, const float *topk_weights,
-                    int64_t row_begin, int64_t row_end, void *recv_x, float *recv_scales,
-                    float *recv_weights, int32_t *recv_src_meta) {
+static int dispatch_rows(int P, int S, int E, int K, int H, int A, int fp8, int zero_padding,
+                         const int64_t *topk_idx, const int32_t *dst_slot,
+                         const int32_t *num_tokens_per_expert_total, const int64_t *expert_offset,
+                         const int64_t *window_row_base, int64_t capacity, const uint16_t *x,
+                         const float *topk_weights, int64_t row_begin, int64_t row_end,
+                         void *recv_x, float *recv_scales, float *recv_weights,
+                         int32_t *recv_src_meta) {
   if (P < 1 || E % P != 0 || H < 1 || (fp8 && H % 128 != 0)) return ORACLE_ERR_SHAPE;
   const int64_t T = (int64_t)P * S;
   const int El = E / P;
@@ -314,7 +324,9 @@ int oracle_dispatch(int P, int S, int E, int K, int H, int A, int fp8, int zero_
     for (int j = 0; j < K; j++) {
       int64_t e = topk_idx[u * K + j];
       if (e < 0) continue;
-      int64_t r = window_row_base[e / El] + dst_slot[u * K + j];
+      int64_t local = dst_slot[u * K + j];
+      if (capacity > 0 && local >= capacity) continue; /* truncated */
+      int64_t r = (capacity > 0 ? (e / El) * capacity : window_row_base[e / El]) + local;
       if (r < row_begin || r >= row_end) continue;
       int64_t rr = r - row_begin;
       if (!recv_x) {
@@ -338,8 +350,10 @@ int oracle_dispatch(int P, int S, int E, int K, int H, int A, int fp8, int zero_
     int d = e / El, l = e % El;
     int64_t n = num_tokens_per_expert_total[e];
     int64_t padded = ((n + A - 1) / A) * A;
-    int64_t first = window_row_base[d] + expert_offset[(int64_t)d * (El + 1) + l];
-    for (int64_t r = first + n; r < first + padded; r++) {
+    int64_t local0 = expert_offset[(int64_t)d * (El + 1) + l];
+    for (int64_t local = local0 + n; local < local0 + padded; local++) {
+      if (capacity > 0 && local >= capacity) break; /* truncated */
+      int64_t r = (capacity > 0 ? d * capacity : window_row_base[d]) + local;
       if (r < row_begin || r >= row_end) continue;
       int64_t rr = r - row_begin;
       if (recv_weights) recv_weights[rr] = 0.0f;
@@ -357,9 +371,79 @@ int oracle_dispatch(int P, int S, int E, int K, int H, int A, int fp8, int zero_
       }
     }
   }
+  /* Tail rows of a fixed-length window: always x / scales / weights 0 and
+   * index -1 ([BLOG] "output length"). */
+  if (capacity > 0) {
+    for (int d = 0; d < P; d++) {
+      int64_t used = expert_offset[(int64_t)d * (El + 1) + El]; /* num_expanded[d] */
+      for (int64_t local = used; local < capacity; local++) {
+        int64_t r = d * capacity + local;
+        if (r < row_begin || r >= row_end) continue;
+        int64_t rr = r - row_begin;
+        if (recv_weights) recv_weights[rr] = 0.0f;
+        if (recv_src_meta) {
+          recv_src_meta[2 * rr] = -1;
+          recv_src_meta[2 * rr + 1] = -1;
+        }
+        if (recv_x) {
+          if (fp8) {
+            memset((uint8_t *)recv_x + rr * H, 0, (size_t)H);
+            for (int b = 0; b < nb; b++) recv_scales[rr * nb + b] = 0.0f;
+          } else {
+            for (int h = 0; h < H; h++) ((uint16_t *)recv_x)[rr * H + h] = 0;
+          }
+        }
+      }
+    }
+  }
   free(codes);
   free(scales);
   return ORACLE_OK;
+}
+
+int oracle_dispatch(int P, int S, int E, int K, int H, int A, int fp8, int zero_padding,
+                    const int64_t *topk_idx, const int32_t *dst_slot,
+                    const int32_t *num_tokens_per_expert_total, const int64_t *expert_offset,
+                    const int64_t *window_row_base, const uint16_t *x, const float *topk_weights,
+                    int64_t row_begin, int64_t row_end, void *recv_x, float *recv_scales,
+                    float *recv_weights, int32_t *recv_src_meta) {
+  return dispatch_rows(P, S, E, K, H, A, fp8, zero_padding, topk_idx, dst_slot,
+                       num_tokens_per_expert_total, expert_offset, window_row_base, 0, x,
+                       topk_weights, row_begin, row_end, recv_x, recv_scales, recv_weights,
+                       recv_src_meta);
+}
+
+/* Fixed output length ([BLOG] "the output length has a dynamic and a fixed
+ * mode"): the caller fixes in advance how many rows every rank's output holds
+ * (num_worst_tokens there; here `capacity` expanded rows per window), so no
+ * count has to be read back before the output is sized.  Window d is rows
+ * [d * capacity, (d + 1) * capacity) and holds the first min(num_expanded[d],
+ * capacity) rows of the exact window, at the same window-local index.
+ *  - num_expanded[d] < capacity: the rest is the tail, with payload, scales
+ *    and weights 0 and index (-1, -1), whatever zero_padding says.
+ *  - num_expanded[d] > capacity: the rows from capacity on are not published.
+ *    The page's implementation drops them silently; here *dropped receives
+ *    sum_d max(0, num_expanded[d] - capacity), the rows left out.
+ * Rows [row_begin, row_end) of the P * capacity output, as oracle_dispatch. */
+int oracle_dispatch_fixed(int P, int S, int E, int K, int H, int A, int fp8, int zero_padding,
+                          const int64_t *topk_idx, const int32_t *dst_slot,
+                          const int32_t *num_tokens_per_expert_total,
+                          const int64_t *expert_offset, int64_t capacity, const uint16_t *x,
+                          const float *topk_weights, int64_t row_begin, int64_t row_end,
+                          void *recv_x, float *recv_scales, float *recv_weights,
+                          int32_t *recv_src_meta, int64_t *dropped) {
+  if (capacity < 1 || P < 1 || E % P != 0) return ORACLE_ERR_SHAPE;
+  const int El = E / P;
+  int64_t drop = 0;
+  for (int d = 0; d < P; d++) {
+    int64_t used = expert_offset[(int64_t)d * (El + 1) + El];
+    if (used > capacity) drop += used - capacity;
+  }
+  if (dropped) *dropped = drop;
+  return dispatch_rows(P, S, E, K, H, A, fp8, zero_padding, topk_idx, dst_slot,
+                       num_tokens_per_expert_total, expert_offset, NULL, capacity, x,
+                       topk_weights, row_begin, row_end, recv_x, recv_scales, recv_weights,
+                       recv_src_meta);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -374,13 +458,15 @@ int oracle_dispatch(int P, int S, int E, int K, int H, int A, int fp8, int zero_
  *     acc = fl(acc + fl(w[u][j] * float(y[window_row_base[rank(e)] + dst_slot[u][j]][h])))
  *   out[u][h] = bf16(acc)
  * topk_weights == NULL means every weight is 1.
+ * capacity > 0: fixed-length windows (oracle_dispatch_fixed): row
+ * rank(e) * capacity + dst_slot, and a slot whose row was not published
+ * (dst_slot >= capacity) is skipped like an unused one.
  * out holds only tokens [tok_begin, tok_end). */
-int oracle_combine(int P, int S, int E, int K, int H, const int64_t *topk_idx,
-                   const int32_t *dst_slot, const int64_t *window_row_base, const uint16_t *y,
-                   const float *topk_weights, int64_t tok_begin, int64_t tok_end,
-                   uint16_t *out) {
+static int combine_rows(int P, int E, int K, int H, const int64_t *topk_idx,
+                        const int32_t *dst_slot, const int64_t *window_row_base,
+                        int64_t capacity, const uint16_t *y, const float *topk_weights,
+                        int64_t tok_begin, int64_t tok_end, uint16_t *out) {
   if (P < 1 || E % P != 0) return ORACLE_ERR_SHAPE;
-  (void)S;
   const int El = E / P;
   for (int64_t u = tok_begin; u < tok_end; u++) {
     for (int h = 0; h < H; h++) {
@@ -388,7 +474,9 @@ int oracle_combine(int P, int S, int E, int K, int H, const int64_t *topk_idx,
       for (int j = 0; j < K; j++) {
         int64_t e = topk_idx[u * K + j];
         if (e < 0) continue;
-        int64_t r = window_row_base[e / El] + dst_slot[u * K + j];
+        int64_t local = dst_slot[u * K + j];
+        if (capacity > 0 && local >= capacity) continue;
+        int64_t r = (capacity > 0 ? (e / El) * capacity : window_row_base[e / El]) + local;
         float w = topk_weights ? topk_weights[u * K + j] : 1.0f;
         float prod = w * oracle_bf16_to_float(y[r * H + h]);
         acc = acc + prod;
@@ -397,6 +485,25 @@ int oracle_combine(int P, int S, int E, int K, int H, const int64_t *topk_idx,
     }
   }
   return ORACLE_OK;
+}
+
+int oracle_combine(int P, int S, int E, int K, int H, const int64_t *topk_idx,
+                   const int32_t *dst_slot, const int64_t *window_row_base, const uint16_t *y,
+                   const float *topk_weights, int64_t tok_begin, int64_t tok_end,
+                   uint16_t *out) {
+  (void)S;
+  return combine_rows(P, E, K, H, topk_idx, dst_slot, window_row_base, 0, y, topk_weights,
+                      tok_begin, tok_end, out);
+}
+
+int oracle_combine_fixed(int P, int S, int E, int K, int H, const int64_t *topk_idx,
+                         const int32_t *dst_slot, int64_t capacity, const uint16_t *y,
+                         const float *topk_weights, int64_t tok_begin, int64_t tok_end,
+                         uint16_t *out) {
+  (void)S;
+  if (capacity < 1) return ORACLE_ERR_SHAPE;
+  return combine_rows(P, E, K, H, topk_idx, dst_slot, NULL, capacity, y, topk_weights,
+                      tok_begin, tok_end, out);
 }
 
 /* combine(identity_expert(dispatch(x))) for tokens [tok_begin, tok_end),

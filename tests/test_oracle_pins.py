@@ -469,3 +469,115 @@ def test_combine_identity_fp8_error_bound():
     bound = sw * (2.0 ** -4 * np.abs(xf) + 2.0 ** -8 * np.abs(xf)) + 2.0 ** -7 * np.abs(xf * sw) + 1e-30
     scale_floor = np.repeat(np.abs(xf).reshape(w.T, -1, 128).max(2) / 448 * 2.0 ** -9, 128, axis=1)
     assert np.all(np.abs(out - xf * sw) <= bound + sw * scale_floor)
+
+
+# ---------------------------------------------------------------------------
+# fixed output length ("Ascend DeepEP MoE Dispatch Optimization", section on the
+# dynamic and fixed output-length modes)
+# ---------------------------------------------------------------------------
+
+
+def test_fixed_length_worked_example_from_pages(golden):
+    """The page's example: a rank that receives 237 rows, exposed as 256 rows, the last 19
+    of them padding (index -1, x / weights 0) -- also without the zero-padding flag."""
+    ex = golden["num_worst_tokens_example"]
+    valid, public, tail = ex["valid_rows"], ex["public_rows"], ex["padding_rows"]
+    assert valid + tail == public
+    P, S, E, K, A, H = 2, 200, 4, 1, 1, 128
+    topk = np.full((P * S, K), -1, np.int64)
+    topk[:valid, 0] = np.arange(valid) % 2          # rank 0's experts 0 and 1
+    topk[valid:valid + 120, 0] = 2 + np.arange(120) % 2  # rank 1: 120 rows
+    x = synth.gen_bf16_rows(5, 1, P * S, H)
+    wt = np.linspace(0.5, 1.5, P * S * K, dtype=np.float32).reshape(P * S, K)
+    lay = oracle.layout(P, S, E, K, A, topk)
+    assert int(lay.num_expanded[0]) == valid
+    rx, _, rw, meta, dropped = oracle.dispatch_fixed(lay, H, public, x, wt, False, False, fill=0xFFFF)
+    assert dropped == 0 and rx.shape == (P * public, H)
+    # rank 0: the first 237 rows hold the tokens, the last 19 are the tail
+    assert np.all(meta[:valid, 0] >= 0)
+    assert np.all(meta[valid:public] == -1) and np.all(rw[valid:public] == 0)
+    assert np.all(rx[valid:public] == 0)
+    assert (meta[:public, 0] < 0).sum() == tail
+    for r in range(valid):
+        u = meta[r, 0]
+        np.testing.assert_array_equal(rx[r], x[u])
+    # rank 1: 120 rows then 136 tail rows
+    assert np.all(meta[public:public + 120, 0] >= 0) and np.all(meta[public + 120:] == -1)
+
+
+def _exact_and_fixed(w, topk, W, fp8, zero_padding, seed):
+    x = synth.gen_bf16_rows(seed, 1, w.T, w.H)
+    wt = synth.gen_weights(w)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    ex = oracle.dispatch(lay, w.H, x, wt, fp8, zero_padding, fill=0xAB)
+    fx = oracle.dispatch_fixed(lay, w.H, W, x, wt, fp8, zero_padding, fill=0xCD)
+    return lay, x, wt, ex, fx
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("zero_padding", [True, False])
+def test_fixed_length_is_exact_window_plus_tail(fp8, zero_padding):
+    """With a capacity at least every window's rows, window d of the fixed output is the
+    exact window d followed by a zero tail (index -1): the same rows at the same
+    window-local positions, nothing dropped."""
+    w = small_workload(P=4, S=64, E=16, K=3, H=256, A=16, seed=31)
+    topk = synth.gen_routing(w).copy()
+    topk[::11, 1] = -1
+    lay0 = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    W = int(lay0.num_expanded.max()) + 37
+    lay, x, wt, (erx, esc, erw, emeta), (frx, fsc, frw, fmeta, dropped) = _exact_and_fixed(
+        w, topk, W, fp8, zero_padding, 32)
+    assert dropped == 0
+    for d in range(w.P):
+        b, n = int(lay.window_row_base[d]), int(lay.num_expanded[d])
+        f = slice(d * W, d * W + n)
+        e = slice(b, b + n)
+        np.testing.assert_array_equal(fmeta[f], emeta[e])
+        np.testing.assert_array_equal(frw[f], erw[e])
+        defined = (emeta[e, 0] >= 0) | zero_padding  # padding payload is defined only with zero padding
+        np.testing.assert_array_equal(frx[f][defined], erx[e][defined])
+        if fp8:
+            np.testing.assert_array_equal(fsc[f][defined], esc[e][defined])
+        t = slice(d * W + n, (d + 1) * W)
+        assert np.all(fmeta[t] == -1) and np.all(frw[t] == 0) and np.all(frx[t] == 0)
+        if fp8:
+            assert np.all(fsc[t] == 0)
+    # combine over the fixed windows equals the exact combine bit for bit
+    y_exact = erx if not fp8 else oracle.dispatch(lay, w.H, x, wt, False, True)[0]
+    y_fixed = frx if not fp8 else oracle.dispatch_fixed(lay, w.H, W, x, wt, False, True)[0]
+    np.testing.assert_array_equal(oracle.combine_fixed(lay, w.H, W, y_fixed, wt),
+                                  oracle.combine(lay, w.H, y_exact, wt))
+
+
+@pytest.mark.parametrize("A", [1, 8])
+def test_fixed_length_truncation_drops_tail_rows_and_their_slots(A):
+    """A capacity below some window's row count publishes the first W rows of each window;
+    the dropped count is sum_d max(0, num_expanded[d] - W) (num_expanded from its closed
+    form); combine then equals the exact combine with the dropped slots' weights zeroed."""
+    w = small_workload(P=4, S=80, E=16, K=4, H=128, A=A, routing="zipf", seed=33)
+    topk = synth.gen_routing(w)
+    n = np.bincount(topk[topk >= 0], minlength=w.E)
+    ne = (-(-n // A) * A).reshape(w.P, -1).sum(1)
+    W = int(np.sort(ne)[w.P // 2])  # about half the windows overflow
+    assert (ne > W).any() and (ne < W).any()
+    lay, x, wt, (erx, _, erw, emeta), (frx, _, frw, fmeta, dropped) = _exact_and_fixed(
+        w, topk, W, False, True, 34)
+    assert dropped == int(np.maximum(ne - W, 0).sum())
+    for d in range(w.P):
+        b, k = int(lay.window_row_base[d]), min(int(ne[d]), W)
+        np.testing.assert_array_equal(fmeta[d * W:d * W + k], emeta[b:b + k])
+        np.testing.assert_array_equal(frx[d * W:d * W + k], erx[b:b + k])
+        np.testing.assert_array_equal(frw[d * W:d * W + k], erw[b:b + k])
+        assert np.all(fmeta[d * W + k:(d + 1) * W] == -1)
+    # every published slot appears once; the others are the slots whose row index reached W
+    kept = fmeta[fmeta[:, 0] >= 0]
+    trunc = np.zeros((w.T, w.K), bool)
+    for u in range(w.T):
+        for j in range(w.K):
+            if topk[u, j] >= 0 and lay.dst_slot[u, j] >= W:
+                trunc[u, j] = True
+    assert len(kept) == int((topk >= 0).sum() - trunc.sum())
+    wt0 = wt.copy()
+    wt0[trunc] = 0.0
+    np.testing.assert_array_equal(oracle.combine_fixed(lay, w.H, W, frx, wt),
+                                  oracle.combine(lay, w.H, erx, wt0))
