@@ -23,6 +23,8 @@ from ._native import (  # noqa: F401
     EpError,
     Handle,
     LibraryMissing,
+    STATUS_ROUTING,
+    STATUS_TRUNCATED,
     Status,
     TENSORS,
     combine,

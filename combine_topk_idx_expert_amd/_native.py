@@ -9,12 +9,15 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libep_mi355x.so"
-EP_ABI_VERSION = 1
+EP_ABI_VERSION = 2
 
 # dispatch flags
 _FP8 = 1
 _ZERO_PADDING = 2
 _SYMMETRIC_WINDOWS = 1
+# ep_handle_status bits
+STATUS_ROUTING = 1
+STATUS_TRUNCATED = 2
 
 
 class Status(enum.IntEnum):
@@ -70,12 +73,15 @@ class _Config(ctypes.Structure):
         ("num_experts", ctypes.c_int32),
         ("expert_alignment", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("num_worst_rows", ctypes.c_int32),
     ]
 
 
 @dataclasses.dataclass(frozen=True)
 class Config:
-    """P virtual ranks x S tokens, hidden H, top-K of E experts, expert_alignment A."""
+    """P virtual ranks x S tokens, hidden H, top-K of E experts, expert_alignment A.
+
+    num_worst_rows > 0 fixes every window at that many expanded rows (no read-back)."""
 
     P: int
     S: int
@@ -84,10 +90,11 @@ class Config:
     E: int
     A: int
     symmetric_windows: bool = False
+    num_worst_rows: int = 0
 
     def _c(self) -> _Config:
         return _Config(self.P, self.S, self.H, self.K, self.E, self.A,
-                       _SYMMETRIC_WINDOWS if self.symmetric_windows else 0)
+                       _SYMMETRIC_WINDOWS if self.symmetric_windows else 0, self.num_worst_rows)
 
     @property
     def T(self) -> int:
@@ -121,9 +128,11 @@ def lib() -> ctypes.CDLL:
         L.ep_handle_config.argtypes = [vp, ctypes.POINTER(_Config)]
         L.ep_handle_check.argtypes = [vp, ctypes.POINTER(_Config)]
         L.ep_handle_counts.argtypes = [vp, vp, vp, vp]
+        L.ep_handle_status.argtypes = [vp, ctypes.POINTER(u32), ctypes.POINTER(i64)]
         L.ep_handle_tensor.argtypes = [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(i32)]
         for fn in ("ep_get_layout", "ep_relayout", "ep_dispatch", "ep_dispatch_cached", "ep_combine",
-                   "ep_handle_config", "ep_handle_check", "ep_handle_counts", "ep_handle_tensor"):
+                   "ep_handle_config", "ep_handle_check", "ep_handle_counts", "ep_handle_status",
+                   "ep_handle_tensor"):
             getattr(L, fn).restype = i32
         L.ep_debug_e4m3_encode.argtypes = [vp, vp, i64, vp]
         L.ep_debug_e4m3_encode.restype = i32
@@ -206,6 +215,12 @@ class Handle:
         _check(lib().ep_handle_counts(self.ptr, ne.ctypes.data, nr.ctypes.data, wb.ctypes.data))
         return ne, nr, wb
 
+    def status(self):
+        """(EP_STATUS_* flags, dropped rows) of the last layout; waits for it in fixed mode."""
+        f, d = ctypes.c_uint32(), ctypes.c_int64()
+        _check(lib().ep_handle_status(self.ptr, ctypes.byref(f), ctypes.byref(d)))
+        return f.value, d.value
+
     def tensor(self, name: str):
         """A device copy (torch tensor) of one of the handle's arrays."""
         import torch
@@ -236,7 +251,8 @@ def _hip_memcpy_d2d(dst: int, src: int, nbytes: int, stream: int) -> None:
 
 
 def get_layout(cfg: Config, topk_idx) -> Handle:
-    """ep_get_layout: topk_idx int64 [T, K] on the device -> Handle (synchronizes once)."""
+    """ep_get_layout: topk_idx int64 [T, K] on the device -> Handle (synchronizes once in exact
+    mode; only enqueues with cfg.num_worst_rows > 0)."""
     import torch
 
     _require(topk_idx, torch.int64, (cfg.T, cfg.K), "topk_idx")

@@ -58,9 +58,13 @@ struct ep_handle {
   LayoutDims dims;
   int64_t T;
   int device;
-  // read back by the layout
+  // read back by the layout (fixed windows: on first use, see ensure_counts)
   int64_t total_rows = 0, total_pad = 0, sum_recv = 0, sum_expanded = 0;
+  int64_t dropped = 0;
+  uint32_t status = 0;  // EP_STATUS_* of the last layout
   bool valid = false;
+  bool fixed = false;          // num_worst_rows > 0
+  bool counts_known = false;   // host fields above hold the last layout's summary
   // device arena and the arrays inside it
   void* arena = nullptr;
   size_t arena_bytes = 0;
@@ -70,6 +74,7 @@ struct ep_handle {
   int32_t *dst_slot, *dst_row, *send_head, *recv_src_idx;
   int32_t *pad_base, *pad_rows, *chunk_hist, *chunk_excl_t, *col_total, *row_slot;
   int64_t* packed_base;
+  int64_t* tail_base;
   float* tok_scales = nullptr;  // fp8 per-token scales (H % 128 == 0 only)
   int64_t* summary_dev;
   int64_t* summary_host = nullptr;  // pinned
@@ -94,8 +99,14 @@ ep_status validate_config(const ep_config* c) {
                 c->num_experts, c->num_ranks, EP_MAX_EXPERTS);
   if (c->expert_alignment < 1) return fail(EP_ERR_SHAPE, "expert_alignment %d < 1", c->expert_alignment);
   if (c->flags & ~EP_LAYOUT_SYMMETRIC_WINDOWS) return fail(EP_ERR_SHAPE, "unknown layout flags 0x%x", c->flags);
+  if (c->num_worst_rows < 0) return fail(EP_ERR_SHAPE, "num_worst_rows %d < 0", c->num_worst_rows);
+  if (c->num_worst_rows > 0 && (c->flags & EP_LAYOUT_SYMMETRIC_WINDOWS))
+    return fail(EP_ERR_SHAPE, "num_worst_rows fixes the window size; EP_LAYOUT_SYMMETRIC_WINDOWS must be unset");
   const int64_t T = (int64_t)c->num_ranks * c->num_tokens;
   const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)c->num_ranks * c->num_worst_rows >= lim)
+    return fail(EP_ERR_OVERFLOW, "P * num_worst_rows = %lld reaches 2^31",
+                (long long)((int64_t)c->num_ranks * c->num_worst_rows));
   if (T * c->num_topk >= lim) return fail(EP_ERR_OVERFLOW, "T*K = %lld reaches 2^31", (long long)(T * c->num_topk));
   if (T * c->num_ranks >= lim) return fail(EP_ERR_OVERFLOW, "T*P = %lld reaches 2^31", (long long)(T * c->num_ranks));
   const int64_t max_rows = T * c->num_topk + (int64_t)c->num_experts * (c->expert_alignment - 1);
@@ -117,6 +128,7 @@ LayoutDims make_dims(const ep_config& c) {
   d.ebits = bits_for((uint32_t)d.E);
   d.pbits = bits_for((uint32_t)d.P);
   d.symmetric = (c.flags & EP_LAYOUT_SYMMETRIC_WINDOWS) ? 1 : 0;
+  d.cap = c.num_worst_rows;
   return d;
 }
 
@@ -151,6 +163,7 @@ ep_status allocate(ep_handle* h) {
       {(void**)&h->summary_dev, (size_t)((kSummaryHeader + 3 * P + 1) * 8)},
       {(void**)&h->row_slot, (size_t)((T * K + max_pad) * 4)},
       {(void**)&h->packed_base, (size_t)((P + 1) * 8)},
+      {(void**)&h->tail_base, (size_t)((P + 1) * 8)},
       {(void**)&h->tok_scales, (size_t)(h->cfg.hidden % 128 == 0 ? T * (h->cfg.hidden / 128) * 4 : 0)},
   };
   size_t total = 0;
@@ -200,7 +213,8 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
       h->rank_prefix_matrix);
   EP_LAUNCHED("layout_scan_kernel");
   FinalizeOut fo{h->n_e, h->expert_offset, h->num_expanded, h->window_row_base, h->num_recv,
-                 h->recv_src_base, h->pad_base, h->pad_rows, h->packed_base, h->row_slot, h->summary_dev};
+                 h->recv_src_base, h->pad_base, h->pad_rows, h->packed_base, h->row_slot, h->tail_base,
+                 h->summary_dev};
   layout_finalize_kernel<<<1, kFinalizeThreads, h->lds_finalize, s>>>(d, h->col_total, fo);
   EP_LAUNCHED("layout_finalize_kernel");
   EP_HIP(hipMemcpyAsync(h->summary_host, h->summary_dev, (size_t)(kSummaryHeader + 3 * d.P + 1) * 8,
@@ -214,6 +228,13 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
     EP_LAUNCHED("layout_rank_kernel");
   }
   EP_HIP(hipEventRecord(h->done, s));
+  h->counts_known = false;
+  if (h->fixed) {  // fixed windows: nothing to wait for
+    h->total_rows = (int64_t)d.P * d.cap;
+    h->valid = true;
+    if (total_rows) *total_rows = h->total_rows;
+    return EP_OK;
+  }
   EP_HIP(hipEventSynchronize(h->done));
   const int64_t* sm = h->summary_host;
   if (sm[2] != 0) return fail(EP_ERR_ROUTING, "topk_idx holds an expert id outside {-1} U [0, %d)", d.E);
@@ -224,8 +245,28 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
   h->sum_expanded = 0;
   for (int r = 0; r < d.P; ++r) h->sum_expanded += sm[kSummaryHeader + r];
   h->sum_recv = sm[3];
+  h->status = 0;
+  h->dropped = 0;
+  h->counts_known = true;
   h->valid = true;
   if (total_rows) *total_rows = h->total_rows;
+  return EP_OK;
+}
+
+// Fixed windows: wait for the last layout and take its summary (host fields
+// are mutable caches of device results).
+ep_status ensure_counts(const ep_handle* hc) {
+  ep_handle* h = const_cast<ep_handle*>(hc);
+  if (h->counts_known) return EP_OK;
+  EP_HIP(hipEventSynchronize(h->done));
+  const int64_t* sm = h->summary_host;
+  h->total_pad = sm[1];
+  h->sum_recv = sm[3];
+  h->sum_expanded = 0;
+  for (int r = 0; r < h->dims.P; ++r) h->sum_expanded += sm[kSummaryHeader + r];
+  h->dropped = sm[5];
+  h->status = (sm[2] != 0 ? EP_STATUS_ROUTING : 0u) | (sm[5] > 0 ? EP_STATUS_TRUNCATED : 0u);
+  h->counts_known = true;
   return EP_OK;
 }
 
@@ -267,12 +308,19 @@ int pick_nc(int H, int want) {
 
 int parts_per_row(int H, int nc) { return ((H >> 3) + nc * kWave - 1) / (nc * kWave); }
 
+// Fixed windows: waves that stride over the padding and tail rows, whose
+// number only the device knows (at most P * cap rows).
+constexpr int64_t kZeroWaves = 16384;
+
 template <bool FP8, bool META>
 ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
   const int nc = pick_nc(a.H, FP8 ? EP_DISPATCH_NC_FP8 : EP_DISPATCH_NC_BF16);
   a.split = parts_per_row(a.H, nc);
-  const int64_t meta_items = META ? ((int64_t)a.sum_expanded + kWave - 1) / kWave : 0;
-  const int64_t waves = ((int64_t)a.T + (a.zero_pad ? a.total_pad : 0)) * a.split + meta_items;
+  const int64_t out_rows = a.cap > 0 ? (int64_t)a.P * a.cap : (int64_t)a.sum_expanded;
+  const int64_t meta_items = META ? (out_rows + kWave - 1) / kWave : 0;
+  a.zero_waves = a.cap > 0 ? (int)std::min<int64_t>((int64_t)a.P * a.cap * a.split, kZeroWaves) : 0;
+  const int64_t zero_items = a.cap > 0 ? a.zero_waves : (a.zero_pad ? (int64_t)a.total_pad * a.split : 0);
+  const int64_t waves = (int64_t)a.T * a.split + zero_items + meta_items;
   if (waves >= ((int64_t)1 << 31) / kWave) return fail(EP_ERR_OVERFLOW, "dispatch grid too large (%lld waves)", (long long)waves);
   if (waves > 0) {
     const int threads = EP_ROW_BLOCK_WAVES * kWave;
@@ -289,7 +337,7 @@ ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
     EP_LAUNCHED("dispatch_kernel");
   }
   if constexpr (FP8) {
-    const int64_t n = (int64_t)a.sum_expanded * (a.H >> 7);
+    const int64_t n = out_rows * (a.H >> 7);
     if (n > 0) {
       if (n >= ((int64_t)1 << 31)) return fail(EP_ERR_OVERFLOW, "scale grid too large");
       dispatch_scales_kernel<<<(int)((n + 255) / 256), 256, 0, s>>>(a);
@@ -341,6 +389,11 @@ ep_status dispatch_common(const ep_handle* h, uint32_t flags, const void* x, con
   a.split = 1;
   a.zero_pad = zero_pad ? 1 : 0;
   a.symmetric = h->dims.symmetric;
+  a.cap = h->dims.cap;
+  a.zero_waves = 0;
+  a.counts = h->summary_dev;
+  a.tail_base = h->tail_base;
+  a.num_expanded = h->num_expanded;
   if (fp8) return meta ? launch_dispatch<true, true>(a, s) : launch_dispatch<true, false>(a, s);
   return meta ? launch_dispatch<false, true>(a, s) : launch_dispatch<false, false>(a, s);
 }
@@ -362,6 +415,7 @@ ep_status ep_get_layout(const ep_config* cfg, const int64_t* topk_idx, void* str
   h->cfg = *cfg;
   h->dims = make_dims(*cfg);
   h->T = T;
+  h->fixed = cfg->num_worst_rows > 0;
   if (hipGetDevice(&h->device) != hipSuccess) {
     delete h;
     return fail(EP_ERR_HIP, "no HIP device");
@@ -459,24 +513,37 @@ ep_status ep_handle_check(const ep_handle* h, const ep_config* cfg) {
   const ep_config& a = h->cfg;
   if (a.num_ranks != cfg->num_ranks || a.num_tokens != cfg->num_tokens || a.hidden != cfg->hidden ||
       a.num_topk != cfg->num_topk || a.num_experts != cfg->num_experts ||
-      a.expert_alignment != cfg->expert_alignment || a.flags != cfg->flags)
+      a.expert_alignment != cfg->expert_alignment || a.flags != cfg->flags ||
+      a.num_worst_rows != cfg->num_worst_rows)
     return fail(EP_ERR_HANDLE_MISMATCH,
-                "handle built for P=%d S=%d H=%d K=%d E=%d A=%d flags=%u, got P=%d S=%d H=%d K=%d E=%d A=%d flags=%u",
+                "handle built for P=%d S=%d H=%d K=%d E=%d A=%d flags=%u W=%d, got P=%d S=%d H=%d K=%d E=%d A=%d "
+                "flags=%u W=%d",
                 a.num_ranks, a.num_tokens, a.hidden, a.num_topk, a.num_experts, a.expert_alignment, a.flags,
-                cfg->num_ranks, cfg->num_tokens, cfg->hidden, cfg->num_topk, cfg->num_experts,
-                cfg->expert_alignment, cfg->flags);
+                a.num_worst_rows, cfg->num_ranks, cfg->num_tokens, cfg->hidden, cfg->num_topk, cfg->num_experts,
+                cfg->expert_alignment, cfg->flags, cfg->num_worst_rows);
   return EP_OK;
 }
 
 ep_status ep_handle_counts(const ep_handle* h, int64_t* num_expanded, int64_t* num_recv_tokens,
                            int64_t* window_row_base) {
   ep_status st = check_handle(h);
+  if (st == EP_OK) st = ensure_counts(h);
   if (st != EP_OK) return st;
   const int P = h->dims.P;
   const int64_t* sm = h->summary_host + kSummaryHeader;
   if (num_expanded) memcpy(num_expanded, sm, P * 8);
   if (num_recv_tokens) memcpy(num_recv_tokens, sm + P, P * 8);
   if (window_row_base) memcpy(window_row_base, sm + 2 * P, (P + 1) * 8);
+  return EP_OK;
+}
+
+ep_status ep_handle_status(const ep_handle* h, uint32_t* flags, int64_t* dropped_rows) {
+  if (!flags) return fail(EP_ERR_NULL, "flags is NULL");
+  ep_status st = check_handle(h);
+  if (st == EP_OK) st = ensure_counts(h);
+  if (st != EP_OK) return st;
+  *flags = h->status;
+  if (dropped_rows) *dropped_rows = h->dropped;
   return EP_OK;
 }
 
@@ -501,7 +568,12 @@ ep_status ep_handle_tensor(const ep_handle* h, int32_t which, const void** dev_p
     case EP_T_WINDOW_ROW_BASE: p = h->window_row_base; n = P + 1; b = 8; break;
     case EP_T_DST_SLOT: p = h->dst_slot; n = T * K; break;
     case EP_T_SEND_HEAD: p = h->send_head; n = T * P; break;
-    case EP_T_RECV_SRC_IDX: p = h->recv_src_idx; n = h->sum_recv; break;
+    case EP_T_RECV_SRC_IDX:
+      st = ensure_counts(h);
+      if (st != EP_OK) return st;
+      p = h->recv_src_idx;
+      n = h->sum_recv;
+      break;
     case EP_T_RECV_SRC_BASE: p = h->recv_src_base; n = P + 1; b = 8; break;
     case EP_T_DST_ROW: p = h->dst_row; n = T * K; break;
     default: return fail(EP_ERR_SHAPE, "unknown tensor id %d", which);

@@ -49,6 +49,12 @@ struct DispatchArgs {
   int total_pad, sum_expanded;
   int split;                     // parts per row = ceil((H / 8) / (64 * NC))
   int zero_pad, symmetric;
+  // fixed windows of cap rows (cap > 0); the row counts are known on the device only
+  int cap;
+  int zero_waves;                // waves that share the padding / tail rows
+  const int64_t* counts;         // layout summary: [1] padding rows, [4] tail rows
+  const int64_t* tail_base;      // [P+1]
+  const int64_t* num_expanded;   // [P]
 };
 
 // Wave-uniform global wave index of the calling lane.
@@ -86,10 +92,34 @@ __device__ __forceinline__ u32x2 quantize8(u32x4 v, float scale, bool zero_block
   return out;
 }
 
+// Row of the k-th tail row of fixed windows: tail rows are the last
+// tail_base[r+1] - tail_base[r] rows of window r.
+__device__ __forceinline__ int64_t tail_row(const DispatchArgs& a, int64_t k) {
+  int lo = 0, hi = a.P;  // last window with tail_base <= k
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.tail_base[mid] <= k) lo = mid; else hi = mid;
+  }
+  const int64_t len = a.tail_base[lo + 1] - a.tail_base[lo];
+  return (int64_t)lo * a.cap + (a.cap - len) + (k - a.tail_base[lo]);
+}
+
+// Source slot of output row g of fixed windows: -1 for padding and tail rows.
+__device__ __forceinline__ int fixed_row_slot(const DispatchArgs& a, int64_t g) {
+  const int r = (int)(g / a.cap);
+  const int64_t l = g - (int64_t)r * a.cap;
+  return l < a.num_expanded[r] ? a.row_slot[a.packed_base[r] + l] : -1;
+}
+
 // Work items, in grid order:
 //   [0, T*split)                      payload of (token, part)
+//   exact windows:
 //   [.., + total_pad*split)           zero payload of (padding row, part)   if zero_pad
 //   [.., + ceil(sum_expanded / 64))   row metadata of 64 rows               if META
+//   fixed windows (cap > 0), counts read on the device:
+//   [.., + zero_waves)                waves striding over (padding row, part) if zero_pad
+//                                     and (tail row, part)
+//   [.., + ceil(P * cap / 64))        row metadata of 64 rows               if META
 // NC: 16-byte chunks per lane per wave (the column part is 64 * NC chunks).
 // Store pacing: after each destination row, wait until at most
 // EP_DISPATCH_ROWS_IN_FLIGHT - 1 earlier rows' stores of this wave are still
@@ -114,6 +144,23 @@ __device__ __forceinline__ void store_pacing() {
   }
 }
 
+template <int NC, bool FP8>
+__device__ __forceinline__ void zero_row_part(uint8_t* recv, int64_t row, int part, int64_t out_row_bytes,
+                                              int nchunk, int lane) {
+  uint8_t* dst = recv + row * out_row_bytes;
+  const int tile = part * NC * kWave;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int q = tile + c * kWave + lane;  // 16-byte bf16 chunk index
+    if (q < nchunk) {
+      if constexpr (FP8)
+        stream_store((u32x2*)dst + q, u32x2{0, 0});
+      else
+        stream_store((u32x4*)dst + q, u32x4{0, 0, 0, 0});
+    }
+  }
+}
+
 template <int NC, bool FP8, bool META>
 __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
   const int gw = wave_index();
@@ -122,7 +169,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
   const int64_t out_row_bytes = FP8 ? (int64_t)a.H : (int64_t)a.H * 2;
   uint8_t* recv = (uint8_t*)a.recv_x;
   const int token_items = a.T * a.split;
-  const int pad_items = a.zero_pad ? a.total_pad * a.split : 0;
+  const int pad_items = a.cap > 0 ? a.zero_waves : a.zero_pad ? a.total_pad * a.split : 0;
 
   if (gw < token_items) {
     const int u = gw / a.split;
@@ -178,45 +225,67 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
       }
     }
   } else if (gw < token_items + pad_items) {
-    const int p = (gw - token_items) / a.split;
-    const int part = (gw - token_items) - p * a.split;
-    uint8_t* dst = recv + (int64_t)a.pad_rows[p] * out_row_bytes;
-    const int tile = part * NC * kWave;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int q = tile + c * kWave + lane;  // 16-byte bf16 chunk index
-      if (q < nchunk) {
-        if constexpr (FP8)
-          stream_store((u32x2*)dst + q, u32x2{0, 0});
-        else
-          stream_store((u32x4*)dst + q, u32x4{0, 0, 0, 0});
+    if (a.cap == 0) {
+      const int p = (gw - token_items) / a.split;
+      const int part = (gw - token_items) - p * a.split;
+      zero_row_part<NC, FP8>(recv, a.pad_rows[p], part, out_row_bytes, nchunk, lane);
+    } else {
+      // fixed windows: padding rows (if asked) then tail rows (always), counted on the device
+      const int64_t npad = a.counts[1], ntail = a.counts[4];
+      const int64_t z0 = a.zero_pad ? 0 : npad;
+      const int64_t nitems = (npad + ntail - z0) * a.split;
+      for (int64_t it = gw - token_items; it < nitems; it += a.zero_waves) {
+        const int64_t z = z0 + it / a.split;
+        const int part = (int)(it - (z - z0) * a.split);
+        const int64_t row = z < npad ? (int64_t)a.pad_rows[z] : tail_row(a, z - npad);
+        zero_row_part<NC, FP8>(recv, row, part, out_row_bytes, nchunk, lane);
       }
     }
   } else if (META) {
     const int64_t pr = (int64_t)(gw - token_items - pad_items) * kWave + lane;
-    if (pr < a.sum_expanded) {
-      const int slot = a.row_slot[pr];
-      const int64_t row = packed_to_row(a, pr);
-      const int u = slot >= 0 ? slot / a.K : -1;
-      a.recv_weights[row] = slot >= 0 ? a.w[slot] : 0.0f;
-      ((int2*)a.recv_meta)[row] = make_int2(u, slot >= 0 ? slot - u * a.K : -1);
+    int slot;
+    int64_t row;
+    if (a.cap == 0) {
+      if (pr >= a.sum_expanded) return;
+      slot = a.row_slot[pr];
+      row = packed_to_row(a, pr);
+    } else {
+      if (pr >= (int64_t)a.P * a.cap) return;
+      slot = fixed_row_slot(a, pr);
+      row = pr;
     }
+    const int u = slot >= 0 ? slot / a.K : -1;
+    a.recv_weights[row] = slot >= 0 ? a.w[slot] : 0.0f;
+    ((int2*)a.recv_meta)[row] = make_int2(u, slot >= 0 ? slot - u * a.K : -1);
   }
 }
 
 // fp8 row scales in row order: recv_scales[row][b] = scale of the row's
-// source token (0 for padding rows with zero padding; otherwise untouched).
+// source token (0 for padding rows with zero padding, otherwise untouched; 0
+// for the tail rows of fixed windows).
 __global__ __launch_bounds__(256) void dispatch_scales_kernel(DispatchArgs a) {
   const int nblk = a.H >> 7;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)a.sum_expanded * nblk) return;
+  const int64_t rows = a.cap > 0 ? (int64_t)a.P * a.cap : (int64_t)a.sum_expanded;
+  if (i >= rows * nblk) return;
   const int64_t pr = i / nblk;
   const int b = (int)(i - pr * nblk);
-  const int slot = a.row_slot[pr];
-  const int64_t row = packed_to_row(a, pr);
+  int slot;
+  int64_t row;
+  bool tail = false;
+  if (a.cap == 0) {
+    slot = a.row_slot[pr];
+    row = packed_to_row(a, pr);
+  } else {
+    row = pr;
+    const int r = (int)(pr / a.cap);
+    const int64_t l = pr - (int64_t)r * a.cap;
+    tail = l >= a.num_expanded[r];
+    slot = tail ? -1 : a.row_slot[a.packed_base[r] + l];
+  }
   if (slot >= 0)
     a.recv_scales[row * nblk + b] = a.tok_scales[(int64_t)(slot / a.K) * nblk + b];
-  else if (a.zero_pad)
+  else if (a.zero_pad || tail)
     a.recv_scales[row * nblk + b] = 0.0f;
 }
 

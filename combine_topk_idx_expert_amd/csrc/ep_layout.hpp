@@ -36,6 +36,7 @@ struct LayoutDims {
   int ebits;       // bits for expert keys 0..E (E = "no expert")
   int pbits;       // bits for rank keys 0..P (P = "not a new destination")
   int symmetric;   // window policy
+  int cap;         // fixed rows per window (0: exact windows)
 };
 
 struct ChunkPos {
@@ -229,10 +230,11 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
 // --------------------------------------------------------------------------
 // 3. finalize
 // --------------------------------------------------------------------------
-// Host summary (int64): [0] total_rows  [1] total_pad  [2] error flag
-// [3] sum of num_recv_tokens (error flag = number of out-of-range ids)  [4, 4+P) num_expanded  [4+P, 4+2P) num_recv_tokens
-// [4+2P, 5+3P) window_row_base.
-constexpr int kSummaryHeader = 4;
+// Host summary (int64): [0] total_rows  [1] total_pad (padding rows inside the
+// windows)  [2] number of out-of-range ids  [3] sum of num_recv_tokens
+// [4] tail rows of fixed windows  [5] rows dropped past fixed windows' ends
+// [6, 6+P) num_expanded  [6+P, 6+2P) num_recv_tokens  [6+2P, 7+3P) window_row_base.
+constexpr int kSummaryHeader = 6;
 constexpr int kFinalizeThreads = 1024;
 
 struct FinalizeOut {
@@ -246,6 +248,7 @@ struct FinalizeOut {
   int32_t* pad_rows;        // [E*(A-1)] capacity
   int64_t* packed_base;     // [P+1] windows laid end to end (row_slot index space)
   int32_t* row_slot;        // [sum num_expanded] source slot u*K+j of each row, -1 padding
+  int64_t* tail_base;       // [P+1] fixed windows: prefix of the tail row counts
   int64_t* summary;         // host summary, see above
 };
 
@@ -285,6 +288,29 @@ __global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
   }
   __syncthreads();
 
+  // Fixed windows keep only window-local rows < cap: the padding rows of an
+  // expert are [off + n, off + p) clipped to the window.
+  if (d.cap > 0) {
+    int64_t carry = 0;
+    for (int base = 0; base < d.E; base += kFinalizeThreads) {
+      const int e = base + tid;
+      int64_t pad = 0;
+      if (e < d.E) {
+        const int r = e / d.El;
+        const int64_t off = g[e] - g[r * d.El];
+        const int64_t n = col_total[e];
+        const int64_t pe = ((n + d.A - 1) / d.A) * d.A;
+        pad = min(off + pe, (int64_t)d.cap) - min(off + n, (int64_t)d.cap);
+      }
+      int64_t tp;
+      const int64_t xp = block_excl_scan<kFinalizeThreads>(pad, wsum, &tp);
+      if (e < d.E) pb[e] = (int32_t)(carry + xp);
+      carry += tp;
+    }
+    if (tid == 0) pb[d.E] = (int32_t)carry;
+    __syncthreads();
+  }
+
   // window sizes; packed bases are the global prefix at each window's first expert
   int64_t my_max = 0;
   for (int r = tid; r < d.P; r += kFinalizeThreads) {
@@ -306,7 +332,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
   __syncthreads();
 
   for (int r = tid; r <= d.P; r += kFinalizeThreads) {
-    const int64_t base = d.symmetric ? (int64_t)r * wmax : g[min(r, d.P) * d.El];
+    const int64_t base = d.cap > 0 ? (int64_t)r * d.cap : d.symmetric ? (int64_t)r * wmax : g[min(r, d.P) * d.El];
     o.window_row_base[r] = base;
     o.packed_base[r] = g[r * d.El];
     o.summary[kSummaryHeader + 2 * d.P + r] = base;
@@ -332,10 +358,33 @@ __global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
   }
   if (tid == 0) {
     o.recv_src_base[d.P] = carry_r;
-    o.summary[0] = d.symmetric ? (int64_t)d.P * wmax : g[d.E];
+    o.summary[0] = d.cap > 0 ? (int64_t)d.P * d.cap : d.symmetric ? (int64_t)d.P * wmax : g[d.E];
     o.summary[1] = pb[d.E];
     o.summary[2] = col_total[d.E + d.P];
     o.summary[3] = carry_r;
+  }
+
+  // fixed windows: tail rows [min(ne, cap), cap) of each window, and the rows
+  // past cap that are dropped
+  int64_t carry_t = 0, carry_d = 0;
+  if (d.cap > 0) {
+    for (int base = 0; base < d.P; base += kFinalizeThreads) {
+      const int r = base + tid;
+      const int64_t ne = r < d.P ? g[(r + 1) * d.El] - g[r * d.El] : 0;
+      const int64_t tail = r < d.P ? d.cap - min(ne, (int64_t)d.cap) : 0;
+      const int64_t drop = r < d.P ? max(ne - (int64_t)d.cap, (int64_t)0) : 0;
+      int64_t tt, td;
+      const int64_t xt = block_excl_scan<kFinalizeThreads>(tail, wsum, &tt);
+      (void)block_excl_scan<kFinalizeThreads>(drop, wsum, &td);
+      if (r < d.P) o.tail_base[r] = carry_t + xt;
+      carry_t += tt;
+      carry_d += td;
+    }
+  }
+  if (tid == 0) {
+    o.tail_base[d.P] = carry_t;
+    o.summary[4] = carry_t;
+    o.summary[5] = carry_d;
   }
 
 }
@@ -418,7 +467,8 @@ __global__ __launch_bounds__(64) void layout_rank_kernel(LayoutDims d, const int
         if (e >= 0) {
           const int64_t slot = expert_offset[(int64_t)r * (d.El + 1) + (e - r * d.El)] + be + count_below(pe);
           o.dst_slot[u * d.K + j] = (int32_t)slot;
-          o.dst_row[u * d.K + j] = (int32_t)(window_row_base[r] + slot);
+          // a row past a fixed window's end is dropped
+          o.dst_row[u * d.K + j] = (d.cap > 0 && slot >= d.cap) ? -1 : (int32_t)(window_row_base[r] + slot);
           o.row_slot[packed_base[r] + slot] = (int32_t)(u * d.K + j);
         } else {
           o.dst_slot[u * d.K + j] = -1;
@@ -447,7 +497,8 @@ __global__ __launch_bounds__(64) void layout_rank_kernel(LayoutDims d, const int
     }
   }
 
-  // padding rows: [first + n_e, first + ceil(n_e / A) * A) of each expert's segment
+  // padding rows: [first + n_e, first + ceil(n_e / A) * A) of each expert's
+  // segment (clipped to fixed windows by pad_base)
   for (int e = blockIdx.x; e < d.E; e += gridDim.x) {
     const int r = e / d.El, l = e - r * d.El;
     const int n = in.n_e[e];

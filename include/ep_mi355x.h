@@ -33,6 +33,17 @@
  *    before anything is enqueued.  ep_last_error() gives a message.
  *  - One handle may be used by any number of ep_dispatch_cached / ep_combine
  *    calls; ep_handle_free and ep_relayout require that none is in flight.
+ *  - Two output-length modes ("Ascend DeepEP MoE Dispatch Optimization",
+ *    section "Output length has a dynamic and a fixed mode"):
+ *      exact  (num_worst_rows == 0): ep_get_layout reads the per-window row
+ *             counts back once and sizes the expanded tensors exactly;
+ *      fixed  (num_worst_rows == W > 0): every window is W rows, window d is
+ *             rows [d*W, (d+1)*W), and nothing is read back: ep_get_layout /
+ *             ep_relayout only enqueue.  Rows past a window's num_expanded
+ *             (its tail) get payload 0, scales 0, weight 0, meta (-1, -1) on
+ *             every dispatch.  A window that needs more than W rows keeps its
+ *             first W; the rest are dropped (not written, and skipped by
+ *             combine) and ep_handle_status reports EP_STATUS_TRUNCATED.
  */
 #ifndef EP_MI355X_H
 #define EP_MI355X_H
@@ -43,7 +54,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 1
+#define EP_ABI_VERSION 2
 
 /* Limits of this build. */
 #define EP_MAX_RANKS 1024
@@ -79,6 +90,9 @@ typedef struct {
   int32_t num_experts;      /* E, multiple of P, <= EP_MAX_EXPERTS                       */
   int32_t expert_alignment; /* A >= 1: every expert's row count is padded to a multiple  */
   uint32_t flags;           /* EP_LAYOUT_* bits                                          */
+  int32_t num_worst_rows;   /* 0: exact output length; W > 0: fixed length of W expanded */
+                            /* rows per window (the pages' num_worst_tokens); P*W < 2^31 */
+                            /* and EP_LAYOUT_SYMMETRIC_WINDOWS unset                      */
 } ep_config;
 
 typedef struct ep_handle ep_handle; /* opaque; owns its device arrays */
@@ -106,10 +120,13 @@ typedef struct ep_handle ep_handle; /* opaque; owns its device arrays */
  *   recv_src_idx (per destination, the local token index of each received
  *   token).  Receive lists are ordered by source rank then token; the rows of
  *   one expert are ordered by (u, j) -- the tutorial's deterministic order.
- * Allocates the handle's device memory (hipMalloc) and synchronizes `stream`
- * once to read back the per-window row counts (the pages' do_cpu_sync mode).
- * Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_OVERFLOW, EP_ERR_ROUTING,
- * EP_ERR_NOMEM, EP_ERR_HIP.
+ * Allocates the handle's device memory (hipMalloc).  Exact mode: synchronizes
+ * `stream` once to read back the per-window row counts (the pages' do_cpu_sync
+ * mode).  Fixed mode: returns as soon as the work is enqueued, with
+ * total_rows = P * num_worst_rows; a routing error does not fail the call
+ * (the bad slots are treated as unused) and is reported by ep_handle_status.
+ * Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_OVERFLOW, EP_ERR_ROUTING (exact
+ * mode), EP_ERR_NOMEM, EP_ERR_HIP.
  */
 ep_status ep_get_layout(const ep_config *cfg, const int64_t *topk_idx, void *stream,
                         ep_handle **out, int64_t *total_rows);
@@ -141,7 +158,9 @@ ep_status ep_relayout(ep_handle *h, const int64_t *topk_idx, void *stream, int64
  * EP_DISPATCH_ZERO_PADDING, a zero payload (and zero scales); otherwise their
  * payload is left as it was ("Ascend DeepEP MoE Dispatch Optimization",
  * section "Output length has a dynamic and a fixed mode"; tutorial 2.2).
- * Rows past num_expanded in symmetric windows are not touched.
+ * Rows past num_expanded in symmetric windows are not touched; in fixed mode
+ * they are the tail (zero payload and scales, weight 0, meta (-1, -1)) and
+ * slots whose row would lie past the window are not written.
  * Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_HIP.
  */
 ep_status ep_dispatch(const ep_handle *h, uint32_t flags, const void *x, const float *topk_weights,
@@ -166,7 +185,8 @@ ep_status ep_dispatch_cached(const ep_handle *h, uint32_t flags, const void *x, 
  *   out           device, bf16 [T, H].
  * out[u][h] = bf16_rne(acc) with acc = +0 and, for j = 0..K-1 over valid
  * slots in order, acc = fl(acc + fl(w[u][j] * float(y[row(u,j)][h]))) in fp32
- * (no fused multiply-add).  A token without valid slots gets +0.
+ * (no fused multiply-add).  A token without valid slots gets +0.  In fixed
+ * mode a slot whose row was dropped counts as unused.
  * The backward of dispatch is this call and the backward of combine is
  * ep_dispatch_cached, with the same handle (tutorial 2.3).
  * Errors: EP_ERR_NULL, EP_ERR_HIP.
@@ -180,7 +200,8 @@ ep_status ep_combine(const ep_handle *h, const void *y, const float *topk_weight
 void ep_handle_free(ep_handle *h);
 
 /* --------------------------------------------------------------------------
- * Introspection (host-side, no device work).
+ * Introspection (host-side, no device work; in fixed mode some calls wait for
+ * the last layout, as stated).
  */
 
 /* Config the handle was built with. */
@@ -192,9 +213,19 @@ ep_status ep_handle_config(const ep_handle *h, ep_config *cfg);
 ep_status ep_handle_check(const ep_handle *h, const ep_config *cfg);
 
 /* Host copies of the read-back counts: num_expanded [P], num_recv_tokens [P],
- * window_row_base [P+1] (int64).  Any pointer may be NULL. */
+ * window_row_base [P+1] (int64).  Any pointer may be NULL.  In fixed mode the
+ * first call after a layout waits for that layout to finish. */
 ep_status ep_handle_counts(const ep_handle *h, int64_t *num_expanded, int64_t *num_recv_tokens,
                            int64_t *window_row_base);
+
+/* Outcome of the handle's last layout.  flags receives EP_STATUS_* bits;
+ * dropped_rows (may be NULL) the number of rows past a fixed window's end,
+ * sum_d max(0, num_expanded[d] - num_worst_rows).  Waits for the layout to
+ * finish (in exact mode it already has, and both are always 0).
+ * Errors: EP_ERR_NULL, EP_ERR_HANDLE_MISMATCH (no layout), EP_ERR_HIP. */
+#define EP_STATUS_ROUTING 1u   /* ids outside {-1} U [0, E) were seen and treated as unused */
+#define EP_STATUS_TRUNCATED 2u /* some window needed more than num_worst_rows rows            */
+ep_status ep_handle_status(const ep_handle *h, uint32_t *flags, int64_t *dropped_rows);
 
 /* Device arrays of the handle, for parity checks and for callers that want
  * the pages' handle tensors.  The pointer stays valid until ep_handle_free /
@@ -213,7 +244,8 @@ enum {
   EP_T_SEND_HEAD = 10,            /* i32 [T, P]   receive-list position, -1 if unsent */
   EP_T_RECV_SRC_IDX = 11,         /* i32 [sum num_recv_tokens], destination-major     */
   EP_T_RECV_SRC_BASE = 12,        /* i64 [P + 1]  start of each destination's list    */
-  EP_T_DST_ROW = 13,              /* i32 [T, K]   global row (window base + dst_slot) */
+  EP_T_DST_ROW = 13,              /* i32 [T, K]   global row (window base + dst_slot), */
+                                  /*              -1 if unused or dropped (fixed mode) */
   EP_T_COUNT = 14
 };
 ep_status ep_handle_tensor(const ep_handle *h, int32_t which, const void **dev_ptr, int64_t *numel,

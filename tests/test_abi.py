@@ -54,7 +54,8 @@ def _layout_status(L, cfg: _Config, topk_ptr=1):
     return st, h.value
 
 
-GOOD = dict(num_ranks=8, num_tokens=4096, hidden=7168, num_topk=8, num_experts=256, expert_alignment=128, flags=0)
+GOOD = dict(num_ranks=8, num_tokens=4096, hidden=7168, num_topk=8, num_experts=256, expert_alignment=128, flags=0,
+            num_worst_rows=0)
 
 
 @pytest.mark.parametrize("change,status", [
@@ -73,6 +74,9 @@ GOOD = dict(num_ranks=8, num_tokens=4096, hidden=7168, num_topk=8, num_experts=2
     (dict(num_ranks=8, num_tokens=1 << 28), ep.Status.ERR_OVERFLOW),       # T*K >= 2^31
     (dict(num_ranks=1024, num_experts=1024, num_topk=1, num_tokens=1 << 21), ep.Status.ERR_OVERFLOW),  # T*P
     (dict(num_tokens=(1 << 31) // 64 - 100, num_topk=8), ep.Status.ERR_OVERFLOW),
+    (dict(num_worst_rows=-1), ep.Status.ERR_SHAPE),
+    (dict(num_worst_rows=4096, flags=1), ep.Status.ERR_SHAPE),       # fixed windows are not symmetric ones
+    (dict(num_worst_rows=(1 << 31) // 8), ep.Status.ERR_OVERFLOW),    # P * W >= 2^31
 ])
 def test_validation_errors(L, change, status):
     cfg = _Config(**{**GOOD, **change})
@@ -92,7 +96,9 @@ def test_null_arguments(L):
                  lambda: L.ep_dispatch_cached(None, 0, None, None, None, None),
                  lambda: L.ep_combine(None, None, None, None, None),
                  lambda: L.ep_relayout(None, None, None, None),
-                 lambda: L.ep_handle_counts(None, None, None, None)):
+                 lambda: L.ep_handle_counts(None, None, None, None),
+                 lambda: L.ep_handle_status(None, ctypes.byref(ctypes.c_uint32()), None),
+                 lambda: L.ep_handle_status(None, None, None)):
         assert call() == ep.Status.ERR_NULL
     L.ep_handle_free(None)  # no-op
 

@@ -372,3 +372,169 @@ def test_device_e4m3_conversion_matches_oracle():
     say("device e4m3 conversion on", q.size, "values")
     got = ep.debug_e4m3_encode(torch.from_numpy(q).to(DEV)).cpu().numpy()
     np.testing.assert_array_equal(got, oracle.e4m3_encode(q))
+
+
+# --------------------------------------------------------------------------
+# fixed output length (num_worst_rows): no read-back, tail rows, truncation
+# --------------------------------------------------------------------------
+
+def fixed_layout_both(w, topk, W):
+    say("fixed layout", w.name, "W", W)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, np.where(topk >= w.E, -1, np.where(topk < -1, -1, topk)))
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A, num_worst_rows=W), torch.from_numpy(topk).to(DEV))
+    assert h.total_rows == w.P * W  # known without waiting
+    torch.cuda.synchronize()
+    return lay, h
+
+
+def check_fixed_layout(lay, h, W):
+    for name in LAYOUT_TENSORS:
+        if name == "window_row_base":
+            continue
+        got = h.tensor(name).cpu().numpy()
+        exp = getattr(lay, name).reshape(-1)
+        np.testing.assert_array_equal(got, exp.astype(got.dtype), err_msg=name)
+    np.testing.assert_array_equal(h.tensor("window_row_base").cpu().numpy(), np.arange(lay.P + 1) * W)
+    El = lay.E // lay.P
+    rank = np.where(lay.topk_idx >= 0, lay.topk_idx // El, 0)
+    exp_row = np.where((lay.dst_slot >= 0) & (lay.dst_slot < W), rank * W + lay.dst_slot, -1)
+    np.testing.assert_array_equal(h.tensor("dst_row").cpu().numpy(), exp_row.reshape(-1))
+    ne, nr, wb = h.counts()
+    np.testing.assert_array_equal(ne, lay.num_expanded)
+    np.testing.assert_array_equal(nr, lay.num_recv_tokens)
+    np.testing.assert_array_equal(wb, np.arange(lay.P + 1) * W)
+
+
+FIXED_CASES = [SMALL[0], SMALL[1], SMALL[2], SMALL[4], SMALL[6], SMALL[7]]
+
+
+@pytest.mark.parametrize("w", FIXED_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("fit", ["roomy", "tight", "one"])
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_fixed_windows_small(w, fit, fp8):
+    if fp8 and w.H % 128:
+        pytest.skip("fp8 needs H % 128 == 0")
+    topk = routing_with_holes(w, 13)
+    ne = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk).num_expanded
+    W = {"roomy": int(ne.max()) + 37, "tight": max(1, int(np.median(ne))), "one": 1}[fit]
+    x = synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H)
+    x[:3, :128] = 0
+    wt = synth.gen_weights(w)
+    lay, h = fixed_layout_both(w, topk, W)
+    check_fixed_layout(lay, h, W)
+    flags, dropped = h.status()
+    exp_drop = int(np.maximum(lay.num_expanded - W, 0).sum())
+    assert dropped == exp_drop and flags == (ep.STATUS_TRUNCATED if exp_drop else 0)
+    R = w.P * W
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    for zp in (False, True):
+        say("fixed dispatch", w.name, fit, "fp8" if fp8 else "bf16", "zp" if zp else "no zp")
+        rx = torch.full((R, w.H), 0x7F if fp8 else -1, dtype=torch.uint8 if fp8 else torch.int16, device=DEV)
+        if not fp8:
+            rx = rx.view(torch.bfloat16)
+        sc = torch.full((R, w.H // 128), float("nan"), dtype=torch.float32, device=DEV) if fp8 else None
+        rw = torch.full((R,), float("nan"), dtype=torch.float32, device=DEV)
+        rm = torch.full((R, 2), 77, dtype=torch.int32, device=DEV)
+        ep.dispatch(h, xd, wd, fp8=fp8, zero_padding=zp, out=(rx, sc, rw, rm))
+        torch.cuda.synchronize()
+        ox, osc, ow, om, odrop = oracle.dispatch_fixed(lay, w.H, W, x, wt, fp8, zp, fill=0x7F if fp8 else 0xFFFF)
+        assert odrop == dropped
+        np.testing.assert_array_equal(rx.cpu().numpy() if fp8 else host_u16(rx), ox)
+        np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+        np.testing.assert_array_equal(rm.cpu().numpy(), om)
+        tail = np.arange(R) % W >= np.repeat(lay.num_expanded, W)
+        touched = (om[:, 0] >= 0) | zp | tail  # rows whose payload and scales dispatch writes
+        if fp8:
+            gs = sc.cpu().numpy()
+            np.testing.assert_array_equal(gs[touched].view(np.uint32), osc[touched].view(np.uint32))
+            assert np.all(np.isnan(gs[~touched]))
+        say("fixed dispatch_cached", w.name, fit)
+        tmask = torch.from_numpy(touched).to(DEV)
+        cx = rx.clone()
+        cx.view(torch.uint8)[tmask] = 0x55
+        csc = None
+        if fp8:
+            csc = sc.clone()
+            csc[tmask] = 3.0
+        ep.dispatch_cached(h, xd, fp8=fp8, zero_padding=zp, out=(cx, csc))
+        torch.cuda.synchronize()
+        assert torch.equal(cx.view(torch.uint8), rx.view(torch.uint8))
+        if fp8:
+            assert torch.equal(csc.view(torch.int32), sc.view(torch.int32))
+    y = synth.gen_expert_out(w, R)
+    say("fixed combine", w.name, fit)
+    out = ep.combine(h, dev_bf16(y), wd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_u16(out), oracle.combine_fixed(lay, w.H, W, y, wt))
+    # relayout in fixed mode: new routing, same W
+    b = synth.gen_routing(synth.scaled(w, seed=w.seed + 50))
+    ep.relayout(h, torch.from_numpy(b).to(DEV))
+    assert h.total_rows == R
+    check_fixed_layout(oracle.layout(w.P, w.S, w.E, w.K, w.A, b), h, W)
+    h.free()
+
+
+def test_fixed_windows_routing_error_is_a_status():
+    w = D["tiny-p4-s64-e16-k2-h512"]
+    topk = synth.gen_routing(w).copy()
+    topk[5, 0], topk[77, 1] = 16, -7
+    lay, h = fixed_layout_both(w, topk, 200)
+    check_fixed_layout(lay, h, 200)  # the bad slots count as unused
+    flags, dropped = h.status()
+    assert flags & ep.STATUS_ROUTING and dropped == 0
+    h.free()
+
+
+def test_fixed_windows_empty_tokens():
+    w = wl.Workload("empty-fixed", 4, 0, 16, 2, 128, 4, True, "uniform")
+    lay, h = fixed_layout_both(w, np.zeros((0, 2), np.int64), 5)
+    x = torch.zeros((0, 128), dtype=torch.bfloat16, device=DEV)
+    rx, sc, rw, rm = ep.dispatch(h, x, torch.zeros((0, 2), dtype=torch.float32, device=DEV), fp8=True)
+    torch.cuda.synchronize()
+    assert rx.shape == (20, 128) and int(rx.max()) == 0
+    assert float(sc.abs().max()) == 0 and float(rw.abs().max()) == 0 and bool((rm == -1).all())
+    assert h.status() == (0, 0)
+    h.free()
+
+
+@pytest.mark.parametrize("name,fit", [("dsv3-bf16-p8-s4096-e256-k8-h7168", "bucket"),
+                                      ("ep128-zipf-p128-s1024-e256-k6-h7168", "truncate")])
+def test_fixed_windows_full_size(name, fit):
+    """Full-size fixed windows: a safe bucket (no truncation) and, under Zipf skew, a capacity
+    the hot windows overflow.  Metadata against the oracle, every published slot's payload,
+    tails zero, and combine(identity) against the oracle with the dropped slots unused."""
+    w = D[name]
+    topk = synth.gen_routing(w)
+    ne = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk).num_expanded
+    W = int(-(-int(ne.max()) // 1024) * 1024) if fit == "bucket" else 8192
+    lay, h = fixed_layout_both(w, topk, W)
+    check_fixed_layout(lay, h, W)
+    flags, dropped = h.status()
+    exp_drop = int(np.maximum(lay.num_expanded - W, 0).sum())
+    assert dropped == exp_drop and (exp_drop > 0) == (fit == "truncate")
+    x = synth.gen_x(w)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    say("fixed dispatch full", name, "W", W, "dropped", dropped)
+    rx, _, rw, rm = ep.dispatch(h, xd, wd, zero_padding=w.zero_padding)
+    torch.cuda.synchronize()
+    _, _, ow, om, _ = oracle.dispatch_fixed(lay, w.H, W, None, wt, False, w.zero_padding)
+    np.testing.assert_array_equal(rm.cpu().numpy(), om)
+    np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+    tail = np.flatnonzero(np.arange(w.P * W) % W >= np.repeat(lay.num_expanded, W))
+    if len(tail):
+        assert int(gather_rows(rx.view(torch.int16), tail).abs().max()) == 0
+    kept = np.where((lay.dst_slot >= 0) & (lay.dst_slot < W), lay.topk_idx, -1)
+    import dataclasses
+    lay_w = dataclasses.replace(lay, topk_idx=kept, window_row_base=np.arange(w.P + 1, dtype=np.int64) * W)
+    check_payload_rows(rx, xd, lay_w, False)
+    toks = np.arange(0, w.T, 8)
+    say("fixed combine full", name, "tokens", len(toks))
+    out = ep.combine(h, rx, wd)
+    torch.cuda.synchronize()
+    got = host_u16(gather_rows(out, toks))
+    exp = np.concatenate([oracle.combine_identity(w.K, w.H, False, kept, x, wt, u, u + 1) for u in toks])
+    np.testing.assert_array_equal(got, exp)
+    h.free()
+    del rx, rw, rm, out, xd
+    torch.cuda.empty_cache()
