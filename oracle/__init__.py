@@ -60,6 +60,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_combine.restype = i32
         L.oracle_combine_fixed.argtypes = [i32] * 5 + [P_] * 2 + [i64] + [P_] * 2 + [i64, i64, P_]
         L.oracle_combine_fixed.restype = i32
+        L.oracle_dispatch_general.argtypes = [i32] * 9 + [i64] + [P_] * 9 + [i64, i64] + [P_] * 5
+        L.oracle_dispatch_general.restype = i32
+        L.oracle_combine_general.argtypes = [i32] * 5 + [i64] + [P_] * 6 + [i64, i64, P_]
+        L.oracle_combine_general.restype = i32
+        L.oracle_combine_identity_bias.argtypes = [i32] * 3 + [P_] * 4 + [i64, i64, P_]
+        L.oracle_combine_identity_bias.restype = i32
         L.oracle_combine_identity.argtypes = [i32] * 3 + [P_] * 3 + [i64, i64, P_]
         L.oracle_combine_identity.restype = i32
         L.oracle_quantize_row.argtypes = [P_, i32, P_, P_]
@@ -209,6 +215,59 @@ def dispatch_fixed(lay: Layout, H: int, capacity: int, x: np.ndarray | None,
     return recv_x, recv_scales, recv_w, recv_meta, int(dropped[0])
 
 
+def dispatch_general(lay: Layout, H: int, *, fp8: bool, zero_padding: bool, topk_weights=None,
+                     x: np.ndarray | None = None, x_codes: np.ndarray | None = None,
+                     x_scales: np.ndarray | None = None, capacity: int = 0, scales_col_major: bool = False,
+                     row_begin: int = 0, row_end: int | None = None, with_meta: bool = True, fill: int = 0):
+    """``oracle_dispatch_general``: exact (capacity 0) or fixed windows, row- or column-major
+    scales, fused quantisation of x or pre-quantised (x_codes, x_scales).
+    -> (recv_x, recv_scales, recv_weights, recv_src_meta, dropped_rows); recv_scales is
+    [n, H/128], or [H/128, n] when scales_col_major."""
+    total = lay.P * capacity if capacity > 0 else lay.total_rows
+    if row_end is None:
+        row_end = total
+    n = row_end - row_begin
+    payload = x is not None or x_codes is not None
+    x = np.zeros((0,), np.uint16) if x is None else np.ascontiguousarray(x, dtype=np.uint16).reshape(lay.T, H)
+    xc = None if x_codes is None else np.ascontiguousarray(x_codes, dtype=np.uint8).reshape(lay.T, H)
+    xs = None if x_scales is None else np.ascontiguousarray(x_scales, dtype=np.float32).reshape(lay.T, H // 128)
+    recv_x = np.full((n, H), fill, np.uint8 if fp8 else np.uint16) if payload else None
+    recv_scales = None
+    if fp8 and payload:
+        recv_scales = np.zeros((H // 128, n) if scales_col_major else (n, H // 128), np.float32)
+    recv_w = np.zeros(n, np.float32) if with_meta else None
+    recv_meta = np.zeros((n, 2), np.int32) if with_meta else None
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    assert w is not None or not with_meta, "row metadata needs topk_weights"
+    dropped = np.zeros(1, np.int64)
+    st = lib().oracle_dispatch_general(
+        lay.P, lay.S, lay.E, lay.K, H, lay.A, int(fp8), int(zero_padding), int(scales_col_major), capacity,
+        _p(lay.topk_idx), _p(lay.dst_slot), _p(lay.num_tokens_per_expert_total), _p(lay.expert_offset),
+        _p(lay.window_row_base), _p(x), _p(xc), _p(xs), _p(w), row_begin, row_end, _p(recv_x),
+        _p(recv_scales), _p(recv_w), _p(recv_meta), _p(dropped))
+    if st != OK:
+        raise OracleError(st)
+    return recv_x, recv_scales, recv_w, recv_meta, int(dropped[0])
+
+
+def combine_general(lay: Layout, H: int, y: np.ndarray, topk_weights: np.ndarray | None,
+                    bias: np.ndarray | None = None, capacity: int = 0, tok_begin: int = 0,
+                    tok_end: int | None = None) -> np.ndarray:
+    """``oracle_combine_general``: exact or fixed windows, optional bf16 bias [T, H]."""
+    if tok_end is None:
+        tok_end = lay.T
+    y = np.ascontiguousarray(y, dtype=np.uint16)
+    out = np.zeros((tok_end - tok_begin, H), np.uint16)
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16).reshape(lay.T, H)
+    st = lib().oracle_combine_general(lay.P, lay.S, lay.E, lay.K, H, capacity, _p(lay.topk_idx),
+                                      _p(lay.dst_slot), _p(lay.window_row_base), _p(y), _p(w), _p(b),
+                                      tok_begin, tok_end, _p(out))
+    if st != OK:
+        raise OracleError(st)
+    return out
+
+
 def combine_fixed(lay: Layout, H: int, capacity: int, y: np.ndarray, topk_weights: np.ndarray | None,
                   tok_begin: int = 0, tok_end: int | None = None) -> np.ndarray:
     """Combine over fixed-length windows (``oracle_combine_fixed``): y is [P * capacity, H]."""
@@ -241,13 +300,19 @@ def combine(lay: Layout, H: int, y: np.ndarray, topk_weights: np.ndarray | None,
 
 
 def combine_identity(K: int, H: int, fp8: bool, topk_idx: np.ndarray, x: np.ndarray,
-                     topk_weights: np.ndarray | None, tok_begin: int, tok_end: int) -> np.ndarray:
+                     topk_weights: np.ndarray | None, tok_begin: int, tok_end: int,
+                     bias: np.ndarray | None = None) -> np.ndarray:
     topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
     x = np.ascontiguousarray(x, dtype=np.uint16)
     out = np.zeros((tok_end - tok_begin, H), np.uint16)
     w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
-    st = lib().oracle_combine_identity(K, H, int(fp8), _p(topk_idx), _p(x), _p(w), tok_begin, tok_end,
-                                       _p(out))
+    if bias is None:
+        st = lib().oracle_combine_identity(K, H, int(fp8), _p(topk_idx), _p(x), _p(w), tok_begin, tok_end,
+                                           _p(out))
+    else:
+        b = np.ascontiguousarray(bias, dtype=np.uint16)
+        st = lib().oracle_combine_identity_bias(K, H, int(fp8), _p(topk_idx), _p(x), _p(w), _p(b), tok_begin,
+                                                tok_end, _p(out))
     if st != OK:
         raise OracleError(st)
     return out

@@ -293,26 +293,50 @@ void oracle_quantize_row(const uint16_t *x, int H, uint8_t *codes, float *scales
  * do_zero_padding).  Without zero_padding their payload is left untouched.
  * Rows not covered (symmetric-window tails) are left untouched.
  *
- * capacity > 0 is the fixed output length of every window (see
- * oracle_dispatch_fixed): window d starts at d * capacity, window-local rows
- * >= capacity are not written, and the rows [num_expanded[d], capacity) of a
- * window are its tail.
+ * Options (oracle_dispatch_general):
+ *  capacity > 0      the fixed output length of every window (see
+ *                    oracle_dispatch_fixed): window d starts at d * capacity,
+ *                    window-local rows >= capacity are not written, and the rows
+ *                    [num_expanded[d], capacity) of a window are its tail.
+ *  scales_col_major  recv_scales is laid out [H/128][n] (n = row_end - row_begin:
+ *                    one scale position contiguous across rows) instead of
+ *                    [n][H/128] ([TUT] 3.6 (3): the column-major scale layout is
+ *                    the transpose of the row-major one, with no padding of the
+ *                    row dimension).
+ *  x_codes, x_scales pre-quantised input ([TUT] 3.6 (2): x may be the pair of
+ *                    E4M3 data [T][H] and one fp32 scale per 128 channels
+ *                    [T][H/128]); rows then carry these bytes and scales as
+ *                    they are, and x is not read.  fp8 only.
  *
  * Output arrays hold only rows [row_begin, row_end): element (r, h) is at
  * (r - row_begin) * H + h.  recv_weights / recv_src_meta may be NULL (cached
  * dispatch moves payload only); recv_x may be NULL (metadata only).
  * recv_scales is used only when fp8. */
+static void put_scales(float *recv_scales, int col_major, int64_t n, int64_t rr, int nb,
+                       const float *src) {
+  for (int b = 0; b < nb; b++) {
+    float v = src ? src[b] : 0.0f;
+    if (col_major)
+      recv_scales[(int64_t)b * n + rr] = v;
+    else
+      recv_scales[rr * nb + b] = v;
+  }
+}
+
 static int dispatch_rows(int P, int S, int E, int K, int H, int A, int fp8, int zero_padding,
-                         const int64_t *topk_idx, const int32_t *dst_slot,
+                         int scales_col_major, const int64_t *topk_idx, const int32_t *dst_slot,
                          const int32_t *num_tokens_per_expert_total, const int64_t *expert_offset,
                          const int64_t *window_row_base, int64_t capacity, const uint16_t *x,
+                         const uint8_t *x_codes, const float *x_scales,
                          const float *topk_weights, int64_t row_begin, int64_t row_end,
                          void *recv_x, float *recv_scales, float *recv_weights,
                          int32_t *recv_src_meta) {
   if (P < 1 || E % P != 0 || H < 1 || (fp8 && H % 128 != 0)) return ORACLE_ERR_SHAPE;
+  if (x_codes && !fp8) return ORACLE_ERR_SHAPE;
   const int64_t T = (int64_t)P * S;
   const int El = E / P;
   const int nb = H / 128;
+  const int64_t n_out = row_end - row_begin;
   uint8_t *codes = NULL;
   float *scales = NULL;
   if (fp8) {
@@ -332,9 +356,14 @@ static int dispatch_rows(int P, int S, int E, int K, int H, int A, int fp8, int 
       if (!recv_x) {
         /* metadata only */
       } else if (fp8) {
-        oracle_quantize_row(x + u * H, H, codes, scales);
+        if (x_codes) {
+          memcpy(codes, x_codes + u * H, (size_t)H);
+          memcpy(scales, x_scales + u * nb, sizeof(float) * (size_t)nb);
+        } else {
+          oracle_quantize_row(x + u * H, H, codes, scales);
+        }
         memcpy((uint8_t *)recv_x + rr * H, codes, (size_t)H);
-        memcpy(recv_scales + rr * nb, scales, sizeof(float) * (size_t)nb);
+        put_scales(recv_scales, scales_col_major, n_out, rr, nb, scales);
       } else {
         memcpy((uint16_t *)recv_x + rr * H, x + u * H, sizeof(uint16_t) * (size_t)H);
       }
@@ -364,7 +393,7 @@ static int dispatch_rows(int P, int S, int E, int K, int H, int A, int fp8, int 
       if (zero_padding && recv_x) {
         if (fp8) {
           memset((uint8_t *)recv_x + rr * H, 0, (size_t)H);
-          for (int b = 0; b < nb; b++) recv_scales[rr * nb + b] = 0.0f;
+          put_scales(recv_scales, scales_col_major, n_out, rr, nb, NULL);
         } else {
           for (int h = 0; h < H; h++) ((uint16_t *)recv_x)[rr * H + h] = 0;
         }
@@ -388,7 +417,7 @@ static int dispatch_rows(int P, int S, int E, int K, int H, int A, int fp8, int 
         if (recv_x) {
           if (fp8) {
             memset((uint8_t *)recv_x + rr * H, 0, (size_t)H);
-            for (int b = 0; b < nb; b++) recv_scales[rr * nb + b] = 0.0f;
+            put_scales(recv_scales, scales_col_major, n_out, rr, nb, NULL);
           } else {
             for (int h = 0; h < H; h++) ((uint16_t *)recv_x)[rr * H + h] = 0;
           }
@@ -407,10 +436,20 @@ int oracle_dispatch(int P, int S, int E, int K, int H, int A, int fp8, int zero_
                     const int64_t *window_row_base, const uint16_t *x, const float *topk_weights,
                     int64_t row_begin, int64_t row_end, void *recv_x, float *recv_scales,
                     float *recv_weights, int32_t *recv_src_meta) {
-  return dispatch_rows(P, S, E, K, H, A, fp8, zero_padding, topk_idx, dst_slot,
-                       num_tokens_per_expert_total, expert_offset, window_row_base, 0, x,
-                       topk_weights, row_begin, row_end, recv_x, recv_scales, recv_weights,
+  return dispatch_rows(P, S, E, K, H, A, fp8, zero_padding, 0, topk_idx, dst_slot,
+                       num_tokens_per_expert_total, expert_offset, window_row_base, 0, x, NULL,
+                       NULL, topk_weights, row_begin, row_end, recv_x, recv_scales, recv_weights,
                        recv_src_meta);
+}
+
+/* Rows past the fixed length of each window, sum_d max(0, num_expanded[d] - capacity). */
+static int64_t dropped_rows(int P, int El, const int64_t *expert_offset, int64_t capacity) {
+  int64_t drop = 0;
+  for (int d = 0; d < P; d++) {
+    int64_t used = expert_offset[(int64_t)d * (El + 1) + El];
+    if (used > capacity) drop += used - capacity;
+  }
+  return drop;
 }
 
 /* Fixed output length ([BLOG] "the output length has a dynamic and a fixed
@@ -433,17 +472,30 @@ int oracle_dispatch_fixed(int P, int S, int E, int K, int H, int A, int fp8, int
                           void *recv_x, float *recv_scales, float *recv_weights,
                           int32_t *recv_src_meta, int64_t *dropped) {
   if (capacity < 1 || P < 1 || E % P != 0) return ORACLE_ERR_SHAPE;
-  const int El = E / P;
-  int64_t drop = 0;
-  for (int d = 0; d < P; d++) {
-    int64_t used = expert_offset[(int64_t)d * (El + 1) + El];
-    if (used > capacity) drop += used - capacity;
-  }
-  if (dropped) *dropped = drop;
-  return dispatch_rows(P, S, E, K, H, A, fp8, zero_padding, topk_idx, dst_slot,
-                       num_tokens_per_expert_total, expert_offset, NULL, capacity, x,
+  if (dropped) *dropped = dropped_rows(P, E / P, expert_offset, capacity);
+  return dispatch_rows(P, S, E, K, H, A, fp8, zero_padding, 0, topk_idx, dst_slot,
+                       num_tokens_per_expert_total, expert_offset, NULL, capacity, x, NULL, NULL,
                        topk_weights, row_begin, row_end, recv_x, recv_scales, recv_weights,
                        recv_src_meta);
+}
+
+/* Every option at once (see dispatch_rows): exact (capacity 0) or fixed
+ * windows, row- or column-major scales, quantised here or pre-quantised
+ * input.  *dropped (may be NULL) as in oracle_dispatch_fixed. */
+int oracle_dispatch_general(int P, int S, int E, int K, int H, int A, int fp8, int zero_padding,
+                            int scales_col_major, int64_t capacity, const int64_t *topk_idx,
+                            const int32_t *dst_slot, const int32_t *num_tokens_per_expert_total,
+                            const int64_t *expert_offset, const int64_t *window_row_base,
+                            const uint16_t *x, const uint8_t *x_codes, const float *x_scales,
+                            const float *topk_weights, int64_t row_begin, int64_t row_end,
+                            void *recv_x, float *recv_scales, float *recv_weights,
+                            int32_t *recv_src_meta, int64_t *dropped) {
+  if (capacity < 0 || P < 1 || E % P != 0) return ORACLE_ERR_SHAPE;
+  if (dropped) *dropped = capacity > 0 ? dropped_rows(P, E / P, expert_offset, capacity) : 0;
+  return dispatch_rows(P, S, E, K, H, A, fp8, zero_padding, scales_col_major, topk_idx,
+                       dst_slot, num_tokens_per_expert_total, expert_offset, window_row_base,
+                       capacity, x, x_codes, x_scales, topk_weights, row_begin, row_end, recv_x,
+                       recv_scales, recv_weights, recv_src_meta);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -456,8 +508,10 @@ int oracle_dispatch_fixed(int P, int S, int E, int K, int H, int A, int fp8, int
  *   acc = +0
  *   for j = 0..K-1 with a valid slot:
  *     acc = fl(acc + fl(w[u][j] * float(y[window_row_base[rank(e)] + dst_slot[u][j]][h])))
+ *   with a bias ([TUT] 3.3: combine's optional bias, the fused residual or
+ *   shared-expert output, bf16 [T][H]):  acc = fl(acc + float(bias[u][h]))
  *   out[u][h] = bf16(acc)
- * topk_weights == NULL means every weight is 1.
+ * topk_weights == NULL means every weight is 1; bias == NULL means none.
  * capacity > 0: fixed-length windows (oracle_dispatch_fixed): row
  * rank(e) * capacity + dst_slot, and a slot whose row was not published
  * (dst_slot >= capacity) is skipped like an unused one.
@@ -465,7 +519,7 @@ int oracle_dispatch_fixed(int P, int S, int E, int K, int H, int A, int fp8, int
 static int combine_rows(int P, int E, int K, int H, const int64_t *topk_idx,
                         const int32_t *dst_slot, const int64_t *window_row_base,
                         int64_t capacity, const uint16_t *y, const float *topk_weights,
-                        int64_t tok_begin, int64_t tok_end, uint16_t *out) {
+                        const uint16_t *bias, int64_t tok_begin, int64_t tok_end, uint16_t *out) {
   if (P < 1 || E % P != 0) return ORACLE_ERR_SHAPE;
   const int El = E / P;
   for (int64_t u = tok_begin; u < tok_end; u++) {
@@ -481,6 +535,7 @@ static int combine_rows(int P, int E, int K, int H, const int64_t *topk_idx,
         float prod = w * oracle_bf16_to_float(y[r * H + h]);
         acc = acc + prod;
       }
+      if (bias) acc = acc + oracle_bf16_to_float(bias[u * H + h]);
       out[(u - tok_begin) * H + h] = oracle_bf16_round(acc);
     }
   }
@@ -492,7 +547,7 @@ int oracle_combine(int P, int S, int E, int K, int H, const int64_t *topk_idx,
                    const float *topk_weights, int64_t tok_begin, int64_t tok_end,
                    uint16_t *out) {
   (void)S;
-  return combine_rows(P, E, K, H, topk_idx, dst_slot, window_row_base, 0, y, topk_weights,
+  return combine_rows(P, E, K, H, topk_idx, dst_slot, window_row_base, 0, y, topk_weights, NULL,
                       tok_begin, tok_end, out);
 }
 
@@ -502,8 +557,21 @@ int oracle_combine_fixed(int P, int S, int E, int K, int H, const int64_t *topk_
                          uint16_t *out) {
   (void)S;
   if (capacity < 1) return ORACLE_ERR_SHAPE;
-  return combine_rows(P, E, K, H, topk_idx, dst_slot, NULL, capacity, y, topk_weights,
+  return combine_rows(P, E, K, H, topk_idx, dst_slot, NULL, capacity, y, topk_weights, NULL,
                       tok_begin, tok_end, out);
+}
+
+/* Every option at once: exact (capacity 0, rows at window_row_base) or fixed
+ * windows, with or without a bias. */
+int oracle_combine_general(int P, int S, int E, int K, int H, int64_t capacity,
+                           const int64_t *topk_idx, const int32_t *dst_slot,
+                           const int64_t *window_row_base, const uint16_t *y,
+                           const float *topk_weights, const uint16_t *bias, int64_t tok_begin,
+                           int64_t tok_end, uint16_t *out) {
+  (void)S;
+  if (capacity < 0) return ORACLE_ERR_SHAPE;
+  return combine_rows(P, E, K, H, topk_idx, dst_slot, window_row_base, capacity, y, topk_weights,
+                      bias, tok_begin, tok_end, out);
 }
 
 /* combine(identity_expert(dispatch(x))) for tokens [tok_begin, tok_end),
@@ -513,9 +581,10 @@ int oracle_combine_fixed(int P, int S, int E, int K, int H, const int64_t *topk_
  *   fp8:   bf16(fl(decode(code) * scale))  (the identity expert dequantises)
  * and the combine of those rows follows oracle_combine's order.  [TUT] 2.3
  * (combine is the inverse of dispatch). */
-int oracle_combine_identity(int K, int H, int fp8, const int64_t *topk_idx, const uint16_t *x,
-                            const float *topk_weights, int64_t tok_begin, int64_t tok_end,
-                            uint16_t *out) {
+static int combine_identity_rows(int K, int H, int fp8, const int64_t *topk_idx,
+                                 const uint16_t *x, const float *topk_weights,
+                                 const uint16_t *bias, int64_t tok_begin, int64_t tok_end,
+                                 uint16_t *out) {
   if (fp8 && H % 128 != 0) return ORACLE_ERR_SHAPE;
   uint16_t *row = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)H);
   uint8_t *codes = (uint8_t *)malloc((size_t)H);
@@ -537,6 +606,7 @@ int oracle_combine_identity(int K, int H, int fp8, const int64_t *topk_idx, cons
         float prod = w * oracle_bf16_to_float(row[h]);
         acc = acc + prod;
       }
+      if (bias) acc = acc + oracle_bf16_to_float(bias[u * H + h]);
       out[(u - tok_begin) * H + h] = oracle_bf16_round(acc);
     }
   }
@@ -544,6 +614,21 @@ int oracle_combine_identity(int K, int H, int fp8, const int64_t *topk_idx, cons
   free(codes);
   free(scales);
   return ORACLE_OK;
+}
+
+int oracle_combine_identity(int K, int H, int fp8, const int64_t *topk_idx, const uint16_t *x,
+                            const float *topk_weights, int64_t tok_begin, int64_t tok_end,
+                            uint16_t *out) {
+  return combine_identity_rows(K, H, fp8, topk_idx, x, topk_weights, NULL, tok_begin, tok_end, out);
+}
+
+/* As oracle_combine_identity, plus combine's optional bias (oracle_combine_general). */
+int oracle_combine_identity_bias(int K, int H, int fp8, const int64_t *topk_idx,
+                                 const uint16_t *x, const float *topk_weights,
+                                 const uint16_t *bias, int64_t tok_begin, int64_t tok_end,
+                                 uint16_t *out) {
+  return combine_identity_rows(K, H, fp8, topk_idx, x, topk_weights, bias, tok_begin, tok_end,
+                               out);
 }
 
 /* Array forms of the scalar encoders, for the self-tests. */

@@ -581,3 +581,107 @@ def test_fixed_length_truncation_drops_tail_rows_and_their_slots(A):
     wt0[trunc] = 0.0
     np.testing.assert_array_equal(oracle.combine_fixed(lay, w.H, W, frx, wt),
                                   oracle.combine(lay, w.H, erx, wt0))
+
+
+# ---------------------------------------------------------------------------
+# API variants: column-major scales, pre-quantised input, combine bias
+# (TileLang tutorial ch. 38, sections 3.3 and 3.6)
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("capacity", [0, 150])
+def test_scales_col_major_is_the_transpose_of_row_major(capacity):
+    """The column-major scale layout holds scale b of row r at b * rows + r: the transpose of
+    the row-major [rows, H/128] layout, with no padding of the row dimension.  Six blocks
+    per row, so that a swapped index cannot hide behind a square or a short block count."""
+    w = small_workload(P=4, S=40, E=16, K=3, H=768, A=8, seed=41)
+    topk = synth.gen_routing(w)
+    x = synth.gen_bf16_rows(42, 1, w.T, w.H)
+    wt = synth.gen_weights(w)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    rm = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=True, topk_weights=wt, x=x, capacity=capacity)
+    cm = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=True, topk_weights=wt, x=x, capacity=capacity,
+                                 scales_col_major=True)
+    n = rm[0].shape[0]
+    assert rm[1].shape == (n, 6) and cm[1].shape == (6, n)
+    np.testing.assert_array_equal(cm[1], rm[1].T)
+    np.testing.assert_array_equal(cm[0], rm[0])
+    flat = cm[1].ravel()
+    meta = rm[3]
+    for r in np.flatnonzero(meta[:, 0] >= 0)[::17]:
+        u = meta[r, 0]
+        xf = bf16_bits_to_f64(x[u]).astype(np.float32).reshape(6, 128)
+        amax = np.abs(xf).max(axis=1)
+        for b in range(6):
+            assert flat[b * n + r] == np.float32(amax[b]) / np.float32(448.0)
+
+
+def test_prequantised_input_is_copied_and_matches_fused_quantisation():
+    """Dispatching (E4M3 data, fp32 scales) moves those bytes unchanged to every row of the
+    token; fed with the per-token quantisation of x it equals the fused fp8 dispatch."""
+    w = small_workload(P=4, S=48, E=16, K=3, H=512, A=4, seed=43)
+    topk = synth.gen_routing(w).copy()
+    topk[::9, 2] = -1
+    x = synth.gen_bf16_rows(44, 1, w.T, w.H)
+    wt = synth.gen_weights(w)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    codes = np.empty((w.T, w.H), np.uint8)
+    scales = np.empty((w.T, w.H // 128), np.float32)
+    for u in range(w.T):
+        codes[u], scales[u] = oracle.quantize_row(x[u])
+    fused = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=True, topk_weights=wt, x=x)
+    pre = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=True, topk_weights=wt, x_codes=codes,
+                                  x_scales=scales)
+    for a, b in zip(fused[:4], pre[:4]):
+        np.testing.assert_array_equal(a, b)
+    # arbitrary bytes (NaN codes included) and scales travel bit for bit
+    rng = np.random.default_rng(45)
+    rc = rng.integers(0, 256, (w.T, w.H), dtype=np.uint8)
+    rs = rng.standard_normal((w.T, w.H // 128)).astype(np.float32)
+    got = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=False, topk_weights=wt, x_codes=rc,
+                                  x_scales=rs, fill=0xEE)
+    meta = got[3]
+    valid = meta[:, 0] >= 0
+    np.testing.assert_array_equal(got[0][valid], rc[meta[valid, 0]])
+    np.testing.assert_array_equal(got[1][valid].view(np.uint32), rs[meta[valid, 0]].view(np.uint32))
+    assert np.all(got[0][~valid] == 0xEE)  # padding untouched without zero padding
+
+
+def test_combine_bias_closed_forms():
+    """Bias is added after the K slots, before the single rounding.  With y rows = x and unit
+    weights the result is exactly bf16((k + 1) x) for a bias equal to x (k valid slots), and
+    +0 for a bias equal to -x when a token has one valid slot."""
+    w = small_workload(P=4, S=64, E=16, K=4, H=256, A=4, seed=46)
+    topk = synth.gen_routing(w).copy()
+    topk[::5, 1:] = -1  # tokens with a single valid slot
+    x = synth.gen_bf16_rows(47, 1, w.T, w.H)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    y, _, _, _ = oracle.dispatch(lay, w.H, x, np.ones((w.T, w.K), np.float32), False, True)
+    kv = (topk >= 0).sum(1).astype(np.float64)
+    out = oracle.combine_general(lay, w.H, y, None, bias=x)
+    expect = torch_bf16_bits((bf16_bits_to_f64(x) * (kv + 1)[:, None]).astype(np.float32))
+    np.testing.assert_array_equal(out, expect)
+    neg = x ^ np.uint16(0x8000)
+    out = oracle.combine_general(lay, w.H, y, None, bias=neg)
+    one = kv == 1
+    assert np.all(out[one] == 0)  # x + (-x) = +0 in round-to-nearest
+    np.testing.assert_array_equal(oracle.combine_identity(w.K, w.H, False, topk, x, None, 0, w.T, bias=x),
+                                  oracle.combine_general(lay, w.H, y, None, bias=x))
+
+
+def test_combine_bias_general_within_one_ulp():
+    w = small_workload(P=4, S=64, E=32, K=8, H=256, A=8, seed=48)
+    topk = synth.gen_routing(w)
+    wt = synth.gen_weights(w)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    y = synth.gen_bf16_rows(49, 1, lay.total_rows, w.H)
+    bias = synth.gen_bf16_rows(50, 1, w.T, w.H)
+    out = oracle.combine_general(lay, w.H, y, wt, bias=bias)
+    El = w.E // w.P
+    rows = lay.window_row_base[topk // El] + lay.dst_slot
+    exact = (bf16_bits_to_f64(y)[rows] * wt[:, :, None].astype(np.float64)).sum(1) + bf16_bits_to_f64(bias)
+    ref = torch_bf16_bits(exact.astype(np.float32))
+    d = bf16_ulp_diff(out, ref)
+    assert d.max() <= 1 and (d == 0).mean() > 0.99
+    # a dropped bias term is caught
+    assert (bf16_ulp_diff(out, oracle.combine_general(lay, w.H, y, wt)) > 1).mean() > 0.5
