@@ -9,11 +9,12 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libep_mi355x.so"
-EP_ABI_VERSION = 2
+EP_ABI_VERSION = 3
 
 # dispatch flags
 _FP8 = 1
 _ZERO_PADDING = 2
+_SCALES_COL_MAJOR = 4
 _SYMMETRIC_WINDOWS = 1
 # ep_handle_status bits
 STATUS_ROUTING = 1
@@ -122,7 +123,9 @@ def lib() -> ctypes.CDLL:
         L.ep_relayout.argtypes = [vp, vp, vp, ctypes.POINTER(i64)]
         L.ep_dispatch.argtypes = [vp, u32, vp, vp, vp, vp, vp, vp, vp]
         L.ep_dispatch_cached.argtypes = [vp, u32, vp, vp, vp, vp]
-        L.ep_combine.argtypes = [vp, vp, vp, vp, vp]
+        L.ep_dispatch_prequant.argtypes = [vp, u32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.ep_dispatch_prequant_cached.argtypes = [vp, u32, vp, vp, vp, vp, vp]
+        L.ep_combine.argtypes = [vp, vp, vp, vp, vp, vp]
         L.ep_handle_free.argtypes = [vp]
         L.ep_handle_free.restype = None
         L.ep_handle_config.argtypes = [vp, ctypes.POINTER(_Config)]
@@ -130,7 +133,8 @@ def lib() -> ctypes.CDLL:
         L.ep_handle_counts.argtypes = [vp, vp, vp, vp]
         L.ep_handle_status.argtypes = [vp, ctypes.POINTER(u32), ctypes.POINTER(i64)]
         L.ep_handle_tensor.argtypes = [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(i32)]
-        for fn in ("ep_get_layout", "ep_relayout", "ep_dispatch", "ep_dispatch_cached", "ep_combine",
+        for fn in ("ep_get_layout", "ep_relayout", "ep_dispatch", "ep_dispatch_cached", "ep_dispatch_prequant",
+                   "ep_dispatch_prequant_cached", "ep_combine",
                    "ep_handle_config", "ep_handle_check", "ep_handle_counts", "ep_handle_status",
                    "ep_handle_tensor"):
             getattr(L, fn).restype = i32
@@ -277,62 +281,93 @@ def relayout(h: Handle, topk_idx) -> Handle:
     return h
 
 
-def _flags(fp8: bool, zero_padding: bool) -> int:
-    return (_FP8 if fp8 else 0) | (_ZERO_PADDING if zero_padding else 0)
+def _flags(fp8: bool, zero_padding: bool, scales_col_major: bool = False) -> int:
+    return (_FP8 if fp8 else 0) | (_ZERO_PADDING if zero_padding else 0) | (_SCALES_COL_MAJOR if scales_col_major else 0)
 
 
-def _alloc_recv(h: Handle, fp8: bool, device):
+def _alloc_recv(h: Handle, fp8: bool, device, scales_col_major: bool = False):
     import torch
 
     H, R = h.cfg.H, h.total_rows
     recv_x = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=device)
-    recv_scales = torch.empty((R, H // 128), dtype=torch.float32, device=device) if fp8 else None
+    recv_scales = None
+    if fp8:
+        shape = (H // 128, R) if scales_col_major else (R, H // 128)
+        recv_scales = torch.empty(shape, dtype=torch.float32, device=device)
     return recv_x, recv_scales
 
 
-def dispatch(h: Handle, x, topk_weights, fp8: bool = False, zero_padding: bool = False, out=None):
-    """ep_dispatch -> (recv_x, recv_scales | None, recv_weights, recv_src_meta).
+def _input(h: Handle, x):
+    """x: bf16 [T, H], or the pre-quantised pair (E4M3 bytes uint8 [T, H], fp32 scales [T, H/128])."""
+    import torch
+
+    cfg = h.cfg
+    if isinstance(x, tuple):
+        codes, scales = x
+        _require(codes, torch.uint8, (cfg.T, cfg.H), "x codes")
+        _require(scales, torch.float32, (cfg.T, cfg.H // 128), "x scales")
+        return codes, scales, codes.device
+    _require(x, torch.bfloat16, (cfg.T, cfg.H), "x")
+    return x, None, x.device
+
+
+def dispatch(h: Handle, x, topk_weights, fp8: bool = False, zero_padding: bool = False,
+             scales_col_major: bool = False, out=None):
+    """ep_dispatch (x bf16) or ep_dispatch_prequant (x = (codes, scales), output fp8)
+    -> (recv_x, recv_scales | None, recv_weights, recv_src_meta).
 
     out: optional preallocated (recv_x, recv_scales, recv_weights, recv_src_meta)."""
     import torch
 
     cfg = h.cfg
-    _require(x, torch.bfloat16, (cfg.T, cfg.H), "x")
+    xin, xs, device = _input(h, x)
+    fp8 = fp8 or xs is not None
     _require(topk_weights, torch.float32, (cfg.T, cfg.K), "topk_weights")
     if out is None:
-        recv_x, recv_scales = _alloc_recv(h, fp8, x.device)
-        recv_w = torch.empty(h.total_rows, dtype=torch.float32, device=x.device)
-        recv_meta = torch.empty((h.total_rows, 2), dtype=torch.int32, device=x.device)
+        recv_x, recv_scales = _alloc_recv(h, fp8, device, scales_col_major)
+        recv_w = torch.empty(h.total_rows, dtype=torch.float32, device=device)
+        recv_meta = torch.empty((h.total_rows, 2), dtype=torch.int32, device=device)
     else:
         recv_x, recv_scales, recv_w, recv_meta = out
-    _check(lib().ep_dispatch(h.ptr, _flags(fp8, zero_padding), _ptr(x), _ptr(topk_weights), _ptr(recv_x),
-                             _ptr(recv_scales), _ptr(recv_w), _ptr(recv_meta), _stream(x.device)))
+    flags = _flags(fp8, zero_padding, scales_col_major)
+    if xs is None:
+        _check(lib().ep_dispatch(h.ptr, flags, _ptr(xin), _ptr(topk_weights), _ptr(recv_x), _ptr(recv_scales),
+                                 _ptr(recv_w), _ptr(recv_meta), _stream(device)))
+    else:
+        _check(lib().ep_dispatch_prequant(h.ptr, flags, _ptr(xin), _ptr(xs), _ptr(topk_weights), _ptr(recv_x),
+                                          _ptr(recv_scales), _ptr(recv_w), _ptr(recv_meta), _stream(device)))
     return recv_x, recv_scales, recv_w, recv_meta
 
 
-def dispatch_cached(h: Handle, x, fp8: bool = False, zero_padding: bool = False, out=None):
-    """ep_dispatch_cached -> (recv_x, recv_scales | None); out: optional (recv_x, recv_scales)."""
-    import torch
-
-    cfg = h.cfg
-    _require(x, torch.bfloat16, (cfg.T, cfg.H), "x")
-    recv_x, recv_scales = _alloc_recv(h, fp8, x.device) if out is None else out
-    _check(lib().ep_dispatch_cached(h.ptr, _flags(fp8, zero_padding), _ptr(x), _ptr(recv_x), _ptr(recv_scales),
-                                    _stream(x.device)))
+def dispatch_cached(h: Handle, x, fp8: bool = False, zero_padding: bool = False, scales_col_major: bool = False,
+                    out=None):
+    """ep_dispatch_cached / ep_dispatch_prequant_cached -> (recv_x, recv_scales | None);
+    out: optional (recv_x, recv_scales)."""
+    xin, xs, device = _input(h, x)
+    fp8 = fp8 or xs is not None
+    recv_x, recv_scales = _alloc_recv(h, fp8, device, scales_col_major) if out is None else out
+    flags = _flags(fp8, zero_padding, scales_col_major)
+    if xs is None:
+        _check(lib().ep_dispatch_cached(h.ptr, flags, _ptr(xin), _ptr(recv_x), _ptr(recv_scales), _stream(device)))
+    else:
+        _check(lib().ep_dispatch_prequant_cached(h.ptr, flags, _ptr(xin), _ptr(xs), _ptr(recv_x),
+                                                 _ptr(recv_scales), _stream(device)))
     return recv_x, recv_scales
 
 
-def combine(h: Handle, y, topk_weights=None, out=None):
-    """ep_combine: y bf16 [total_rows, H] -> out bf16 [T, H]."""
+def combine(h: Handle, y, topk_weights=None, bias=None, out=None):
+    """ep_combine: y bf16 [total_rows, H] (+ optional bias bf16 [T, H]) -> out bf16 [T, H]."""
     import torch
 
     cfg = h.cfg
     _require(y, torch.bfloat16, (h.total_rows, cfg.H), "y")
     if topk_weights is not None:
         _require(topk_weights, torch.float32, (cfg.T, cfg.K), "topk_weights")
+    if bias is not None:
+        _require(bias, torch.bfloat16, (cfg.T, cfg.H), "bias")
     if out is None:
         out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=y.device)
-    _check(lib().ep_combine(h.ptr, _ptr(y), _ptr(topk_weights), _ptr(out), _stream(y.device)))
+    _check(lib().ep_combine(h.ptr, _ptr(y), _ptr(topk_weights), _ptr(bias), _ptr(out), _stream(y.device)))
     return out
 
 

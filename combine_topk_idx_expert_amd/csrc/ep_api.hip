@@ -312,7 +312,7 @@ int parts_per_row(int H, int nc) { return ((H >> 3) + nc * kWave - 1) / (nc * kW
 // number only the device knows (at most P * cap rows).
 constexpr int64_t kZeroWaves = 16384;
 
-template <bool FP8, bool META>
+template <bool FP8, bool META, bool PREQ>
 ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
   const int nc = pick_nc(a.H, FP8 ? EP_DISPATCH_NC_FP8 : EP_DISPATCH_NC_BF16);
   a.split = parts_per_row(a.H, nc);
@@ -327,12 +327,12 @@ ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
     const int blocks = (int)((waves + EP_ROW_BLOCK_WAVES - 1) / EP_ROW_BLOCK_WAVES);
     const size_t lds = EP_DISPATCH_LDS_BYTES;  // > 0 caps workgroups per CU (occupancy)
     switch (nc) {
-      case 1: dispatch_kernel<1, FP8, META><<<blocks, threads, lds, s>>>(a); break;
-      case 2: dispatch_kernel<2, FP8, META><<<blocks, threads, lds, s>>>(a); break;
-      case 4: dispatch_kernel<4, FP8, META><<<blocks, threads, lds, s>>>(a); break;
-      case 7: dispatch_kernel<7, FP8, META><<<blocks, threads, lds, s>>>(a); break;
-      case 8: dispatch_kernel<8, FP8, META><<<blocks, threads, lds, s>>>(a); break;
-      default: dispatch_kernel<14, FP8, META><<<blocks, threads, lds, s>>>(a); break;
+      case 1: dispatch_kernel<1, FP8, META, PREQ><<<blocks, threads, lds, s>>>(a); break;
+      case 2: dispatch_kernel<2, FP8, META, PREQ><<<blocks, threads, lds, s>>>(a); break;
+      case 4: dispatch_kernel<4, FP8, META, PREQ><<<blocks, threads, lds, s>>>(a); break;
+      case 7: dispatch_kernel<7, FP8, META, PREQ><<<blocks, threads, lds, s>>>(a); break;
+      case 8: dispatch_kernel<8, FP8, META, PREQ><<<blocks, threads, lds, s>>>(a); break;
+      default: dispatch_kernel<14, FP8, META, PREQ><<<blocks, threads, lds, s>>>(a); break;
     }
     EP_LAUNCHED("dispatch_kernel");
   }
@@ -347,19 +347,22 @@ ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
   return EP_OK;
 }
 
-ep_status dispatch_common(const ep_handle* h, uint32_t flags, const void* x, const float* w, void* recv_x,
-                          float* recv_scales, float* recv_weights, int32_t* recv_meta, bool meta,
-                          hipStream_t s) {
+// x: bf16 [T][H]; or, with prequant, E4M3 codes [T][H] and x_scales [T][H/128].
+ep_status dispatch_common(const ep_handle* h, uint32_t flags, const void* x, const float* x_scales, bool prequant,
+                          const float* w, void* recv_x, float* recv_scales, float* recv_weights,
+                          int32_t* recv_meta, bool meta, hipStream_t s) {
   ep_status st = check_handle(h);
   if (st != EP_OK) return st;
-  if (flags & ~(uint32_t)(EP_DISPATCH_FP8 | EP_DISPATCH_ZERO_PADDING))
+  if (flags & ~(uint32_t)(EP_DISPATCH_FP8 | EP_DISPATCH_ZERO_PADDING | EP_DISPATCH_SCALES_COL_MAJOR))
     return fail(EP_ERR_SHAPE, "unknown dispatch flags 0x%x", flags);
-  const bool fp8 = flags & EP_DISPATCH_FP8;
+  const bool fp8 = (flags & EP_DISPATCH_FP8) || prequant;
   const bool zero_pad = flags & EP_DISPATCH_ZERO_PADDING;
   if (fp8 && h->cfg.hidden % 128 != 0)
     return fail(EP_ERR_SHAPE, "fp8 dispatch needs hidden %% 128 == 0 (hidden %d)", h->cfg.hidden);
   const bool rows = h->total_rows > 0;
-  if (h->T > 0 && !x) return fail(EP_ERR_NULL, "x is NULL");
+  if (h->T > 0 && !x) return fail(EP_ERR_NULL, prequant ? "x_codes is NULL" : "x is NULL");
+  if (prequant && h->T > 0 && !x_scales) return fail(EP_ERR_NULL, "x_scales is NULL");
+  if (misaligned(x_scales, 4)) return fail(EP_ERR_SHAPE, "x_scales must be 4-byte aligned");
   if (rows && !recv_x) return fail(EP_ERR_NULL, "recv_x is NULL");
   if (rows && fp8 && !recv_scales) return fail(EP_ERR_NULL, "recv_scales is NULL (fp8)");
   if (meta && h->T > 0 && !w) return fail(EP_ERR_NULL, "topk_weights is NULL");
@@ -394,8 +397,16 @@ ep_status dispatch_common(const ep_handle* h, uint32_t flags, const void* x, con
   a.counts = h->summary_dev;
   a.tail_base = h->tail_base;
   a.num_expanded = h->num_expanded;
-  if (fp8) return meta ? launch_dispatch<true, true>(a, s) : launch_dispatch<true, false>(a, s);
-  return meta ? launch_dispatch<false, true>(a, s) : launch_dispatch<false, false>(a, s);
+  a.x_codes = prequant ? (const uint8_t*)x : nullptr;
+  a.scales_cm = (flags & EP_DISPATCH_SCALES_COL_MAJOR) ? 1 : 0;
+  a.scale_rows = h->total_rows;
+  if (prequant) {
+    a.x = nullptr;
+    a.tok_scales = const_cast<float*>(x_scales);  // read only: the rows' scales come from here
+    return meta ? launch_dispatch<true, true, true>(a, s) : launch_dispatch<true, false, true>(a, s);
+  }
+  if (fp8) return meta ? launch_dispatch<true, true, false>(a, s) : launch_dispatch<true, false, false>(a, s);
+  return meta ? launch_dispatch<false, true, false>(a, s) : launch_dispatch<false, false, false>(a, s);
 }
 
 }  // namespace
@@ -442,32 +453,46 @@ ep_status ep_relayout(ep_handle* h, const int64_t* topk_idx, void* stream, int64
 ep_status ep_dispatch(const ep_handle* h, uint32_t flags, const void* x, const float* topk_weights,
                       void* recv_x, float* recv_scales, float* recv_weights, int32_t* recv_src_meta,
                       void* stream) {
-  return dispatch_common(h, flags, x, topk_weights, recv_x, recv_scales, recv_weights, recv_src_meta, true,
-                         (hipStream_t)stream);
+  return dispatch_common(h, flags, x, nullptr, false, topk_weights, recv_x, recv_scales, recv_weights,
+                         recv_src_meta, true, (hipStream_t)stream);
 }
 
 ep_status ep_dispatch_cached(const ep_handle* h, uint32_t flags, const void* x, void* recv_x,
                              float* recv_scales, void* stream) {
-  return dispatch_common(h, flags, x, nullptr, recv_x, recv_scales, nullptr, nullptr, false,
+  return dispatch_common(h, flags, x, nullptr, false, nullptr, recv_x, recv_scales, nullptr, nullptr, false,
                          (hipStream_t)stream);
 }
 
-ep_status ep_combine(const ep_handle* h, const void* y, const float* topk_weights, void* out, void* stream) {
+ep_status ep_dispatch_prequant(const ep_handle* h, uint32_t flags, const uint8_t* x_codes, const float* x_scales,
+                               const float* topk_weights, void* recv_x, float* recv_scales, float* recv_weights,
+                               int32_t* recv_src_meta, void* stream) {
+  return dispatch_common(h, flags, x_codes, x_scales, true, topk_weights, recv_x, recv_scales, recv_weights,
+                         recv_src_meta, true, (hipStream_t)stream);
+}
+
+ep_status ep_dispatch_prequant_cached(const ep_handle* h, uint32_t flags, const uint8_t* x_codes,
+                                      const float* x_scales, void* recv_x, float* recv_scales, void* stream) {
+  return dispatch_common(h, flags, x_codes, x_scales, true, nullptr, recv_x, recv_scales, nullptr, nullptr,
+                         false, (hipStream_t)stream);
+}
+
+ep_status ep_combine(const ep_handle* h, const void* y, const float* topk_weights, const void* bias, void* out,
+                     void* stream) {
   ep_status st = check_handle(h);
   if (st != EP_OK) return st;
   if (h->T == 0) return EP_OK;
   if (!out) return fail(EP_ERR_NULL, "out is NULL");
   if (h->total_rows > 0 && !y) return fail(EP_ERR_NULL, "y is NULL");
-  if (misaligned(y, 16) || misaligned(out, 16) || misaligned(topk_weights, 4))
-    return fail(EP_ERR_SHAPE, "y / out must be 16-byte aligned, topk_weights 4-byte aligned");
+  if (misaligned(y, 16) || misaligned(out, 16) || misaligned(bias, 16) || misaligned(topk_weights, 4))
+    return fail(EP_ERR_SHAPE, "y / bias / out must be 16-byte aligned, topk_weights 4-byte aligned");
   // Whole rows of up to 8 KiB (K <= 8, so <= 64 KiB of LDS per token and two
   // workgroups per CU) go through the LDS kernel: every wave streams one slot's
   // full row.  Measured faster than the register kernel at hidden 4096 and not
   // at 7168, where a token's rows no longer fit twice per CU.
   if (h->dims.K <= 8 && h->cfg.hidden <= 4096) {
     const int need = ((h->cfg.hidden >> 3) + kWave - 1) / kWave;  // chunks per lane for a whole row
-    CombineArgs a{(const uint16_t*)y, topk_weights, h->dst_row, (uint16_t*)out, (int)h->T, h->dims.K,
-                  h->cfg.hidden, 1};
+    CombineArgs a{(const uint16_t*)y, topk_weights, h->dst_row, (const uint16_t*)bias, (uint16_t*)out,
+                  (int)h->T, h->dims.K, h->cfg.hidden, 1};
     hipStream_t s = (hipStream_t)stream;
     const size_t lds_row = (size_t)h->dims.K * kWave * 16;  // per chunk per lane
     if (h->T >= ((int64_t)1 << 31)) return fail(EP_ERR_OVERFLOW, "combine grid too large");
@@ -484,8 +509,8 @@ ep_status ep_combine(const ep_handle* h, const void* y, const float* topk_weight
     return EP_OK;
   }
   const int nct = std::min(pick_nc(h->cfg.hidden, EP_COMBINE_NCT), 4);
-  CombineArgs a{(const uint16_t*)y, topk_weights, h->dst_row, (uint16_t*)out, (int)h->T, h->dims.K,
-                h->cfg.hidden, parts_per_row(h->cfg.hidden, nct)};
+  CombineArgs a{(const uint16_t*)y, topk_weights, h->dst_row, (const uint16_t*)bias, (uint16_t*)out,
+                (int)h->T, h->dims.K, h->cfg.hidden, parts_per_row(h->cfg.hidden, nct)};
   const int64_t waves = h->T * a.split;
   if (waves >= ((int64_t)1 << 31) / kWave) return fail(EP_ERR_OVERFLOW, "combine grid too large (%lld waves)", (long long)waves);
   const int threads = EP_ROW_BLOCK_WAVES * kWave;

@@ -8,7 +8,8 @@
 // written K times.
 //
 // Combine: every token gathers its K expert rows and reduces them in a fixed
-// slot order in fp32, then rounds to bf16 (section 4.5).
+// slot order in fp32, adds the optional bias (section 3.3), then rounds to
+// bf16 (section 4.5).
 //
 // Work split: one wave per (source token, column part).  Partitioning by source
 // token keeps skewed routing balanced: a hot expert means more rows written,
@@ -55,6 +56,9 @@ struct DispatchArgs {
   const int64_t* counts;         // layout summary: [1] padding rows, [4] tail rows
   const int64_t* tail_base;      // [P+1]
   const int64_t* num_expanded;   // [P]
+  const uint8_t* x_codes;        // [T][H] pre-quantised E4M3 input (tok_scales then holds its scales)
+  int scales_cm;                 // fp8 scales column-major: [H/128][scale_rows]
+  int64_t scale_rows;            // rows of the expanded tensors (the column-major stride)
 };
 
 // Wave-uniform global wave index of the calling lane.
@@ -161,8 +165,11 @@ __device__ __forceinline__ void zero_row_part(uint8_t* recv, int64_t row, int pa
   }
 }
 
-template <int NC, bool FP8, bool META>
+// PREQ: the input is already E4M3 codes (x_codes) with their scales; rows get
+// the bytes unchanged (FP8 only).
+template <int NC, bool FP8, bool META, bool PREQ>
 __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
+  static_assert(!PREQ || FP8, "pre-quantised input is fp8");
   const int gw = wave_index();
   const int lane = lane_id();
   const int nchunk = a.H >> 3;  // 16-byte bf16 chunks per row
@@ -181,10 +188,20 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
     // knows, so per-slot loads inside the store loop would each wait for memory.
     const int my_row = lane < a.K ? a.dst_row[(int64_t)u * a.K + lane] : -1;
     u32x4 v[NC];
+    u32x2 codes[NC];
+    if constexpr (PREQ) {  // 8 code bytes per 16-byte bf16 chunk position
+      const u32x2* csrc = (const u32x2*)(a.x_codes + (int64_t)u * a.H);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int q = tile + c * kWave + lane;
-      v[c] = q < nchunk ? __builtin_nontemporal_load(src + q) : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < NC; ++c) {
+        const int q = tile + c * kWave + lane;
+        codes[c] = q < nchunk ? __builtin_nontemporal_load(csrc + q) : u32x2{0, 0};
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int q = tile + c * kWave + lane;
+        v[c] = q < nchunk ? __builtin_nontemporal_load(src + q) : u32x4{0, 0, 0, 0};
+      }
     }
     if constexpr (!FP8) {
       for (int j = 0; j < a.K; ++j) {
@@ -199,10 +216,9 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
         store_pacing<NC>();
       }
     } else {
-      u32x2 codes[NC];
       const int nblk = a.H >> 7;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
+      for (int c = 0; c < NC && !PREQ; ++c) {
         uint32_t m = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) m = max(m, max(v[c][k] & 0x7FFFu, (v[c][k] >> 16) & 0x7FFFu));
@@ -260,7 +276,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
   }
 }
 
-// fp8 row scales in row order: recv_scales[row][b] = scale of the row's
+// fp8 row scales: recv_scales[row][b] (or [b][row] column-major) = scale of the row's
 // source token (0 for padding rows with zero padding, otherwise untouched; 0
 // for the tail rows of fixed windows).
 __global__ __launch_bounds__(256) void dispatch_scales_kernel(DispatchArgs a) {
@@ -268,8 +284,10 @@ __global__ __launch_bounds__(256) void dispatch_scales_kernel(DispatchArgs a) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t rows = a.cap > 0 ? (int64_t)a.P * a.cap : (int64_t)a.sum_expanded;
   if (i >= rows * nblk) return;
-  const int64_t pr = i / nblk;
-  const int b = (int)(i - pr * nblk);
+  // row-major output: consecutive threads walk a row's blocks; column-major:
+  // consecutive threads walk rows of one block, so either way stores coalesce
+  const int64_t pr = a.scales_cm ? i % rows : i / nblk;
+  const int b = (int)(a.scales_cm ? i / rows : i - pr * nblk);
   int slot;
   int64_t row;
   bool tail = false;
@@ -283,10 +301,11 @@ __global__ __launch_bounds__(256) void dispatch_scales_kernel(DispatchArgs a) {
     tail = l >= a.num_expanded[r];
     slot = tail ? -1 : a.row_slot[a.packed_base[r] + l];
   }
+  float* dst = a.scales_cm ? a.recv_scales + (int64_t)b * a.scale_rows + row : a.recv_scales + row * nblk + b;
   if (slot >= 0)
-    a.recv_scales[row * nblk + b] = a.tok_scales[(int64_t)(slot / a.K) * nblk + b];
+    *dst = a.tok_scales[(int64_t)(slot / a.K) * nblk + b];
   else if (a.zero_pad || tail)
-    a.recv_scales[row * nblk + b] = 0.0f;
+    *dst = 0.0f;
 }
 
 // Test hook: the dispatch kernel's float -> E4M3 conversion applied to an
@@ -311,6 +330,7 @@ struct CombineArgs {
   const uint16_t* y;       // [rows][H] bf16
   const float* w;          // [T][K] or null (unit weights)
   const int32_t* dst_row;  // [T][K]
+  const uint16_t* bias;    // [T][H] bf16 or null, added after the K slots
   uint16_t* out;           // [T][H] bf16
   int T, K, H;
   int split;               // parts per row = ceil((H / 8) / (64 * NCT))
@@ -333,6 +353,15 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
   const int my_row = lane < a.K ? a.dst_row[(int64_t)u * a.K + lane] : -1;
   const float my_w = (lane < a.K && a.w) ? a.w[(int64_t)u * a.K + lane] : 1.0f;
   u32x4* dst = (u32x4*)(a.out + (int64_t)u * a.H);
+  u32x4 bv[NCT];
+  if (a.bias) {
+    const u32x4* bsrc = (const u32x4*)(a.bias + (int64_t)u * a.H);
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int q = tile + c * kWave + lane;
+      bv[c] = q < nchunk ? __builtin_nontemporal_load(bsrc + q) : u32x4{0, 0, 0, 0};
+    }
+  }
 
   float acc[NCT][8];
 #pragma unroll
@@ -371,6 +400,15 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
           acc[c][2 * k + 1] = acc[c][2 * k + 1] + p1;
         }
     }
+  }
+  if (a.bias) {
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[c][2 * k] = acc[c][2 * k] + bf16_lo(bv[c][k]);
+        acc[c][2 * k + 1] = acc[c][2 * k + 1] + bf16_hi(bv[c][k]);
+      }
   }
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
@@ -432,6 +470,14 @@ __global__ __launch_bounds__(512) void combine_lds_kernel(CombineArgs a) {
         const float p1 = wj * bf16_hi(v[k]);
         acc[2 * k] = acc[2 * k] + p0;
         acc[2 * k + 1] = acc[2 * k + 1] + p1;
+      }
+    }
+    if (a.bias) {
+      const u32x4 bv = __builtin_nontemporal_load((const u32x4*)(a.bias + (int64_t)u * a.H) + q);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] = acc[2 * k] + bf16_lo(bv[k]);
+        acc[2 * k + 1] = acc[2 * k + 1] + bf16_hi(bv[k]);
       }
     }
     u32x4 o;

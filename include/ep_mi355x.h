@@ -18,7 +18,7 @@
  *  - Every tensor argument is a DEVICE pointer to row-major, contiguous memory
  *    that the caller allocated and owns; the library never allocates a tensor
  *    that the caller sees and never keeps a caller pointer after returning.
- *    bf16 / fp8 row tensors (x, recv_x, y, out) must be 16-byte aligned, other
+ *    bf16 / fp8 row tensors (x, x_codes, recv_x, y, bias, out) must be 16-byte aligned, other
  *    arrays aligned to their element size (else EP_ERR_SHAPE).
  *  - `stream` is a hipStream_t (0 = the null stream).  All device work of a
  *    call is enqueued on it; calls other than ep_get_layout / ep_relayout
@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 2
+#define EP_ABI_VERSION 3
 
 /* Limits of this build. */
 #define EP_MAX_RANKS 1024
@@ -78,6 +78,7 @@ typedef enum {
 /* Per-call dispatch flags. */
 #define EP_DISPATCH_FP8 1u          /* emit E4M3 codes + fp32 scales per 128 channels  */
 #define EP_DISPATCH_ZERO_PADDING 2u /* zero the alignment padding rows' payload         */
+#define EP_DISPATCH_SCALES_COL_MAJOR 4u /* fp8: recv_scales as [H/128, total_rows]       */
 
 /* Shape of one dispatch/combine problem.  The tutorial's EPBuffer is built for
  * a token capacity, hidden size and top-k, and dispatch takes num_experts and
@@ -145,8 +146,12 @@ ep_status ep_relayout(ep_handle *h, const int64_t *topk_idx, void *stream, int64
  *   x             device, bf16 [T, H].
  *   topk_weights  device, fp32 [T, K].
  *   recv_x        device, [total_rows, H]: bf16, or E4M3 bytes with EP_DISPATCH_FP8.
- *   recv_scales   device, fp32 [total_rows, H/128] row-major; required with
- *                 EP_DISPATCH_FP8 (H % 128 == 0), ignored otherwise.
+ *   recv_scales   device, fp32 [total_rows, H/128] row-major, or [H/128,
+ *                 total_rows] with EP_DISPATCH_SCALES_COL_MAJOR (scale b of row
+ *                 r at b * total_rows + r: one scale position contiguous across
+ *                 rows, no row padding; TileLang tutorial ch. 38, section 3.6);
+ *                 required with EP_DISPATCH_FP8 (H % 128 == 0), ignored
+ *                 otherwise.
  *   recv_weights  device, fp32 [total_rows].
  *   recv_src_meta device, int32 [total_rows, 2]: (u, j) of the slot a row came
  *                 from ((-1, -1) for padding rows).
@@ -175,6 +180,24 @@ ep_status ep_dispatch(const ep_handle *h, uint32_t flags, const void *x, const f
 ep_status ep_dispatch_cached(const ep_handle *h, uint32_t flags, const void *x, void *recv_x,
                              float *recv_scales, void *stream);
 
+/* ep_dispatch_prequant / ep_dispatch_prequant_cached -- dispatch of input that
+ * the caller already quantised: the pair (E4M3 data, fp32 scale per 128
+ * channels) that the tutorial's dispatch takes in fp8 mode (TileLang
+ * tutorial ch. 38, section 3.6 (2)).
+ *   x_codes   device, u8 [T, H] (E4M3FN bytes; copied unchanged, any pattern).
+ *   x_scales  device, fp32 [T, H/128] row-major (copied unchanged).
+ * The output is fp8 whatever EP_DISPATCH_FP8 says: every valid row gets its
+ * token's bytes and scales; everything else is as in ep_dispatch /
+ * ep_dispatch_cached (padding, tails, metadata, EP_DISPATCH_SCALES_COL_MAJOR).
+ * H % 128 == 0.  Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_HIP. */
+ep_status ep_dispatch_prequant(const ep_handle *h, uint32_t flags, const uint8_t *x_codes,
+                               const float *x_scales, const float *topk_weights, void *recv_x,
+                               float *recv_scales, float *recv_weights, int32_t *recv_src_meta,
+                               void *stream);
+ep_status ep_dispatch_prequant_cached(const ep_handle *h, uint32_t flags, const uint8_t *x_codes,
+                                      const float *x_scales, void *recv_x, float *recv_scales,
+                                      void *stream);
+
 /* --------------------------------------------------------------------------
  * ep_combine -- weighted reduction of the K expert rows of every token back
  * to token order (TileLang tutorial ch. 38, sections 2.1, 3.6(5) and 4.5).
@@ -182,17 +205,21 @@ ep_status ep_dispatch_cached(const ep_handle *h, uint32_t flags, const void *x, 
  *   y             device, bf16 [total_rows, H] (expert outputs; padding rows
  *                 are never read).
  *   topk_weights  device, fp32 [T, K], or NULL for unit weights.
+ *   bias          device, bf16 [T, H], or NULL: the tutorial's optional
+ *                 combine bias (a residual or the shared experts' output,
+ *                 section 3.3), added once per token.
  *   out           device, bf16 [T, H].
  * out[u][h] = bf16_rne(acc) with acc = +0 and, for j = 0..K-1 over valid
  * slots in order, acc = fl(acc + fl(w[u][j] * float(y[row(u,j)][h]))) in fp32
- * (no fused multiply-add).  A token without valid slots gets +0.  In fixed
- * mode a slot whose row was dropped counts as unused.
+ * (no fused multiply-add); then, with a bias, acc = fl(acc + float(bias[u][h])).
+ * A token without valid slots gets +0 (or its bias).  In fixed mode a slot
+ * whose row was dropped counts as unused.
  * The backward of dispatch is this call and the backward of combine is
  * ep_dispatch_cached, with the same handle (tutorial 2.3).
  * Errors: EP_ERR_NULL, EP_ERR_HIP.
  */
-ep_status ep_combine(const ep_handle *h, const void *y, const float *topk_weights, void *out,
-                     void *stream);
+ep_status ep_combine(const ep_handle *h, const void *y, const float *topk_weights, const void *bias,
+                     void *out, void *stream);
 
 /* ep_handle_free -- waits for the handle's own layout work, then releases its
  * device and pinned host memory.  The caller guarantees no other call using

@@ -94,7 +94,9 @@ def test_null_arguments(L):
     assert L.ep_get_layout(ctypes.byref(cfg), ctypes.c_void_p(1), None, None, None) == ep.Status.ERR_NULL
     for call in (lambda: L.ep_dispatch(None, 0, None, None, None, None, None, None, None),
                  lambda: L.ep_dispatch_cached(None, 0, None, None, None, None),
-                 lambda: L.ep_combine(None, None, None, None, None),
+                 lambda: L.ep_combine(None, None, None, None, None, None),
+                 lambda: L.ep_dispatch_prequant(None, 0, None, None, None, None, None, None, None, None),
+                 lambda: L.ep_dispatch_prequant_cached(None, 0, None, None, None, None, None),
                  lambda: L.ep_relayout(None, None, None, None),
                  lambda: L.ep_handle_counts(None, None, None, None),
                  lambda: L.ep_handle_status(None, ctypes.byref(ctypes.c_uint32()), None),

@@ -538,3 +538,114 @@ def test_fixed_windows_full_size(name, fit):
     h.free()
     del rx, rw, rm, out, xd
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------
+# API variants: column-major scales, pre-quantised fp8 input, combine bias
+# --------------------------------------------------------------------------
+
+VARIANT_CASES = [SMALL[0], SMALL[1], SMALL[2], SMALL[4], SMALL[7]]
+
+
+def _dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+@pytest.mark.parametrize("w", VARIANT_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("mode", ["exact", "fixed"])
+def test_variants_small(w, mode):
+    topk = routing_with_holes(w, 14)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    W = max(1, int(np.median(lay.num_expanded))) if mode == "fixed" else 0
+    cfg = ep.Config(w.P, w.S, w.H, w.K, w.E, w.A, num_worst_rows=W)
+    say("variants", w.name, mode, "W", W)
+    h = ep.get_layout(cfg, torch.from_numpy(topk).to(DEV))
+    R = h.total_rows
+    x = synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    rng = np.random.default_rng(15)
+    codes = rng.integers(0, 256, (w.T, w.H), dtype=np.uint8)
+    scales = rng.standard_normal((w.T, w.H // 128)).astype(np.float32)
+    nb = w.H // 128
+    for src in ("fused", "prequant"):
+        for cm in (False, True):
+            for zp in (False, True):
+                say("variant dispatch", w.name, mode, src, "col-major" if cm else "row-major", "zp" if zp else "")
+                xin = xd if src == "fused" else (_dev_u8(codes), torch.from_numpy(scales).to(DEV))
+                rx = torch.full((R, w.H), 0x7F, dtype=torch.uint8, device=DEV)
+                sc = torch.full((nb, R) if cm else (R, nb), float("nan"), dtype=torch.float32, device=DEV)
+                rw = torch.full((R,), float("nan"), dtype=torch.float32, device=DEV)
+                rm = torch.full((R, 2), 77, dtype=torch.int32, device=DEV)
+                ep.dispatch(h, xin, wd, fp8=True, zero_padding=zp, scales_col_major=cm, out=(rx, sc, rw, rm))
+                torch.cuda.synchronize()
+                kw = dict(x=x) if src == "fused" else dict(x_codes=codes, x_scales=scales)
+                ox, osc, ow, om, _ = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=zp, topk_weights=wt,
+                                                             capacity=W, scales_col_major=cm, fill=0x7F, **kw)
+                np.testing.assert_array_equal(rx.cpu().numpy(), ox)
+                np.testing.assert_array_equal(rm.cpu().numpy(), om)
+                np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+                tail = (np.arange(R) % W >= np.repeat(lay.num_expanded, W)) if W else np.zeros(R, bool)
+                touched = (om[:, 0] >= 0) | zp | tail
+                gs = sc.cpu().numpy()
+                gs_rows = gs.T if cm else gs
+                os_rows = osc.T if cm else osc
+                np.testing.assert_array_equal(gs_rows[touched].view(np.uint32), os_rows[touched].view(np.uint32))
+                assert np.all(np.isnan(gs_rows[~touched]))
+                # cached dispatch of the same input reproduces payload and scales
+                tmask = torch.from_numpy(touched).to(DEV)
+                cx = rx.clone()
+                cx[tmask] = 0x55
+                csc = sc.clone()
+                (csc.T if cm else csc)[tmask] = 3.0
+                ep.dispatch_cached(h, xin, fp8=True, zero_padding=zp, scales_col_major=cm, out=(cx, csc))
+                torch.cuda.synchronize()
+                assert torch.equal(cx, rx)
+                assert torch.equal(csc.view(torch.int32), sc.view(torch.int32))
+    # combine with a bias, with and without weights
+    y = synth.gen_expert_out(w, R)
+    bias = synth.gen_bf16_rows(w.seed, wl.STREAM_GRAD_OUT, w.T, w.H)
+    for weights in (wt, None):
+        say("combine bias", w.name, mode, "weighted" if weights is not None else "unit")
+        out = ep.combine(h, dev_bf16(y), None if weights is None else wd, bias=dev_bf16(bias))
+        torch.cuda.synchronize()
+        exp = oracle.combine_general(lay, w.H, y, weights, bias=bias, capacity=W)
+        np.testing.assert_array_equal(host_u16(out), exp)
+    h.free()
+
+
+def test_variants_full_size():
+    """DSv3 shapes: pre-quantised fp8 input with column-major scales, and combine with a
+    bias (the shared-expert output in the pages' usage), against the oracle."""
+    w = D["dsv3-fp8-p8-s4096-e256-k8-h7168"]
+    topk = synth.gen_routing(w)
+    lay, h = layout_both(w, topk)
+    R = lay.total_rows
+    x = synth.gen_x(w)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    say("oracle quantize", w.name)
+    codes, scales = quantize_all(x, w.H)
+    say("prequant dispatch col-major", w.name)
+    rx, sc, rw, rm = ep.dispatch(h, (_dev_u8(codes), torch.from_numpy(scales).to(DEV)), wd, zero_padding=True,
+                                 scales_col_major=True)
+    torch.cuda.synchronize()
+    assert sc.shape == (w.H // 128, R)
+    _, _, ow, om, _ = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=True, topk_weights=wt)
+    np.testing.assert_array_equal(rm.cpu().numpy(), om)
+    check_payload_rows(rx, None, lay, True, codes, scales, sc.t())
+    fx, fsc, _, _ = ep.dispatch(h, xd, wd, fp8=True, zero_padding=True, scales_col_major=True)
+    assert torch.equal(fx, rx) and torch.equal(fsc.view(torch.int32), sc.view(torch.int32))
+    del rx, sc, fx, fsc
+    say("combine with bias", w.name)
+    y, _, _, _ = ep.dispatch(h, xd, wd, zero_padding=True)
+    bias = synth.gen_grad_out(w)
+    out = ep.combine(h, y, wd, bias=dev_bf16(bias))
+    torch.cuda.synchronize()
+    toks = np.arange(0, w.T, 4)
+    got = host_u16(gather_rows(out, toks))
+    exp = np.concatenate([oracle.combine_identity(w.K, w.H, False, topk, x, wt, u, u + 1, bias=bias)
+                          for u in toks])
+    np.testing.assert_array_equal(got, exp)
+    h.free()
+    torch.cuda.empty_cache()
