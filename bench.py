@@ -8,8 +8,18 @@ weighted combine back to token order.  Inputs are resident in HBM before the
 timed region; the handle and the expanded tensors are long-lived buffers
 reused every step, as the pages recommend for the EP buffer.
 
+The same step is also timed with fixed-length windows (num_worst_rows: every
+window a 1024-row bucket above the largest one, no read-back), reported under
+"fixed_windows"; the headline value is the exact-length step.
+
 Prints ONE JSON line.  Usage:
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME] [--no-cpu] [--no-fixed]
+
+`python bench.py --calls` instead times every call of the library on every
+workload (median of 10 back-to-back calls each, HIP events) and prints one
+JSON line per workload: layout, dispatch, cached dispatch, combine, combine
+with a bias, fixed-window dispatch, and for fp8 workloads the pre-quantised
+and column-major-scale dispatches, each with its ledger bytes and % of HBM.
 """
 
 from __future__ import annotations
@@ -134,6 +144,194 @@ def cpu_baseline(w, topk, x, wt, budget_s: float = 25.0) -> dict:
 
 
 # ---------------------------------------------------------------------------
+# fixed-length windows
+# ---------------------------------------------------------------------------
+
+def fixed_leg(ep, h_exact, w, topk, topk_d, x_d, w_d, out, steps: int, warmup: int) -> dict:
+    """The step with every window fixed at W rows (W = the largest window rounded up to
+    1024 rows): layout without any read-back, dispatch (tails zeroed), combine."""
+    import numpy as np
+    import torch
+
+    ne, _, _ = h_exact.counts()
+    W = int(-(-int(ne.max()) // 1024) * 1024)
+    T, K, H = w.T, w.K, w.H
+    dev = x_d.device
+    log("fixed windows W =", W)
+    h = ep.get_layout(ep.Config(w.P, w.S, H, K, w.E, w.A, num_worst_rows=W), topk_d)
+    R = h.total_rows
+    recv_x = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    recv_w = torch.empty(R, dtype=torch.float32, device=dev)
+    recv_m = torch.empty((R, 2), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ep.relayout(h, topk_d)
+        if ev is not None:
+            ev[1].record(stream)
+        ep.dispatch(h, x_d, w_d, fp8=False, zero_padding=w.zero_padding, out=(recv_x, None, recv_w, recv_m))
+        if ev is not None:
+            ev[2].record(stream)
+        ep.combine(h, recv_x, w_d, out=out)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    flags, dropped = h.status()
+    l_us = 1e3 * sum(e[0].elapsed_time(e[1]) for e in events) / steps
+    d_us = 1e3 * sum(e[1].elapsed_time(e[2]) for e in events) / steps
+    c_us = 1e3 * sum(e[2].elapsed_time(e[3]) for e in events) / steps
+    rows = int((topk >= 0).sum())
+    zeroed = R - rows if w.zero_padding else int(np.maximum(W - ne, 0).sum())
+    led = ledger(T, K, H, rows, zeroed, False, True)
+    led["dispatch"] += (R - rows - zeroed) * 12  # metadata of padding rows left unzeroed
+    h.free()
+    return {"num_worst_rows": W, "rows": R, "tail_rows": int(np.maximum(W - ne, 0).sum()),
+            "dropped_rows": dropped, "status_flags": flags, "ms_per_step": ms_step,
+            "tokens_per_s": T / (ms_step * 1e-3), "layout_us_device": l_us, "dispatch_us": d_us,
+            "combine_us": c_us, "dispatch_bytes": led["dispatch"],
+            "dispatch_frac_hbm": led["dispatch"] / (d_us * 1e3) / HBM_PEAK_GBPS,
+            "combine_frac_hbm": led["combine"] / (c_us * 1e3) / HBM_PEAK_GBPS}
+
+
+# ---------------------------------------------------------------------------
+# per-call table
+# ---------------------------------------------------------------------------
+
+def _median_us(fn, reps: int = 10) -> float:
+    import statistics
+
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return statistics.median(ts) * 1e3
+
+
+def calls_table() -> int:
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import combine_topk_idx_expert_amd as ep
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    for name in synth.CONFIG_ORDER:
+        w = synth.CONFIGS[name]
+        T, K, H = w.T, w.K, w.H
+        log("calls", name)
+        topk = synth.gen_routing(w)
+        x = synth.gen_x(w)
+        wt = synth.gen_weights(w)
+        topk_d = torch.from_numpy(topk).to(dev)
+        x_d = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        w_d = torch.from_numpy(wt).to(dev)
+        h = ep.get_layout(ep.Config(w.P, w.S, H, K, w.E, w.A), topk_d)
+        R = h.total_rows
+        ne, _, _ = h.counts()
+        rows = int((topk >= 0).sum())
+        pad = R - rows
+        fp8 = w.fp8
+        nb = H // 128
+        r = {"workload": name, "T": T, "rows": rows, "pad": pad, "dtype": "fp8" if fp8 else "bf16"}
+
+        def put(key, us, nbytes):
+            r[key + "_us"] = round(us, 1)
+            r[key + "_GBps"] = round(nbytes / us / 1e3, 1)
+            r[key + "_frac_hbm"] = round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)
+
+        torch.cuda.synchronize()
+        lt = []
+        for _ in range(10):
+            t0 = time.perf_counter()
+            ep.relayout(h, topk_d)
+            lt.append(time.perf_counter() - t0)
+        r["layout_us_incl_host_sync"] = round(statistics.median(lt) * 1e6, 1)
+        led = ledger(T, K, H, rows, pad, fp8, w.zero_padding)
+        rx = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+        sc = torch.empty((R, nb), dtype=torch.float32, device=dev) if fp8 else None
+        rw = torch.empty(R, dtype=torch.float32, device=dev)
+        rm = torch.empty((R, 2), dtype=torch.int32, device=dev)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        put("dispatch", _median_us(lambda: ep.dispatch(h, x_d, w_d, fp8, w.zero_padding, out=(rx, sc, rw, rm))),
+            led["dispatch"])
+        b = 1 if fp8 else 2
+        sf = 4 * nb if fp8 else 0
+        cached = T * H * 2 + 4 * T * K + rows * (H * b + sf) + (pad * (H * b + sf) if w.zero_padding else 0)
+        put("cached", _median_us(lambda: ep.dispatch_cached(h, x_d, fp8, w.zero_padding, out=(rx, sc))), cached)
+        y = torch.empty((R, H), dtype=torch.bfloat16, device=dev).normal_()
+        put("combine", _median_us(lambda: ep.combine(h, y, w_d, out=out)), led["combine"])
+        bias = torch.empty((T, H), dtype=torch.bfloat16, device=dev).normal_()
+        put("combine_bias", _median_us(lambda: ep.combine(h, y, w_d, bias=bias, out=out)),
+            led["combine"] + T * H * 2)
+        if fp8:
+            codes = torch.randint(0, 256, (T, H), dtype=torch.uint8, device=dev)
+            xs = torch.rand((T, nb), dtype=torch.float32, device=dev)
+            pre = T * H + T * nb * 4 + 8 * T * K + (led["dispatch"] - led["dispatch_read"])
+            put("dispatch_prequant",
+                _median_us(lambda: ep.dispatch(h, (codes, xs), w_d, zero_padding=w.zero_padding,
+                                               out=(rx, sc, rw, rm))), pre)
+            sc_cm = torch.empty((nb, R), dtype=torch.float32, device=dev)
+            put("dispatch_col_major_scales",
+                _median_us(lambda: ep.dispatch(h, x_d, w_d, True, w.zero_padding, scales_col_major=True,
+                                               out=(rx, sc_cm, rw, rm))), led["dispatch"])
+            del codes, xs, sc_cm
+        del rx, sc, rw, rm, y, bias
+        torch.cuda.empty_cache()
+        # fixed windows: a 1024-row bucket above the largest window
+        W = int(-(-int(ne.max()) // 1024) * 1024)
+        hf = ep.get_layout(ep.Config(w.P, w.S, H, K, w.E, w.A, num_worst_rows=W), topk_d)
+        RF = hf.total_rows
+        torch.cuda.synchronize()
+        lt = []
+        for _ in range(10):
+            t0 = time.perf_counter()
+            ep.relayout(hf, topk_d)
+            lt.append(time.perf_counter() - t0)
+        torch.cuda.synchronize()
+        r["fixed_num_worst_rows"] = W
+        r["fixed_layout_host_us"] = round(statistics.median(lt) * 1e6, 1)
+        r["fixed_layout_device_us"] = round(_median_us(lambda: ep.relayout(hf, topk_d)), 1)
+        rxf = torch.empty((RF, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+        scf = torch.empty((RF, nb), dtype=torch.float32, device=dev) if fp8 else None
+        rwf = torch.empty(RF, dtype=torch.float32, device=dev)
+        rmf = torch.empty((RF, 2), dtype=torch.int32, device=dev)
+        tail = int(np.maximum(W - ne, 0).sum())
+        zeroed = (pad if w.zero_padding else 0) + tail
+        fixed_bytes = (T * H * 2 + 8 * T * K + rows * (H * b + sf) + RF * 12 + zeroed * (H * b + sf))
+        put("fixed_dispatch",
+            _median_us(lambda: ep.dispatch(hf, x_d, w_d, fp8, w.zero_padding, out=(rxf, scf, rwf, rmf))),
+            fixed_bytes)
+        hf.free()
+        h.free()
+        del rxf, scf, rwf, rmf, out, x_d
+        torch.cuda.empty_cache()
+        print(json.dumps(r), flush=True)
+    return 0
+
+
+# ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
 
@@ -144,6 +342,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-fixed", action="store_true", help="skip the fixed-length-window leg")
+    ap.add_argument("--calls", action="store_true", help="per-call table over all workloads")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run a plain torch copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -152,6 +352,8 @@ def main() -> int:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the P "
               "expert-parallel ranks are virtual windows in one GPU's HBM.", file=sys.stderr)
         return 2
+    if args.calls:
+        return calls_table()
 
     import numpy as np
     import torch
@@ -264,6 +466,9 @@ def main() -> int:
             "expanded_rows": R, "padding_rows": pad,
         },
     }
+
+    if not args.no_fixed:
+        result["fixed_windows"] = fixed_leg(ep, h, w, topk, topk_d, x_d, w_d, out, args.steps, args.warmup)
 
     if not args.no_cpu:
         log("cpu baseline (oracle, one thread)")

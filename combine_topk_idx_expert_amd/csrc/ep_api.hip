@@ -299,7 +299,12 @@ ep_status check_handle(const ep_handle* h) {
 #define EP_COMBINE_G 8
 #endif
 
-// Largest instantiated chunk count <= want that the row still needs.
+// Column part per wave (16-byte chunks per lane) of the dispatch kernels: a
+// build-time choice, NC KiB of bf16 input per wave.
+constexpr int kNcBf16 = EP_DISPATCH_NC_BF16;
+constexpr int kNcFp8 = EP_DISPATCH_NC_FP8;
+
+// Largest instantiated chunk count <= want that the row still needs (combine).
 int pick_nc(int H, int want) {
   const int need = ((H >> 3) + kWave - 1) / kWave;  // chunks per lane for the whole row
   const int nc = std::min(want, need);
@@ -312,28 +317,21 @@ int parts_per_row(int H, int nc) { return ((H >> 3) + nc * kWave - 1) / (nc * kW
 // number only the device knows (at most P * cap rows).
 constexpr int64_t kZeroWaves = 16384;
 
-template <bool FP8, bool META, bool PREQ>
+template <bool FP8, bool META, bool PREQ, bool FIXED>
 ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
-  const int nc = pick_nc(a.H, FP8 ? EP_DISPATCH_NC_FP8 : EP_DISPATCH_NC_BF16);
+  constexpr int nc = FP8 ? kNcFp8 : kNcBf16;
   a.split = parts_per_row(a.H, nc);
-  const int64_t out_rows = a.cap > 0 ? (int64_t)a.P * a.cap : (int64_t)a.sum_expanded;
+  const int64_t out_rows = FIXED ? (int64_t)a.P * a.cap : (int64_t)a.sum_expanded;
   const int64_t meta_items = META ? (out_rows + kWave - 1) / kWave : 0;
-  a.zero_waves = a.cap > 0 ? (int)std::min<int64_t>((int64_t)a.P * a.cap * a.split, kZeroWaves) : 0;
-  const int64_t zero_items = a.cap > 0 ? a.zero_waves : (a.zero_pad ? (int64_t)a.total_pad * a.split : 0);
+  a.zero_waves = FIXED ? (int)std::min<int64_t>((int64_t)a.P * a.cap * a.split, kZeroWaves) : 0;
+  const int64_t zero_items = FIXED ? a.zero_waves : (a.zero_pad ? (int64_t)a.total_pad * a.split : 0);
   const int64_t waves = (int64_t)a.T * a.split + zero_items + meta_items;
   if (waves >= ((int64_t)1 << 31) / kWave) return fail(EP_ERR_OVERFLOW, "dispatch grid too large (%lld waves)", (long long)waves);
   if (waves > 0) {
     const int threads = EP_ROW_BLOCK_WAVES * kWave;
     const int blocks = (int)((waves + EP_ROW_BLOCK_WAVES - 1) / EP_ROW_BLOCK_WAVES);
     const size_t lds = EP_DISPATCH_LDS_BYTES;  // > 0 caps workgroups per CU (occupancy)
-    switch (nc) {
-      case 1: dispatch_kernel<1, FP8, META, PREQ><<<blocks, threads, lds, s>>>(a); break;
-      case 2: dispatch_kernel<2, FP8, META, PREQ><<<blocks, threads, lds, s>>>(a); break;
-      case 4: dispatch_kernel<4, FP8, META, PREQ><<<blocks, threads, lds, s>>>(a); break;
-      case 7: dispatch_kernel<7, FP8, META, PREQ><<<blocks, threads, lds, s>>>(a); break;
-      case 8: dispatch_kernel<8, FP8, META, PREQ><<<blocks, threads, lds, s>>>(a); break;
-      default: dispatch_kernel<14, FP8, META, PREQ><<<blocks, threads, lds, s>>>(a); break;
-    }
+    dispatch_kernel<nc, FP8, META, PREQ, FIXED><<<blocks, threads, lds, s>>>(a);
     EP_LAUNCHED("dispatch_kernel");
   }
   if constexpr (FP8) {
@@ -345,6 +343,11 @@ ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
     }
   }
   return EP_OK;
+}
+
+template <bool FP8, bool META, bool PREQ>
+ep_status launch_dispatch_mode(const DispatchArgs& a, hipStream_t s) {
+  return a.cap > 0 ? launch_dispatch<FP8, META, PREQ, true>(a, s) : launch_dispatch<FP8, META, PREQ, false>(a, s);
 }
 
 // x: bf16 [T][H]; or, with prequant, E4M3 codes [T][H] and x_scales [T][H/128].
@@ -403,10 +406,10 @@ ep_status dispatch_common(const ep_handle* h, uint32_t flags, const void* x, con
   if (prequant) {
     a.x = nullptr;
     a.tok_scales = const_cast<float*>(x_scales);  // read only: the rows' scales come from here
-    return meta ? launch_dispatch<true, true, true>(a, s) : launch_dispatch<true, false, true>(a, s);
+    return meta ? launch_dispatch_mode<true, true, true>(a, s) : launch_dispatch_mode<true, false, true>(a, s);
   }
-  if (fp8) return meta ? launch_dispatch<true, true, false>(a, s) : launch_dispatch<true, false, false>(a, s);
-  return meta ? launch_dispatch<false, true, false>(a, s) : launch_dispatch<false, false, false>(a, s);
+  if (fp8) return meta ? launch_dispatch_mode<true, true, false>(a, s) : launch_dispatch_mode<true, false, false>(a, s);
+  return meta ? launch_dispatch_mode<false, true, false>(a, s) : launch_dispatch_mode<false, false, false>(a, s);
 }
 
 }  // namespace
