@@ -313,8 +313,8 @@ int pick_nc(int H, int want) {
 
 int parts_per_row(int H, int nc) { return ((H >> 3) + nc * kWave - 1) / (nc * kWave); }
 
-// Fixed windows: waves that stride over the padding and tail rows, whose
-// number only the device knows (at most P * cap rows).
+// Fixed windows: waves that stride over the padding and tail rows (whole rows),
+// whose number only the device knows (at most P * cap rows).
 constexpr int64_t kZeroWaves = 16384;
 
 template <bool FP8, bool META, bool PREQ, bool FIXED>
@@ -323,7 +323,7 @@ ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
   a.split = parts_per_row(a.H, nc);
   const int64_t out_rows = FIXED ? (int64_t)a.P * a.cap : (int64_t)a.sum_expanded;
   const int64_t meta_items = META ? (out_rows + kWave - 1) / kWave : 0;
-  a.zero_waves = FIXED ? (int)std::min<int64_t>((int64_t)a.P * a.cap * a.split, kZeroWaves) : 0;
+  a.zero_waves = FIXED ? (int)std::min<int64_t>((int64_t)a.P * a.cap, kZeroWaves) : 0;
   const int64_t zero_items = FIXED ? a.zero_waves : (a.zero_pad ? (int64_t)a.total_pad * a.split : 0);
   const int64_t waves = (int64_t)a.T * a.split + zero_items + meta_items;
   if (waves >= ((int64_t)1 << 31) / kWave) return fail(EP_ERR_OVERFLOW, "dispatch grid too large (%lld waves)", (long long)waves);

@@ -248,15 +248,28 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
       const int part = (gw - token_items) - p * a.split;
       zero_row_part<NC, FP8>(recv, a.pad_rows[p], part, out_row_bytes, nchunk, lane);
     } else {
-      // fixed windows: padding rows (if asked) then tail rows (always), counted on the device
+      // Fixed windows: padding rows (if asked) then tail rows (always),
+      // counted on the device.  Wave w zeroes whole rows z = z0 + w, z0 + w +
+      // zero_waves, ...: the waves together sweep the list front to back.
+      // Tail rows are found by one search, then followed window by window.
       const int64_t npad = a.counts[1], ntail = a.counts[4];
       const int64_t z0 = a.zero_pad ? 0 : npad;
-      const int64_t nitems = (npad + ntail - z0) * a.split;
-      for (int64_t it = gw - token_items; it < nitems; it += a.zero_waves) {
-        const int64_t z = z0 + it / a.split;
-        const int part = (int)(it - (z - z0) * a.split);
-        const int64_t row = z < npad ? (int64_t)a.pad_rows[z] : tail_row(a, z - npad);
-        zero_row_part<NC, FP8>(recv, row, part, out_row_bytes, nchunk, lane);
+      int win = -1;
+      for (int64_t z = z0 + (gw - token_items); z < npad + ntail; z += a.zero_waves) {
+        int64_t row;
+        if (z < npad) {
+          row = a.pad_rows[z];
+        } else {
+          const int64_t k = z - npad;
+          if (win < 0) {
+            row = tail_row(a, k);
+            win = (int)(row / a.cap);
+          }
+          while (a.tail_base[win + 1] <= k) ++win;
+          row = (int64_t)win * a.cap + a.cap - (a.tail_base[win + 1] - a.tail_base[win]) + (k - a.tail_base[win]);
+        }
+        for (int part = 0; part < a.split; ++part)
+          zero_row_part<NC, FP8>(recv, row, part, out_row_bytes, nchunk, lane);
       }
     }
   } else if (META) {
