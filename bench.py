@@ -20,6 +20,11 @@ workload (median of 10 back-to-back calls each, HIP events) and prints one
 JSON line per workload: layout, dispatch, cached dispatch, combine, combine
 with a bias, fixed-window dispatch, and for fp8 workloads the pre-quantised
 and column-major-scale dispatches, each with its ledger bytes and % of HBM.
+
+`python bench.py --overlap` times the pages' overlap pattern on the DSv3 BF16
+workload: dispatch issued on the library's communication stream while the
+shared experts (a bf16 MLP, hidden 7168 -> 2 x 2048 -> 7168, torch.matmul)
+run on the compute stream, against the two run back to back.
 """
 
 from __future__ import annotations
@@ -332,6 +337,79 @@ def calls_table() -> int:
 
 
 # ---------------------------------------------------------------------------
+# overlap with compute
+# ---------------------------------------------------------------------------
+
+def overlap_table(workload: str, steps: int) -> int:
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import combine_topk_idx_expert_amd as ep
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.CONFIGS[workload]
+    T, K, H = w.T, w.K, w.H
+    topk_d = torch.from_numpy(synth.gen_routing(w)).to(dev)
+    x_d = torch.from_numpy(synth.gen_x(w).view(np.int16)).to(dev).view(torch.bfloat16)
+    w_d = torch.from_numpy(synth.gen_weights(w)).to(dev)
+    h = ep.get_layout(ep.Config(w.P, w.S, H, K, w.E, w.A), topk_d)
+    R = h.total_rows
+    outs = (torch.empty((R, H), dtype=torch.bfloat16, device=dev), None,
+            torch.empty(R, dtype=torch.float32, device=dev), torch.empty((R, 2), dtype=torch.int32, device=dev))
+    inter = 2048  # shared-expert width of the DSv3-like shape
+    g = torch.Generator(device=dev).manual_seed(0)
+    w1 = (torch.randn((H, 2 * inter), device=dev, generator=g) * H ** -0.5).to(torch.bfloat16)
+    w2 = (torch.randn((inter, H), device=dev, generator=g) * inter ** -0.5).to(torch.bfloat16)
+
+    def shared():
+        gu = torch.matmul(x_d, w1)
+        a = torch.nn.functional.silu(gu[:, :inter]) * gu[:, inter:]
+        return torch.matmul(a, w2)
+
+    def disp():
+        return ep.dispatch(h, x_d, w_d, zero_padding=w.zero_padding, out=outs)
+
+    def serial():
+        shared()
+        disp()
+
+    def overlapped():
+        pending = ep.dispatch(h, x_d, w_d, zero_padding=w.zero_padding, out=outs, async_with_compute_stream=True)
+        shared()
+        pending.wait()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return statistics.median(ts)
+
+    res = {}
+    for _ in range(2):  # interleaved twice; the second pass is reported
+        res = {"dispatch_us": timed(disp), "shared_experts_us": timed(shared), "serial_us": timed(serial),
+               "overlapped_us": timed(overlapped)}
+    d, sh = res["dispatch_us"], res["shared_experts_us"]
+    res["hidden_frac_of_dispatch"] = (res["serial_us"] - res["overlapped_us"]) / d
+    flops = 2.0 * T * H * 2 * inter + 2.0 * T * inter * H
+    res["shared_experts_TFLOPs"] = flops / (sh * 1e-6) / 1e12
+    out = {"workload": workload, "overlap": {k: round(v, 3) for k, v in res.items()}}
+    h.free()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+# ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
 
@@ -344,6 +422,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-fixed", action="store_true", help="skip the fixed-length-window leg")
     ap.add_argument("--calls", action="store_true", help="per-call table over all workloads")
+    ap.add_argument("--overlap", action="store_true", help="dispatch overlapped with shared experts")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run a plain torch copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -354,6 +433,8 @@ def main() -> int:
         return 2
     if args.calls:
         return calls_table()
+    if args.overlap:
+        return overlap_table(args.workload, args.steps)
 
     import numpy as np
     import torch

@@ -21,6 +21,7 @@ from ._native import (  # noqa: F401
     EP_ABI_VERSION,
     Config,
     EpError,
+    EventOverlap,
     Handle,
     LibraryMissing,
     STATUS_ROUTING,
@@ -28,6 +29,7 @@ from ._native import (  # noqa: F401
     Status,
     TENSORS,
     combine,
+    comm_stream,
     debug_e4m3_encode,
     dispatch,
     dispatch_cached,

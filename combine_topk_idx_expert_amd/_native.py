@@ -254,6 +254,60 @@ def _hip_memcpy_d2d(dst: int, src: int, nbytes: int, stream: int) -> None:
         raise EpError(Status.ERR_HIP, f"hipMemcpyAsync failed ({rc})")
 
 
+class EventOverlap:
+    """Work enqueued on the library's communication stream, not yet ordered before the
+    caller's stream: the tutorial's EventOverlap (ch. 38, section 3.4).  ``wait()`` makes the
+    caller's current stream wait for it and returns the call's results."""
+
+    def __init__(self, event, result):
+        self.event = event
+        self._result = result
+
+    def wait(self):
+        import torch
+
+        torch.cuda.current_stream().wait_event(self.event)
+        return self._result
+
+
+_comm_streams: dict = {}
+
+
+def comm_stream(device):
+    """The library's communication stream on ``device`` (created once, default priority)."""
+    import torch
+
+    idx = torch.device(device).index
+    if idx is None:
+        idx = torch.cuda.current_device()
+    if idx not in _comm_streams:
+        _comm_streams[idx] = torch.cuda.Stream(device=idx)
+    return _comm_streams[idx]
+
+
+def _overlapped(device, tensors, launch, previous_event):
+    """Run ``launch`` on the communication stream after ``previous_event`` (default: all
+    work enqueued so far on the current stream); return an EventOverlap.  The tensors the
+    call reads or writes are marked as used on the communication stream, so that torch's
+    allocator does not hand their memory out again before that work is done."""
+    import torch
+
+    compute = torch.cuda.current_stream(device)
+    comm = comm_stream(device)
+    if previous_event is None:
+        previous_event = torch.cuda.Event()
+        previous_event.record(compute)
+    comm.wait_event(previous_event)
+    with torch.cuda.stream(comm):
+        result = launch()
+    for t in tensors:
+        if t is not None:
+            t.record_stream(comm)
+    done = torch.cuda.Event()
+    done.record(comm)
+    return EventOverlap(done, result)
+
+
 def get_layout(cfg: Config, topk_idx) -> Handle:
     """ep_get_layout: topk_idx int64 [T, K] on the device -> Handle (synchronizes once in exact
     mode; only enqueues with cfg.num_worst_rows > 0)."""
@@ -312,11 +366,15 @@ def _input(h: Handle, x):
 
 
 def dispatch(h: Handle, x, topk_weights, fp8: bool = False, zero_padding: bool = False,
-             scales_col_major: bool = False, out=None):
+             scales_col_major: bool = False, out=None, async_with_compute_stream: bool = False,
+             previous_event=None):
     """ep_dispatch (x bf16) or ep_dispatch_prequant (x = (codes, scales), output fp8)
     -> (recv_x, recv_scales | None, recv_weights, recv_src_meta).
 
-    out: optional preallocated (recv_x, recv_scales, recv_weights, recv_src_meta)."""
+    out: optional preallocated (recv_x, recv_scales, recv_weights, recv_src_meta).
+    async_with_compute_stream: run on the library's communication stream after
+    previous_event (default: the current stream's work so far) and return an EventOverlap
+    whose wait() gives the tuple; one such call per handle may be in flight at a time."""
     import torch
 
     cfg = h.cfg
@@ -330,33 +388,49 @@ def dispatch(h: Handle, x, topk_weights, fp8: bool = False, zero_padding: bool =
     else:
         recv_x, recv_scales, recv_w, recv_meta = out
     flags = _flags(fp8, zero_padding, scales_col_major)
-    if xs is None:
-        _check(lib().ep_dispatch(h.ptr, flags, _ptr(xin), _ptr(topk_weights), _ptr(recv_x), _ptr(recv_scales),
-                                 _ptr(recv_w), _ptr(recv_meta), _stream(device)))
-    else:
-        _check(lib().ep_dispatch_prequant(h.ptr, flags, _ptr(xin), _ptr(xs), _ptr(topk_weights), _ptr(recv_x),
-                                          _ptr(recv_scales), _ptr(recv_w), _ptr(recv_meta), _stream(device)))
-    return recv_x, recv_scales, recv_w, recv_meta
+
+    def launch():
+        if xs is None:
+            _check(lib().ep_dispatch(h.ptr, flags, _ptr(xin), _ptr(topk_weights), _ptr(recv_x), _ptr(recv_scales),
+                                     _ptr(recv_w), _ptr(recv_meta), _stream(device)))
+        else:
+            _check(lib().ep_dispatch_prequant(h.ptr, flags, _ptr(xin), _ptr(xs), _ptr(topk_weights), _ptr(recv_x),
+                                              _ptr(recv_scales), _ptr(recv_w), _ptr(recv_meta), _stream(device)))
+        return recv_x, recv_scales, recv_w, recv_meta
+
+    if not async_with_compute_stream:
+        return launch()
+    return _overlapped(device, [xin, xs, topk_weights, recv_x, recv_scales, recv_w, recv_meta], launch,
+                       previous_event)
 
 
 def dispatch_cached(h: Handle, x, fp8: bool = False, zero_padding: bool = False, scales_col_major: bool = False,
-                    out=None):
+                    out=None, async_with_compute_stream: bool = False, previous_event=None):
     """ep_dispatch_cached / ep_dispatch_prequant_cached -> (recv_x, recv_scales | None);
-    out: optional (recv_x, recv_scales)."""
+    out: optional (recv_x, recv_scales); async_with_compute_stream as in dispatch."""
     xin, xs, device = _input(h, x)
     fp8 = fp8 or xs is not None
     recv_x, recv_scales = _alloc_recv(h, fp8, device, scales_col_major) if out is None else out
     flags = _flags(fp8, zero_padding, scales_col_major)
-    if xs is None:
-        _check(lib().ep_dispatch_cached(h.ptr, flags, _ptr(xin), _ptr(recv_x), _ptr(recv_scales), _stream(device)))
-    else:
-        _check(lib().ep_dispatch_prequant_cached(h.ptr, flags, _ptr(xin), _ptr(xs), _ptr(recv_x),
-                                                 _ptr(recv_scales), _stream(device)))
-    return recv_x, recv_scales
+
+    def launch():
+        if xs is None:
+            _check(lib().ep_dispatch_cached(h.ptr, flags, _ptr(xin), _ptr(recv_x), _ptr(recv_scales),
+                                            _stream(device)))
+        else:
+            _check(lib().ep_dispatch_prequant_cached(h.ptr, flags, _ptr(xin), _ptr(xs), _ptr(recv_x),
+                                                     _ptr(recv_scales), _stream(device)))
+        return recv_x, recv_scales
+
+    if not async_with_compute_stream:
+        return launch()
+    return _overlapped(device, [xin, xs, recv_x, recv_scales], launch, previous_event)
 
 
-def combine(h: Handle, y, topk_weights=None, bias=None, out=None):
-    """ep_combine: y bf16 [total_rows, H] (+ optional bias bf16 [T, H]) -> out bf16 [T, H]."""
+def combine(h: Handle, y, topk_weights=None, bias=None, out=None, async_with_compute_stream: bool = False,
+            previous_event=None):
+    """ep_combine: y bf16 [total_rows, H] (+ optional bias bf16 [T, H]) -> out bf16 [T, H];
+    async_with_compute_stream as in dispatch (wait() gives out)."""
     import torch
 
     cfg = h.cfg
@@ -367,8 +441,14 @@ def combine(h: Handle, y, topk_weights=None, bias=None, out=None):
         _require(bias, torch.bfloat16, (cfg.T, cfg.H), "bias")
     if out is None:
         out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=y.device)
-    _check(lib().ep_combine(h.ptr, _ptr(y), _ptr(topk_weights), _ptr(bias), _ptr(out), _stream(y.device)))
-    return out
+
+    def launch():
+        _check(lib().ep_combine(h.ptr, _ptr(y), _ptr(topk_weights), _ptr(bias), _ptr(out), _stream(y.device)))
+        return out
+
+    if not async_with_compute_stream:
+        return launch()
+    return _overlapped(y.device, [y, topk_weights, bias, out], launch, previous_event)
 
 
 def debug_e4m3_encode(q):

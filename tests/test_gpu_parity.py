@@ -649,3 +649,52 @@ def test_variants_full_size():
     np.testing.assert_array_equal(got, exp)
     h.free()
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------
+# overlap API: calls on the communication stream, ordered by events
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("mode", ["exact", "fixed"])
+def test_async_with_compute_stream_matches_sync(fp8, mode):
+    """dispatch / cached dispatch / combine issued with async_with_compute_stream=True while a
+    matmul runs on the compute stream give the same bytes as the synchronous calls; the input
+    is produced on the compute stream right before the call, so the result also shows that the
+    communication stream waited for it."""
+    w = SMALL[1]
+    topk = routing_with_holes(w, 16)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    W = int(lay.num_expanded.max()) if mode == "fixed" else 0
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A, num_worst_rows=W), torch.from_numpy(topk).to(DEV))
+    x = synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    ref = ep.dispatch(h, xd, wd, fp8=fp8, zero_padding=True)
+    ref_c = ep.dispatch_cached(h, xd, fp8=fp8, zero_padding=True)
+    y = dev_bf16(synth.gen_expert_out(w, h.total_rows))
+    bias = dev_bf16(synth.gen_bf16_rows(w.seed, wl.STREAM_GRAD_OUT, w.T, w.H))
+    ref_out = ep.combine(h, y, wd, bias=bias)
+    torch.cuda.synchronize()
+    a = torch.randn((2048, 2048), device=DEV)
+    for it in range(3):
+        say("async", mode, "fp8" if fp8 else "bf16", "iteration", it)
+        x2 = xd * 1  # produced on the compute stream just before the call
+        pending = ep.dispatch(h, x2, wd, fp8=fp8, zero_padding=True, async_with_compute_stream=True)
+        busy = a @ a  # compute-stream work in between
+        got = pending.wait()
+        pc = ep.dispatch_cached(h, x2, fp8=fp8, zero_padding=True, async_with_compute_stream=True)
+        got_c = pc.wait()
+        po = ep.combine(h, y * 1, wd, bias=bias, async_with_compute_stream=True)
+        busy = busy @ a
+        out = po.wait()
+        torch.cuda.synchronize()
+        for r, g in zip(ref, got):
+            if r is not None:
+                assert torch.equal(r.view(torch.uint8), g.view(torch.uint8))
+        for r, g in zip(ref_c, got_c):
+            if r is not None:
+                assert torch.equal(r.view(torch.uint8), g.view(torch.uint8))
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    assert torch.isfinite(busy).any()
+    h.free()
