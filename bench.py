@@ -210,6 +210,49 @@ def fixed_leg(ep, h_exact, w, topk, topk_d, x_d, w_d, out, steps: int, warmup: i
 
 
 # ---------------------------------------------------------------------------
+# device ceilings
+# ---------------------------------------------------------------------------
+
+def device_ceilings(dev) -> dict:
+    """Context for the roofline: the HBM peak implied by the device properties (memory
+    clock x bus width, double data rate) and what a plain copy reaches on this machine
+    (torch copy_ of 1 GiB, read + write bytes over the kernel time)."""
+    import ctypes
+
+    import torch
+
+    out = {}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        clk, bus = ctypes.c_int(), ctypes.c_int()
+        # hipDeviceAttributeMemoryClockRate = 60 (kHz), hipDeviceAttributeMemoryBusWidth = 59 (bits)
+        if hip.hipDeviceGetAttribute(ctypes.byref(clk), 60, dev.index or 0) == 0 and \
+                hip.hipDeviceGetAttribute(ctypes.byref(bus), 59, dev.index or 0) == 0:
+            out["memory_clock_khz"] = clk.value
+            out["memory_bus_bits"] = bus.value
+            out["props_peak_GBps"] = 2.0 * clk.value * 1e3 * bus.value / 8 / 1e9
+    except OSError:
+        pass
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    out["copy_1GiB_GBps"] = 2.0 * n / (sorted(ts)[len(ts) // 2] * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
 # per-call table
 # ---------------------------------------------------------------------------
 
@@ -547,6 +590,8 @@ def main() -> int:
             "expanded_rows": R, "padding_rows": pad,
         },
     }
+
+    result["device"] = device_ceilings(dev)
 
     if not args.no_fixed:
         result["fixed_windows"] = fixed_leg(ep, h, w, topk, topk_d, x_d, w_d, out, args.steps, args.warmup)

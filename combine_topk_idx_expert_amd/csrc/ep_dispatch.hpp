@@ -291,21 +291,16 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
   }
 }
 
-// fp8 row scales: recv_scales[row][b] (or [b][row] column-major) = scale of the row's
-// source token (0 for padding rows with zero padding, otherwise untouched; 0
-// for the tail rows of fixed windows).
-__global__ __launch_bounds__(256) void dispatch_scales_kernel(DispatchArgs a) {
-  const int nblk = a.H >> 7;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t rows = a.cap > 0 ? (int64_t)a.P * a.cap : (int64_t)a.sum_expanded;
-  if (i >= rows * nblk) return;
-  // row-major output: consecutive threads walk a row's blocks; column-major:
-  // consecutive threads walk rows of one block, so either way stores coalesce
-  const int64_t pr = a.scales_cm ? i % rows : i / nblk;
-  const int b = (int)(a.scales_cm ? i / rows : i - pr * nblk);
-  int slot;
-  int64_t row;
-  bool tail = false;
+// fp8 row scales: recv_scales[row][b] (or [b][row] column-major) = scale of
+// the row's source token (0 for padding rows with zero padding, otherwise
+// untouched; 0 for the tail rows of fixed windows).
+// Row-major: one thread per (row, block), consecutive threads walk a row's
+// blocks.  Column-major: one thread per row, walking the blocks: each thread
+// reads its token's scales contiguously and, for every block, consecutive
+// threads store to consecutive rows.
+__device__ __forceinline__ void row_source(const DispatchArgs& a, int64_t pr, int& slot, int64_t& row,
+                                           bool& tail) {
+  tail = false;
   if (a.cap == 0) {
     slot = a.row_slot[pr];
     row = packed_to_row(a, pr);
@@ -316,11 +311,42 @@ __global__ __launch_bounds__(256) void dispatch_scales_kernel(DispatchArgs a) {
     tail = l >= a.num_expanded[r];
     slot = tail ? -1 : a.row_slot[a.packed_base[r] + l];
   }
-  float* dst = a.scales_cm ? a.recv_scales + (int64_t)b * a.scale_rows + row : a.recv_scales + row * nblk + b;
+}
+
+__global__ __launch_bounds__(256) void dispatch_scales_kernel(DispatchArgs a) {
+  const int nblk = a.H >> 7;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = a.cap > 0 ? (int64_t)a.P * a.cap : (int64_t)a.sum_expanded;
+  if (i >= rows * nblk) return;
+  const int64_t pr = i / nblk;
+  const int b = (int)(i - pr * nblk);
+  int slot;
+  int64_t row;
+  bool tail;
+  row_source(a, pr, slot, row, tail);
+  float* dst = a.recv_scales + row * nblk + b;
   if (slot >= 0)
     *dst = a.tok_scales[(int64_t)(slot / a.K) * nblk + b];
   else if (a.zero_pad || tail)
     *dst = 0.0f;
+}
+
+__global__ __launch_bounds__(256) void dispatch_scales_cm_kernel(DispatchArgs a) {
+  const int nblk = a.H >> 7;
+  const int64_t pr = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = a.cap > 0 ? (int64_t)a.P * a.cap : (int64_t)a.sum_expanded;
+  if (pr >= rows) return;
+  int slot;
+  int64_t row;
+  bool tail;
+  row_source(a, pr, slot, row, tail);
+  float* dst = a.recv_scales + row;
+  if (slot >= 0) {
+    const float* src = a.tok_scales + (int64_t)(slot / a.K) * nblk;
+    for (int b = 0; b < nblk; ++b) dst[(int64_t)b * a.scale_rows] = src[b];
+  } else if (a.zero_pad || tail) {
+    for (int b = 0; b < nblk; ++b) dst[(int64_t)b * a.scale_rows] = 0.0f;
+  }
 }
 
 // Test hook: the dispatch kernel's float -> E4M3 conversion applied to an
