@@ -184,7 +184,14 @@ ep_status allocate(ep_handle* h) {
   h->lds_count = (size_t)(d.ncols + kChunk * ((d.P + 31) / 32) + kChunk * d.K) * 4;
   h->lds_scan = (size_t)(((d.P + 1) & ~1) * 4 + (kScanThreads / 64) * 8);
   h->lds_finalize = (size_t)((d.E + 1) + ((d.E + 2) / 2) + 1 + kFinalizeThreads / 64) * 8 + (size_t)d.ncols * 4;
-  h->lds_rank = (size_t)((d.E + 1) + (d.P + 1) + 2 * kChunk * d.K) * 4;
+  h->lds_rank = (size_t)(kLayoutWaves * ((d.E + 1) + (d.P + 1)) + 2 * kChunk * d.K) * 4;
+  int lds_max = 0;
+  if (hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, h->device) != hipSuccess)
+    return fail(EP_ERR_HIP, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock) failed");
+  const size_t lds_need = std::max({h->lds_count, h->lds_scan, h->lds_finalize, h->lds_rank});
+  if (lds_need > (size_t)lds_max)
+    return fail(EP_ERR_SHAPE, "layout needs %zu bytes of LDS per workgroup, the device has %d (E=%d P=%d K=%d)",
+                lds_need, lds_max, d.E, d.P, d.K);
   return EP_OK;
 }
 
@@ -204,7 +211,7 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
   h->valid = false;
   const LayoutDims& d = h->dims;
   if (d.num_chunks > 0) {
-    layout_count_kernel<<<d.num_chunks, kWave, h->lds_count, s>>>(d, topk_idx, h->is_token_in_rank,
+    layout_count_kernel<<<d.num_chunks, kLayoutThreads, h->lds_count, s>>>(d, topk_idx, h->is_token_in_rank,
                                                                    h->chunk_hist);
     EP_LAUNCHED("layout_count_kernel");
   }
@@ -224,7 +231,7 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
     RankOut ro{h->dst_slot, h->dst_row, h->row_slot, h->send_head, h->recv_src_idx, h->pad_rows};
     RankIn ri{h->chunk_excl_t, h->n_e, h->pad_base, h->expert_offset, h->window_row_base, h->packed_base,
               h->recv_src_base};
-    layout_rank_kernel<<<std::max(d.num_chunks, 1), kWave, h->lds_rank, s>>>(d, topk_idx, ri, ro);
+    layout_rank_kernel<<<std::max(d.num_chunks, 1), kLayoutThreads, h->lds_rank, s>>>(d, topk_idx, ri, ro);
     EP_LAUNCHED("layout_rank_kernel");
   }
   EP_HIP(hipEventRecord(h->done, s));

@@ -8,25 +8,32 @@
 // (token, destination) pair.
 //
 // How (no global atomics, so the result is the same on every run):
-//  1. layout_count  -- one wave per chunk of 64 tokens of one source rank:
-//     expert and rank histograms of the chunk in LDS, is_token_in_rank rows.
+//  1. layout_count  -- one 4-wave workgroup per chunk of 64 tokens of one
+//     source rank: expert and rank histograms of the chunk in LDS (one thread
+//     per slot), is_token_in_rank rows.
 //  2. layout_scan   -- one workgroup per histogram column (E experts + P
 //     ranks): exclusive scan over chunks in order, per-source-rank sums.
 //  3. layout_finalize -- one workgroup: aligned expert sizes, window offsets,
 //     window bases, receive-list bases, padding-row list, host summary.
-//  4. layout_rank   -- one wave per chunk again: walks the chunk's (u, j)
-//     slots 64 at a time in memory order; lanes holding the same expert (or
-//     the same first-seen destination rank) are found with ballots, their
-//     order within the step is their lane order and a per-key running counter
-//     in LDS carries the order across steps.  Seeded with the chunk's scanned
-//     offsets this yields the global stable order by (u, j).
+//  4. layout_rank   -- one 4-wave workgroup per chunk again; wave w owns the
+//     chunk's tokens [16w, 16w + 16).  Each wave counts its slots per key
+//     (expert, first-seen destination rank); a prefix over the waves, seeded
+//     with the chunk's scanned offsets, gives every wave its starting
+//     position per key.  Each wave then walks its (u, j) slots 64 at a time
+//     in memory order; lanes holding the same key are found with ballots,
+//     their order within the step is their lane order, and the wave's
+//     running counter per key carries the order across steps.  This yields
+//     the global stable order by (u, j).
 #pragma once
 
 #include "ep_device.hpp"
 
 namespace ep {
 
-constexpr int kChunk = 64;  // tokens per layout chunk; one wave per chunk
+constexpr int kChunk = 64;          // tokens per layout chunk
+constexpr int kLayoutThreads = 256;  // workgroup of the count and rank kernels: 4 waves per chunk
+constexpr int kLayoutWaves = kLayoutThreads / kWave;
+constexpr int kTokensPerWave = kChunk / kLayoutWaves;
 
 struct LayoutDims {
   int P, S, E, K, A, El;
@@ -62,7 +69,7 @@ __device__ __forceinline__ void stage_chunk_experts(const LayoutDims& d, const C
                                                     int32_t* ex) {
   const int total = p.n * d.K;
   const int64_t* src = topk_idx + p.u0 * d.K;
-  for (int i = threadIdx.x; i < total; i += kWave) {
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
     const int64_t e = src[i];
     ex[i] = (e >= 0 && e < d.E) ? (int32_t)e : (e == -1 ? -1 : -2);
   }
@@ -97,39 +104,43 @@ __device__ __forceinline__ int64_t block_excl_scan(int64_t v, int64_t* wsum, int
 // --------------------------------------------------------------------------
 // LDS: hist[E + P + 1] | rank bit masks [64][ceil(P/32)] | staged experts [64*K]
 // Column E + P counts out-of-range expert ids (a routing error).
-__global__ __launch_bounds__(64) void layout_count_kernel(LayoutDims d,
-                                                          const int64_t* __restrict__ topk_idx,
-                                                          uint8_t* __restrict__ is_token_in_rank,
-                                                          int32_t* __restrict__ chunk_hist) {
+// A slot is its token's first on rank r if no earlier slot of the token maps
+// to r; that test only reads the staged row, so every slot is one thread.
+__device__ __forceinline__ bool first_on_rank(const LayoutDims& d, const int32_t* ex, int t, int j, int r) {
+  for (int jj = 0; jj < j; ++jj) {
+    const int e2 = ex[t * d.K + jj];
+    if (e2 >= 0 && e2 / d.El == r) return false;
+  }
+  return true;
+}
+
+__global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(LayoutDims d,
+                                                                      const int64_t* __restrict__ topk_idx,
+                                                                      uint8_t* __restrict__ is_token_in_rank,
+                                                                      int32_t* __restrict__ chunk_hist) {
   extern __shared__ int32_t lds[];
   const int words = (d.P + 31) >> 5;
   int32_t* hist = lds;
   uint32_t* rmask = (uint32_t*)(lds + d.ncols);
   int32_t* ex = lds + d.ncols + kChunk * words;
   const ChunkPos p = chunk_pos(d);
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
 
-  for (int i = lane; i < d.ncols; i += kWave) hist[i] = 0;
-  for (int i = lane; i < kChunk * words; i += kWave) rmask[i] = 0;
+  for (int i = tid; i < d.ncols; i += kLayoutThreads) hist[i] = 0;
+  for (int i = tid; i < kChunk * words; i += kLayoutThreads) rmask[i] = 0;
   stage_chunk_experts(d, p, topk_idx, ex);
   __syncthreads();
 
-  if (lane < p.n) {
-    uint32_t* my = rmask + lane * words;
-    int bad = 0;
-    for (int j = 0; j < d.K; ++j) {
-      const int e = ex[lane * d.K + j];
-      bad += (e == -2);
-      if (e < 0) continue;
-      const int r = e / d.El;
-      atomicAdd(&hist[e], 1);
-      const uint32_t bit = 1u << (r & 31);
-      if (!(my[r >> 5] & bit)) {  // first slot of this token on rank r
-        my[r >> 5] |= bit;
-        atomicAdd(&hist[d.E + r], 1);
-      }
+  for (int i = tid; i < p.n * d.K; i += kLayoutThreads) {
+    const int e = ex[i];
+    if (e == -2) atomicAdd(&hist[d.E + d.P], 1);
+    if (e < 0) continue;
+    const int t = i / d.K, j = i - t * d.K, r = e / d.El;
+    atomicAdd(&hist[e], 1);
+    if (first_on_rank(d, ex, t, j, r)) {
+      atomicAdd(&hist[d.E + r], 1);
+      atomicOr(&rmask[t * words + (r >> 5)], 1u << (r & 31));
     }
-    if (bad) atomicAdd(&hist[d.E + d.P], bad);
   }
   __syncthreads();
 
@@ -138,7 +149,7 @@ __global__ __launch_bounds__(64) void layout_count_kernel(LayoutDims d,
   const int nbytes = p.n * d.P;
   if ((d.P & 3) == 0) {
     uint32_t* itr4 = (uint32_t*)itr;  // u0 * P is a multiple of 4
-    for (int wi = lane; wi < (nbytes >> 2); wi += kWave) {
+    for (int wi = tid; wi < (nbytes >> 2); wi += kLayoutThreads) {
       const int t = (wi << 2) / d.P, r0 = (wi << 2) - t * d.P;
       const uint32_t* m = rmask + t * words;
       uint32_t v = 0;
@@ -147,12 +158,12 @@ __global__ __launch_bounds__(64) void layout_count_kernel(LayoutDims d,
       itr4[wi] = v;
     }
   } else {
-    for (int bi = lane; bi < nbytes; bi += kWave) {
+    for (int bi = tid; bi < nbytes; bi += kLayoutThreads) {
       const int t = bi / d.P, r = bi - t * d.P;
       itr[bi] = (uint8_t)((rmask[t * words + (r >> 5)] >> (r & 31)) & 1u);
     }
   }
-  for (int col = lane; col < d.ncols; col += kWave)
+  for (int col = tid; col < d.ncols; col += kLayoutThreads)
     chunk_hist[(int64_t)col * d.num_chunks + p.c] = hist[col];
 }
 
@@ -413,15 +424,17 @@ struct RankIn {
 
 // Also writes the padding rows of experts blockIdx.x, blockIdx.x + grid, ...:
 // pad_rows (global row) and row_slot = -1.
-// LDS: cnt_e[E+1] | cnt_r[P+1] | staged experts [64*K] | send positions [64*K]
-__global__ __launch_bounds__(64) void layout_rank_kernel(LayoutDims d, const int64_t* __restrict__ topk_idx,
-                                                         RankIn in, RankOut o) {
+// LDS: per-wave counters cnt_e[W][E+1] | cnt_r[W][P+1] | staged experts [64*K] |
+//      send positions [64*K]
+__global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(LayoutDims d,
+                                                                     const int64_t* __restrict__ topk_idx,
+                                                                     RankIn in, RankOut o) {
   extern __shared__ int32_t lds[];
-  int32_t* cnt_e = lds;
-  int32_t* cnt_r = lds + d.E + 1;
-  int32_t* ex = cnt_r + d.P + 1;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
+  int32_t* cnt_e_all = lds;                                   // [W][E+1]
+  int32_t* cnt_r_all = cnt_e_all + kLayoutWaves * (d.E + 1);  // [W][P+1]
+  int32_t* ex = cnt_r_all + kLayoutWaves * (d.P + 1);
   int32_t* pos = ex + kChunk * d.K;
-  const int lane = threadIdx.x;
   const int64_t* __restrict__ expert_offset = in.expert_offset;
   const int64_t* __restrict__ window_row_base = in.window_row_base;
   const int64_t* __restrict__ packed_base = in.packed_base;
@@ -429,30 +442,55 @@ __global__ __launch_bounds__(64) void layout_rank_kernel(LayoutDims d, const int
 
   if (blockIdx.x < d.num_chunks) {  // token part: one chunk per workgroup
     const ChunkPos p = chunk_pos(d);
-    const int32_t* my_excl = in.chunk_excl_t + (int64_t)p.c * d.ncols;
-    for (int i = lane; i < d.E; i += kWave) cnt_e[i] = my_excl[i];
-    for (int i = lane; i < d.P; i += kWave) cnt_r[i] = my_excl[d.E + i];
-    if (lane == 0) {
-      cnt_e[d.E] = 0;
-      cnt_r[d.P] = 0;
-    }
+    for (int i = tid; i < kLayoutWaves * (d.E + 1); i += kLayoutThreads) cnt_e_all[i] = 0;
+    for (int i = tid; i < kLayoutWaves * (d.P + 1); i += kLayoutThreads) cnt_r_all[i] = 0;
     stage_chunk_experts(d, p, topk_idx, ex);
     __syncthreads();
 
-    const int total = p.n * d.K;
-    for (int base = 0; base < total; base += kWave) {  // uniform trip count
+    // this wave's slots: tokens [t0, t0 + nt) of the chunk
+    const int t0 = wv * kTokensPerWave;
+    const int nt = max(0, min(kTokensPerWave, p.n - t0));
+    const int first_slot = t0 * d.K, total = nt * d.K;
+    int32_t* cnt_e = cnt_e_all + wv * (d.E + 1);
+    int32_t* cnt_r = cnt_r_all + wv * (d.P + 1);
+
+    // 1. per-wave counts per key
+    for (int i = lane; i < total; i += kWave) {
+      const int s = first_slot + i;
+      const int e = ex[s];
+      if (e < 0) continue;
+      const int t = s / d.K, j = s - t * d.K, r = e / d.El;
+      atomicAdd(&cnt_e[e], 1);
+      if (first_on_rank(d, ex, t, j, r)) atomicAdd(&cnt_r[r], 1);
+    }
+    __syncthreads();
+
+    // 2. starting position of every wave per key: the chunk's scanned offset
+    //    plus the counts of the earlier waves
+    const int32_t* my_excl = in.chunk_excl_t + (int64_t)p.c * d.ncols;
+    for (int k = tid; k < d.E + d.P; k += kLayoutThreads) {
+      const bool is_e = k < d.E;
+      int32_t* c = is_e ? cnt_e_all + k : cnt_r_all + (k - d.E);
+      const int stride = is_e ? d.E + 1 : d.P + 1;
+      int32_t run = my_excl[k];
+#pragma unroll
+      for (int w = 0; w < kLayoutWaves; ++w) {
+        const int32_t n = c[w * stride];
+        c[w * stride] = run;
+        run += n;
+      }
+    }
+    __syncthreads();
+
+    // 3. stable ranks inside the wave
+    for (int base = 0; base < total; base += kWave) {  // uniform trip count per wave
       const int i = base + lane;
       const bool live = i < total;
-      const int e = live ? ex[i] : -1;
-      const int t = i / d.K, j = i - t * d.K;
+      const int s = first_slot + i;
+      const int e = live ? ex[s] : -1;
+      const int t = s / d.K, j = s - t * d.K;
       const int r = e >= 0 ? e / d.El : d.P;
-      bool first = e >= 0;  // first slot of token t on rank r
-      if (e >= 0) {         // (only lanes holding a slot read the token's earlier slots)
-        for (int jj = 0; jj < j; ++jj) {
-          const int e2 = ex[t * d.K + jj];
-          first &= !(e2 >= 0 && e2 / d.El == r);
-        }
-      }
+      const bool first = e >= 0 && first_on_rank(d, ex, t, j, r);
       const uint32_t key_e = e >= 0 ? (uint32_t)e : (uint32_t)d.E;
       const uint32_t key_r = first ? (uint32_t)r : (uint32_t)d.P;
       const uint64_t pe = match_any(key_e, d.ebits);
@@ -479,14 +517,14 @@ __global__ __launch_bounds__(64) void layout_rank_kernel(LayoutDims d, const int
           sh = br + count_below(pr);
           o.recv_src_idx[recv_src_base[r] + sh] = p.t0 + t;
         }
-        pos[i] = sh;
+        pos[s] = sh;
       }
     }
     __syncthreads();
 
     // send_head rows of the chunk: one contiguous int32 range, -1 where not sent
     int32_t* out = o.send_head + p.u0 * d.P;
-    for (int q = lane; q < p.n * d.P; q += kWave) {
+    for (int q = tid; q < p.n * d.P; q += kLayoutThreads) {
       const int t = q / d.P, r = q - t * d.P;
       int32_t v = -1;
       for (int j = 0; j < d.K; ++j) {
@@ -504,7 +542,7 @@ __global__ __launch_bounds__(64) void layout_rank_kernel(LayoutDims d, const int
     const int n = in.n_e[e];
     const int b0 = in.pad_base[e], npad = in.pad_base[e + 1] - b0;
     const int64_t local = expert_offset[(int64_t)r * (d.El + 1) + l] + n;
-    for (int i = lane; i < npad; i += kWave) {
+    for (int i = tid; i < npad; i += kLayoutThreads) {
       o.pad_rows[b0 + i] = (int32_t)(window_row_base[r] + local + i);
       o.row_slot[packed_base[r] + local + i] = -1;
     }
