@@ -182,7 +182,7 @@ ep_status allocate(ep_handle* h) {
   if (e != hipSuccess) return fail(EP_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
 
   h->lds_count = (size_t)(d.ncols + kChunk * ((d.P + 31) / 32) + kChunk * d.K) * 4;
-  h->lds_scan = (size_t)(((d.P + 1) & ~1) * 4 + (kScanThreads / 64) * 8);
+  h->lds_scan = (size_t)(((d.P + 2) & ~1) * 4 + (kScanThreads / 64) * 8);
   h->lds_finalize = (size_t)((d.E + 1) + ((d.E + 2) / 2) + 1 + kFinalizeThreads / 64) * 8 + (size_t)d.ncols * 4;
   h->lds_rank = (size_t)(kLayoutWaves * ((d.E + 1) + (d.P + 1)) + 2 * kChunk * d.K) * 4;
   int lds_max = 0;

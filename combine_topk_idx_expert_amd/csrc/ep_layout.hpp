@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(LayoutDims
 // chunk_hist[col][chunk].  Per-source-rank sums give
 // num_tokens_per_expert[s][e], num_tokens_per_rank[s][d] and
 // rank_prefix_matrix[s][d] (inclusive over s).
-// LDS: rank_sum[P] | wave sums (int64) [4]
+// LDS: rank_start[P+1] | wave sums (int64) [4]
 constexpr int kScanThreads = 256;
 
 // chunk_excl_t[chunk][col] receives the same offsets chunk-major, so that the
@@ -184,14 +184,14 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
     int32_t* __restrict__ col_total, int32_t* __restrict__ num_tokens_per_expert,
     int32_t* __restrict__ num_tokens_per_rank, int32_t* __restrict__ rank_prefix_matrix) {
   extern __shared__ int32_t lds[];
-  int32_t* rank_sum = lds;
-  int64_t* wsum = (int64_t*)(lds + ((d.P + 1) & ~1));
+  int32_t* rank_start = lds;  // [P+1]: the column's prefix at each source rank's first chunk
+  int64_t* wsum = (int64_t*)(lds + ((d.P + 2) & ~1));
   const int col = blockIdx.x;
   const int tid = threadIdx.x;
   const int nc = d.num_chunks;
   int32_t* v = chunk_hist + (int64_t)col * nc;
 
-  for (int i = tid; i < d.P; i += kScanThreads) rank_sum[i] = 0;
+  for (int i = tid; i <= d.P; i += kScanThreads) rank_start[i] = 0;
   __syncthreads();
 
   int64_t carry = 0;
@@ -203,30 +203,37 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
       const int i = base + tid * 4 + q;
       x[q] = i < nc ? v[i] : 0;
       tsum += x[q];
-      if (i < nc && x[q] != 0) atomicAdd(&rank_sum[i / d.cpr], x[q]);
     }
     int64_t tile_total;
     int64_t run = carry + block_excl_scan<kScanThreads>(tsum, wsum, &tile_total);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = base + tid * 4 + q;
-      if (i < nc) chunk_excl_t[(int64_t)i * d.ncols + col] = (int32_t)run;
+      if (i < nc) {
+        chunk_excl_t[(int64_t)i * d.ncols + col] = (int32_t)run;
+        if (i % d.cpr == 0) rank_start[i / d.cpr] = (int32_t)run;  // chunks of a rank are consecutive
+      }
       run += x[q];
     }
     carry += tile_total;
   }
-  if (tid == 0) col_total[col] = (int32_t)carry;
+  if (tid == 0) {
+    col_total[col] = (int32_t)carry;
+    rank_start[d.P] = (int32_t)carry;
+  }
   __syncthreads();
+  // per-source-rank sums of the column
+  const auto rank_sum = [&](int s) { return rank_start[s + 1] - rank_start[s]; };
 
   if (col < d.E) {
     for (int s = tid; s < d.P; s += kScanThreads)
-      num_tokens_per_expert[(int64_t)s * d.E + col] = rank_sum[s];
+      num_tokens_per_expert[(int64_t)s * d.E + col] = rank_sum(s);
   } else if (col < d.E + d.P) {
     const int r = col - d.E;
     int64_t run = 0;
     for (int base = 0; base < d.P; base += kScanThreads) {
       const int s = base + tid;
-      const int64_t val = s < d.P ? rank_sum[s] : 0;
+      const int64_t val = s < d.P ? rank_sum(s) : 0;
       int64_t tile_total;
       const int64_t excl = run + block_excl_scan<kScanThreads>(val, wsum, &tile_total);
       if (s < d.P) {
@@ -522,16 +529,15 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(LayoutDims 
     }
     __syncthreads();
 
-    // send_head rows of the chunk: one contiguous int32 range, -1 where not sent
+    // send_head rows of the chunk: one contiguous int32 range, -1 where not
+    // sent; then each token's first slot on a rank writes its position (the
+    // barrier orders the two writes of the same element)
     int32_t* out = o.send_head + p.u0 * d.P;
-    for (int q = tid; q < p.n * d.P; q += kLayoutThreads) {
-      const int t = q / d.P, r = q - t * d.P;
-      int32_t v = -1;
-      for (int j = 0; j < d.K; ++j) {
-        const int e = ex[t * d.K + j];
-        if (e >= 0 && e / d.El == r && pos[t * d.K + j] >= 0) v = pos[t * d.K + j];
-      }
-      out[q] = v;
+    for (int q = tid; q < p.n * d.P; q += kLayoutThreads) out[q] = -1;
+    __syncthreads();
+    for (int i = tid; i < p.n * d.K; i += kLayoutThreads) {
+      const int sh = pos[i];
+      if (sh >= 0) out[(i / d.K) * d.P + ex[i] / d.El] = sh;
     }
   }
 
