@@ -698,3 +698,42 @@ def test_async_with_compute_stream_matches_sync(fp8, mode):
         assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
     assert torch.isfinite(busy).any()
     h.free()
+
+
+# --------------------------------------------------------------------------
+# the build's limits
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S,A", [(4, 1), (1, 8)])
+def test_maximum_ranks_experts_topk(S, A):
+    """1024 ranks, 4096 experts and top-32 at once (EP_MAX_RANKS, EP_MAX_EXPERTS, EP_MAX_TOPK),
+    with unused slots and duplicate experts: layout, fresh dispatch and combine against the
+    oracle.  A device whose workgroups cannot hold the rank kernel's LDS gets EP_ERR_SHAPE."""
+    w = wl.Workload(f"max-p1024-s{S}-e4096-k32", 1024, S, 4096, 32, 128, A, True, "uniform", seed=21)
+    topk = routing_with_holes(w, 17)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    say("maximum config", w.name)
+    try:
+        h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A), torch.from_numpy(topk).to(DEV))
+    except ep.EpError as err:
+        assert err.status == ep.Status.ERR_SHAPE and "LDS" in str(err)
+        pytest.skip(f"device LDS per workgroup too small for this config: {err}")
+    torch.cuda.synchronize()
+    check_layout(lay, h)
+    x = synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    for fp8 in (False, True):
+        rx, sc, rw, rm = ep.dispatch(h, xd, wd, fp8=fp8, zero_padding=True)
+        torch.cuda.synchronize()
+        ox, osc, ow, om = oracle.dispatch(lay, w.H, x, wt, fp8, True)
+        np.testing.assert_array_equal(rx.cpu().numpy() if fp8 else host_u16(rx), ox)
+        np.testing.assert_array_equal(rm.cpu().numpy(), om)
+        np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+        if fp8:
+            np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    y = synth.gen_expert_out(w, h.total_rows)
+    out = ep.combine(h, dev_bf16(y), wd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_u16(out), oracle.combine(lay, w.H, y, wt))
+    h.free()
