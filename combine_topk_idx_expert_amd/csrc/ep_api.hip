@@ -294,7 +294,10 @@ ep_status check_handle(const ep_handle* h) {
 #define EP_DISPATCH_NC_FP8 1
 #endif
 #ifndef EP_ROW_BLOCK_WAVES
-#define EP_ROW_BLOCK_WAVES 4  // waves per workgroup of the row kernels
+#define EP_ROW_BLOCK_WAVES 4  // waves per workgroup of the dispatch kernel
+#endif
+#ifndef EP_COMBINE_BLOCK_WAVES
+#define EP_COMBINE_BLOCK_WAVES 16  // waves per workgroup of the register combine kernel (1 and 16 measured ~1.5% faster than 4 and 8)
 #endif
 #ifndef EP_DISPATCH_LDS_BYTES
 #define EP_DISPATCH_LDS_BYTES 0
@@ -526,8 +529,8 @@ ep_status ep_combine(const ep_handle* h, const void* y, const float* topk_weight
                 (int)h->T, h->dims.K, h->cfg.hidden, parts_per_row(h->cfg.hidden, nct)};
   const int64_t waves = h->T * a.split;
   if (waves >= ((int64_t)1 << 31) / kWave) return fail(EP_ERR_OVERFLOW, "combine grid too large (%lld waves)", (long long)waves);
-  const int threads = EP_ROW_BLOCK_WAVES * kWave;
-  const int blocks = (int)((waves + EP_ROW_BLOCK_WAVES - 1) / EP_ROW_BLOCK_WAVES);
+  const int threads = EP_COMBINE_BLOCK_WAVES * kWave;
+  const int blocks = (int)((waves + EP_COMBINE_BLOCK_WAVES - 1) / EP_COMBINE_BLOCK_WAVES);
   hipStream_t s = (hipStream_t)stream;
   switch (nct) {
     case 1: combine_kernel<1, EP_COMBINE_G><<<blocks, threads, 0, s>>>(a); break;
