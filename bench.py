@@ -43,9 +43,11 @@ if ROOT not in sys.path:
 METRIC = "dispatch & combine payload GB/s + tokens/s on 1 MI355X; % HBM roofline"
 DEFAULT_WORKLOAD = "dsv3-bf16-p8-s4096-e256-k8-h7168"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+# the dispatch / combine kernels and their launch configuration: a committed counter
+# summary counts only while these are unchanged
 KERNEL_SOURCES = ["combine_topk_idx_expert_amd/csrc/ep_dispatch.hpp",
                   "combine_topk_idx_expert_amd/csrc/ep_device.hpp",
-                  "combine_topk_idx_expert_amd/csrc/ep_api.hip"]
+                  "combine_topk_idx_expert_amd/csrc/ep_launch.hpp"]
 
 
 def log(*a):
@@ -214,12 +216,15 @@ def fixed_leg(ep, h_exact, w, topk, topk_d, x_d, w_d, out, steps: int, warmup: i
 # ---------------------------------------------------------------------------
 
 def device_ceilings(dev) -> dict:
-    """Context for the roofline: the HBM peak implied by the device properties (memory
-    clock x bus width, double data rate) and what a plain copy reaches on this machine
-    (torch copy_ of 1 GiB, read + write bytes over the kernel time)."""
+    """Context for the roofline: the memory clock and bus width the device reports,
+    and what a plain streaming copy reaches on this machine (the library's calibration copy,
+    one wave per KiB with 16-byte nontemporal accesses like the row kernels; read +
+    write bytes over the kernel time, median of 5 copies of 2 GiB)."""
     import ctypes
 
     import torch
+
+    import combine_topk_idx_expert_amd as ep
 
     out = {}
     try:
@@ -230,23 +235,22 @@ def device_ceilings(dev) -> dict:
                 hip.hipDeviceGetAttribute(ctypes.byref(bus), 59, dev.index or 0) == 0:
             out["memory_clock_khz"] = clk.value
             out["memory_bus_bits"] = bus.value
-            out["props_peak_GBps"] = 2.0 * clk.value * 1e3 * bus.value / 8 / 1e9
     except OSError:
         pass
-    n = 1 << 30
+    n = 2 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty(n, dtype=torch.uint8, device=dev)
-    b.copy_(a)
+    ep.debug_copy(b, a)
     torch.cuda.synchronize()
     ts = []
     for _ in range(5):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        b.copy_(a)
+        ep.debug_copy(b, a)
         e1.record()
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
-    out["copy_1GiB_GBps"] = 2.0 * n / (sorted(ts)[len(ts) // 2] * 1e-3) / 1e9
+    out["copy_2GiB_GBps"] = 2.0 * n / (sorted(ts)[len(ts) // 2] * 1e-3) / 1e9
     del a, b
     torch.cuda.empty_cache()
     return out

@@ -30,6 +30,7 @@ from ._native import (  # noqa: F401
     TENSORS,
     combine,
     comm_stream,
+    debug_copy,
     debug_e4m3_encode,
     dispatch,
     dispatch_cached,

@@ -140,6 +140,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, fn).restype = i32
         L.ep_debug_e4m3_encode.argtypes = [vp, vp, i64, vp]
         L.ep_debug_e4m3_encode.restype = i32
+        L.ep_debug_copy.argtypes = [vp, vp, i64, vp]
+        L.ep_debug_copy.restype = i32
         L.ep_last_error.argtypes = []
         L.ep_last_error.restype = ctypes.c_char_p
         L.ep_abi_version.argtypes = []
@@ -390,12 +392,14 @@ def dispatch(h: Handle, x, topk_weights, fp8: bool = False, zero_padding: bool =
     flags = _flags(fp8, zero_padding, scales_col_major)
 
     def launch():
-        if xs is None:
-            _check(lib().ep_dispatch(h.ptr, flags, _ptr(xin), _ptr(topk_weights), _ptr(recv_x), _ptr(recv_scales),
-                                     _ptr(recv_w), _ptr(recv_meta), _stream(device)))
-        else:
-            _check(lib().ep_dispatch_prequant(h.ptr, flags, _ptr(xin), _ptr(xs), _ptr(topk_weights), _ptr(recv_x),
-                                              _ptr(recv_scales), _ptr(recv_w), _ptr(recv_meta), _stream(device)))
+        with torch.cuda.device(device):
+            if xs is None:
+                _check(lib().ep_dispatch(h.ptr, flags, _ptr(xin), _ptr(topk_weights), _ptr(recv_x),
+                                         _ptr(recv_scales), _ptr(recv_w), _ptr(recv_meta), _stream(device)))
+            else:
+                _check(lib().ep_dispatch_prequant(h.ptr, flags, _ptr(xin), _ptr(xs), _ptr(topk_weights),
+                                                  _ptr(recv_x), _ptr(recv_scales), _ptr(recv_w), _ptr(recv_meta),
+                                                  _stream(device)))
         return recv_x, recv_scales, recv_w, recv_meta
 
     if not async_with_compute_stream:
@@ -408,18 +412,21 @@ def dispatch_cached(h: Handle, x, fp8: bool = False, zero_padding: bool = False,
                     out=None, async_with_compute_stream: bool = False, previous_event=None):
     """ep_dispatch_cached / ep_dispatch_prequant_cached -> (recv_x, recv_scales | None);
     out: optional (recv_x, recv_scales); async_with_compute_stream as in dispatch."""
+    import torch
+
     xin, xs, device = _input(h, x)
     fp8 = fp8 or xs is not None
     recv_x, recv_scales = _alloc_recv(h, fp8, device, scales_col_major) if out is None else out
     flags = _flags(fp8, zero_padding, scales_col_major)
 
     def launch():
-        if xs is None:
-            _check(lib().ep_dispatch_cached(h.ptr, flags, _ptr(xin), _ptr(recv_x), _ptr(recv_scales),
-                                            _stream(device)))
-        else:
-            _check(lib().ep_dispatch_prequant_cached(h.ptr, flags, _ptr(xin), _ptr(xs), _ptr(recv_x),
-                                                     _ptr(recv_scales), _stream(device)))
+        with torch.cuda.device(device):
+            if xs is None:
+                _check(lib().ep_dispatch_cached(h.ptr, flags, _ptr(xin), _ptr(recv_x), _ptr(recv_scales),
+                                                _stream(device)))
+            else:
+                _check(lib().ep_dispatch_prequant_cached(h.ptr, flags, _ptr(xin), _ptr(xs), _ptr(recv_x),
+                                                         _ptr(recv_scales), _stream(device)))
         return recv_x, recv_scales
 
     if not async_with_compute_stream:
@@ -443,7 +450,8 @@ def combine(h: Handle, y, topk_weights=None, bias=None, out=None, async_with_com
         out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=y.device)
 
     def launch():
-        _check(lib().ep_combine(h.ptr, _ptr(y), _ptr(topk_weights), _ptr(bias), _ptr(out), _stream(y.device)))
+        with torch.cuda.device(y.device):
+            _check(lib().ep_combine(h.ptr, _ptr(y), _ptr(topk_weights), _ptr(bias), _ptr(out), _stream(y.device)))
         return out
 
     if not async_with_compute_stream:
@@ -460,3 +468,13 @@ def debug_e4m3_encode(q):
     out = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
     _check(lib().ep_debug_e4m3_encode(_ptr(q), _ptr(out), q.numel(), _stream(q.device)))
     return out
+
+
+def debug_copy(dst, src):
+    """Calibration copy (ep_debug_copy) of src into dst: same-size contiguous device tensors,
+    byte size a multiple of 1024."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n or not (src.is_cuda and dst.is_cuda):
+        raise ValueError("dst and src must be device tensors of the same byte size")
+    _check(lib().ep_debug_copy(_ptr(dst), _ptr(src), n, _stream(src.device)))
+    return dst

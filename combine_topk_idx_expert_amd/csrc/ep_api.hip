@@ -277,97 +277,40 @@ ep_status ensure_counts(const ep_handle* hc) {
   return EP_OK;
 }
 
+// Plain streaming copy for calibration: one wave per KiB, one nontemporal
+// 16-byte load and store per lane (the access unit of the row kernels).
+__global__ __launch_bounds__(256) void copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                   int64_t waves) {
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= waves) return;
+  const int64_t i = w * kWave + (threadIdx.x & 63);
+  __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 ep_status check_handle(const ep_handle* h) {
   if (!h) return fail(EP_ERR_NULL, "handle is NULL");
   if (!h->valid) return fail(EP_ERR_HANDLE_MISMATCH, "handle holds no valid layout");
   return EP_OK;
 }
 
-// Column part per wave, in 16-byte chunks per lane (tunable at build time;
-// the defaults are the fastest of sweeps on MI355X at hidden 7168 and 4096:
-// dispatch 1 KiB of bf16 input per wave for bf16 and fp8 output, combine
-// 1 KiB per wave with all K <= 8 row loads in flight).
-#ifndef EP_DISPATCH_NC_BF16
-#define EP_DISPATCH_NC_BF16 1
-#endif
-#ifndef EP_DISPATCH_NC_FP8
-#define EP_DISPATCH_NC_FP8 1
-#endif
-#ifndef EP_ROW_BLOCK_WAVES
-#define EP_ROW_BLOCK_WAVES 4  // waves per workgroup of the dispatch kernel
-#endif
-#ifndef EP_COMBINE_BLOCK_WAVES
-#define EP_COMBINE_BLOCK_WAVES 16  // waves per workgroup of the register combine kernel (1 and 16 measured ~1.5% faster than 4 and 8)
-#endif
-#ifndef EP_DISPATCH_LDS_BYTES
-#define EP_DISPATCH_LDS_BYTES 0
-#endif
-#ifndef EP_COMBINE_NCT
-#define EP_COMBINE_NCT 1
-#endif
-#ifndef EP_COMBINE_G
-#define EP_COMBINE_G 8
-#endif
-
-// Column part per wave (16-byte chunks per lane) of the dispatch kernels: a
-// build-time choice, NC KiB of bf16 input per wave.
-constexpr int kNcBf16 = EP_DISPATCH_NC_BF16;
-constexpr int kNcFp8 = EP_DISPATCH_NC_FP8;
-
-// Largest instantiated chunk count <= want that the row still needs (combine).
-int pick_nc(int H, int want) {
-  const int need = ((H >> 3) + kWave - 1) / kWave;  // chunks per lane for the whole row
-  const int nc = std::min(want, need);
-  return nc >= 14 ? 14 : nc >= 8 ? 8 : nc >= 7 ? 7 : nc >= 4 ? 4 : nc >= 2 ? 2 : 1;
-}
-
-int parts_per_row(int H, int nc) { return ((H >> 3) + nc * kWave - 1) / (nc * kWave); }
-
-// Fixed windows: waves that stride over the padding and tail rows (whole rows),
-// whose number only the device knows (at most P * cap rows).
-constexpr int64_t kZeroWaves = 16384;
-
-template <bool FP8, bool META, bool PREQ, bool FIXED>
-ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
-  constexpr int nc = FP8 ? kNcFp8 : kNcBf16;
-  a.split = parts_per_row(a.H, nc);
-  const int64_t out_rows = FIXED ? (int64_t)a.P * a.cap : (int64_t)a.sum_expanded;
-  const int64_t meta_items = META ? (out_rows + kWave - 1) / kWave : 0;
-  a.zero_waves = FIXED ? (int)std::min<int64_t>((int64_t)a.P * a.cap, kZeroWaves) : 0;
-  const int64_t zero_items = FIXED ? a.zero_waves : (a.zero_pad ? (int64_t)a.total_pad * a.split : 0);
-  const int64_t waves = (int64_t)a.T * a.split + zero_items + meta_items;
-  if (waves >= ((int64_t)1 << 31) / kWave) return fail(EP_ERR_OVERFLOW, "dispatch grid too large (%lld waves)", (long long)waves);
-  if (waves > 0) {
-    const int threads = EP_ROW_BLOCK_WAVES * kWave;
-    const int blocks = (int)((waves + EP_ROW_BLOCK_WAVES - 1) / EP_ROW_BLOCK_WAVES);
-    const size_t lds = EP_DISPATCH_LDS_BYTES;  // > 0 caps workgroups per CU (occupancy)
-    dispatch_kernel<nc, FP8, META, PREQ, FIXED><<<blocks, threads, lds, s>>>(a);
-    EP_LAUNCHED("dispatch_kernel");
-  }
-  if constexpr (FP8) {
-    const int64_t n = a.scales_cm ? out_rows : out_rows * (a.H >> 7);  // threads
-    if (n > 0) {
-      if (n >= ((int64_t)1 << 31)) return fail(EP_ERR_OVERFLOW, "scale grid too large");
-      if (a.scales_cm)
-        dispatch_scales_cm_kernel<<<(int)((n + 255) / 256), 256, 0, s>>>(a);
-      else
-        dispatch_scales_kernel<<<(int)((n + 255) / 256), 256, 0, s>>>(a);
-      EP_LAUNCHED("dispatch_scales_kernel");
-    }
-  }
+// Calls that launch work must run with the handle's device current: its
+// arrays live there, and kernels go to the current device.
+ep_status check_device(const ep_handle* h) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(EP_ERR_HIP, "hipGetDevice failed");
+  if (cur != h->device)
+    return fail(EP_ERR_HANDLE_MISMATCH, "handle lives on device %d, the current device is %d", h->device, cur);
   return EP_OK;
 }
 
-template <bool FP8, bool META, bool PREQ>
-ep_status launch_dispatch_mode(const DispatchArgs& a, hipStream_t s) {
-  return a.cap > 0 ? launch_dispatch<FP8, META, PREQ, true>(a, s) : launch_dispatch<FP8, META, PREQ, false>(a, s);
-}
+#include "ep_launch.hpp"
 
 // x: bf16 [T][H]; or, with prequant, E4M3 codes [T][H] and x_scales [T][H/128].
 ep_status dispatch_common(const ep_handle* h, uint32_t flags, const void* x, const float* x_scales, bool prequant,
                           const float* w, void* recv_x, float* recv_scales, float* recv_weights,
                           int32_t* recv_meta, bool meta, hipStream_t s) {
   ep_status st = check_handle(h);
+  if (st == EP_OK) st = check_device(h);
   if (st != EP_OK) return st;
   if (flags & ~(uint32_t)(EP_DISPATCH_FP8 | EP_DISPATCH_ZERO_PADDING | EP_DISPATCH_SCALES_COL_MAJOR))
     return fail(EP_ERR_SHAPE, "unknown dispatch flags 0x%x", flags);
@@ -461,6 +404,8 @@ ep_status ep_get_layout(const ep_config* cfg, const int64_t* topk_idx, void* str
 
 ep_status ep_relayout(ep_handle* h, const int64_t* topk_idx, void* stream, int64_t* total_rows) {
   if (!h) return fail(EP_ERR_NULL, "handle is NULL");
+  ep_status st = check_device(h);
+  if (st != EP_OK) return st;
   if (h->T > 0 && !topk_idx) return fail(EP_ERR_NULL, "topk_idx is NULL");
   if (misaligned(topk_idx, 8)) return fail(EP_ERR_SHAPE, "topk_idx must be 8-byte aligned");
   return run_layout(h, topk_idx, (hipStream_t)stream, total_rows);
@@ -495,50 +440,16 @@ ep_status ep_dispatch_prequant_cached(const ep_handle* h, uint32_t flags, const 
 ep_status ep_combine(const ep_handle* h, const void* y, const float* topk_weights, const void* bias, void* out,
                      void* stream) {
   ep_status st = check_handle(h);
+  if (st == EP_OK) st = check_device(h);
   if (st != EP_OK) return st;
   if (h->T == 0) return EP_OK;
   if (!out) return fail(EP_ERR_NULL, "out is NULL");
   if (h->total_rows > 0 && !y) return fail(EP_ERR_NULL, "y is NULL");
   if (misaligned(y, 16) || misaligned(out, 16) || misaligned(bias, 16) || misaligned(topk_weights, 4))
     return fail(EP_ERR_SHAPE, "y / bias / out must be 16-byte aligned, topk_weights 4-byte aligned");
-  // Whole rows of up to 8 KiB (K <= 8, so <= 64 KiB of LDS per token and two
-  // workgroups per CU) go through the LDS kernel: every wave streams one slot's
-  // full row.  Measured faster than the register kernel at hidden 4096 and not
-  // at 7168, where a token's rows no longer fit twice per CU.
-  if (h->dims.K <= 8 && h->cfg.hidden <= 4096) {
-    const int need = ((h->cfg.hidden >> 3) + kWave - 1) / kWave;  // chunks per lane for a whole row
-    CombineArgs a{(const uint16_t*)y, topk_weights, h->dst_row, (const uint16_t*)bias, (uint16_t*)out,
-                  (int)h->T, h->dims.K, h->cfg.hidden, 1};
-    hipStream_t s = (hipStream_t)stream;
-    const size_t lds_row = (size_t)h->dims.K * kWave * 16;  // per chunk per lane
-    if (h->T >= ((int64_t)1 << 31)) return fail(EP_ERR_OVERFLOW, "combine grid too large");
-    const int grid = (int)h->T;
-    if (need <= 1)
-      combine_lds_kernel<1><<<grid, 512, lds_row * 1, s>>>(a);
-    else if (need <= 2)
-      combine_lds_kernel<2><<<grid, 512, lds_row * 2, s>>>(a);
-    else if (need <= 4)
-      combine_lds_kernel<4><<<grid, 512, lds_row * 4, s>>>(a);
-    else
-      combine_lds_kernel<8><<<grid, 512, lds_row * 8, s>>>(a);
-    EP_LAUNCHED("combine_lds_kernel");
-    return EP_OK;
-  }
-  const int nct = std::min(pick_nc(h->cfg.hidden, EP_COMBINE_NCT), 4);
   CombineArgs a{(const uint16_t*)y, topk_weights, h->dst_row, (const uint16_t*)bias, (uint16_t*)out,
-                (int)h->T, h->dims.K, h->cfg.hidden, parts_per_row(h->cfg.hidden, nct)};
-  const int64_t waves = h->T * a.split;
-  if (waves >= ((int64_t)1 << 31) / kWave) return fail(EP_ERR_OVERFLOW, "combine grid too large (%lld waves)", (long long)waves);
-  const int threads = EP_COMBINE_BLOCK_WAVES * kWave;
-  const int blocks = (int)((waves + EP_COMBINE_BLOCK_WAVES - 1) / EP_COMBINE_BLOCK_WAVES);
-  hipStream_t s = (hipStream_t)stream;
-  switch (nct) {
-    case 1: combine_kernel<1, EP_COMBINE_G><<<blocks, threads, 0, s>>>(a); break;
-    case 2: combine_kernel<2, EP_COMBINE_G><<<blocks, threads, 0, s>>>(a); break;
-    default: combine_kernel<4, EP_COMBINE_G><<<blocks, threads, 0, s>>>(a); break;
-  }
-  EP_LAUNCHED("combine_kernel");
-  return EP_OK;
+                (int)h->T, h->dims.K, h->cfg.hidden, 1};
+  return launch_combine(a, (hipStream_t)stream);
 }
 
 void ep_handle_free(ep_handle* h) { release(h); }
@@ -622,6 +533,19 @@ ep_status ep_handle_tensor(const ep_handle* h, int32_t which, const void** dev_p
   *dev_ptr = p;
   *numel = n;
   *elem_bytes = b;
+  return EP_OK;
+}
+
+ep_status ep_debug_copy(void* dst, const void* src, int64_t nbytes, void* stream) {
+  if (nbytes < 0 || nbytes % 1024 != 0) return fail(EP_ERR_SHAPE, "nbytes must be a non-negative multiple of 1024");
+  if (nbytes == 0) return EP_OK;
+  if (!dst || !src) return fail(EP_ERR_NULL, "NULL argument");
+  if (misaligned(dst, 16) || misaligned(src, 16)) return fail(EP_ERR_SHAPE, "dst / src must be 16-byte aligned");
+  const int64_t waves = nbytes / 1024;
+  if (waves >= ((int64_t)1 << 31) / kWave) return fail(EP_ERR_OVERFLOW, "nbytes too large");
+  const int blocks = (int)((waves + 3) / 4);
+  copy_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>((u32x4*)dst, (const u32x4*)src, waves);
+  EP_LAUNCHED("copy_kernel");
   return EP_OK;
 }
 

@@ -33,6 +33,9 @@
  *    before anything is enqueued.  ep_last_error() gives a message.
  *  - One handle may be used by any number of ep_dispatch_cached / ep_combine
  *    calls; ep_handle_free and ep_relayout require that none is in flight.
+ *  - A handle belongs to the device that was current at ep_get_layout; calls
+ *    that launch work with another device current return
+ *    EP_ERR_HANDLE_MISMATCH.
  *  - Two output-length modes ("Ascend DeepEP MoE Dispatch Optimization",
  *    section "Output length has a dynamic and a fixed mode"):
  *      exact  (num_worst_rows == 0): ep_get_layout reads the per-window row
@@ -283,6 +286,13 @@ ep_status ep_handle_tensor(const ep_handle *h, int32_t which, const void **dev_p
  * x / scale, so that it can be compared with a reference encoder.  Async on
  * `stream`.  Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_OVERFLOW, EP_ERR_HIP. */
 ep_status ep_debug_e4m3_encode(const float *in, uint8_t *out, int64_t n, void *stream);
+
+/* Calibration hook, not part of the method: a plain streaming copy of nbytes
+ * (a multiple of 1024) from src to dst (device, 16-byte aligned), one wave per
+ * KiB with 16-byte nontemporal accesses, the access unit of the dispatch and
+ * combine kernels.  Async on `stream`; gives the copy ceiling their bandwidth
+ * is compared with.  Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_OVERFLOW, EP_ERR_HIP. */
+ep_status ep_debug_copy(void *dst, const void *src, int64_t nbytes, void *stream);
 
 /* Message for the last non-OK status returned on the calling thread. */
 const char *ep_last_error(void);

@@ -737,3 +737,58 @@ def test_maximum_ranks_experts_topk(S, A):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host_u16(out), oracle.combine(lay, w.H, y, wt))
     h.free()
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_symmetric_windows_dispatch_and_combine(fp8):
+    """Symmetric windows (every window max_d num_expanded rows): the kernels map packed row
+    positions to window rows by a search over the window bases; rows past a window's
+    num_expanded stay untouched.  Then a relayout to another routing on the same handle."""
+    w = SMALL[2]  # 128 ranks, Zipf: very uneven windows
+    topk = routing_with_holes(w, 18)
+    lay, h = layout_both(w, topk, symmetric=True)
+    check_layout(lay, h)
+    x = synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    for it, tk in enumerate((topk, synth.gen_routing(synth.scaled(w, seed=77)))):
+        if it:
+            ep.relayout(h, torch.from_numpy(tk).to(DEV))
+            lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, tk, True)
+            check_layout(lay, h)
+        R = h.total_rows
+        say("symmetric dispatch", "fp8" if fp8 else "bf16", "layout", it, "rows", R)
+        rx = torch.full((R, w.H), 0x7F if fp8 else -1, dtype=torch.uint8 if fp8 else torch.int16, device=DEV)
+        if not fp8:
+            rx = rx.view(torch.bfloat16)
+        sc = torch.full((R, w.H // 128), float("nan"), dtype=torch.float32, device=DEV) if fp8 else None
+        rw = torch.full((R,), float("nan"), dtype=torch.float32, device=DEV)
+        rm = torch.full((R, 2), 77, dtype=torch.int32, device=DEV)
+        ep.dispatch(h, xd, wd, fp8=fp8, zero_padding=True, out=(rx, sc, rw, rm))
+        torch.cuda.synchronize()
+        ox, osc, ow, om = oracle.dispatch(lay, w.H, x, wt, fp8, True, fill=0x7F if fp8 else 0xFFFF)
+        np.testing.assert_array_equal(rx.cpu().numpy() if fp8 else host_u16(rx), ox)
+        # rows past num_expanded (window tails) are not written: meta stays at its fill there
+        used = np.zeros(R, bool)
+        for d in range(w.P):
+            b = int(lay.window_row_base[d])
+            used[b:b + int(lay.num_expanded[d])] = True
+        np.testing.assert_array_equal(rm.cpu().numpy()[used], om[used])
+        assert np.all(rm.cpu().numpy()[~used] == 77)
+        np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32)[used], ow.view(np.uint32)[used])
+        if fp8:
+            np.testing.assert_array_equal(sc.cpu().numpy()[used].view(np.uint32), osc[used].view(np.uint32))
+        y = synth.gen_expert_out(w, R)
+        out = ep.combine(h, dev_bf16(y), wd)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_u16(out), oracle.combine(lay, w.H, y, wt))
+    h.free()
+
+
+def test_debug_copy_is_a_copy():
+    """The calibration copy moves every byte (a few MiB, an odd number of KiB)."""
+    src = torch.randint(0, 256, ((4 << 20) + 3 * 1024,), dtype=torch.uint8, device=DEV)
+    dst = torch.zeros_like(src)
+    ep.debug_copy(dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
