@@ -79,6 +79,7 @@ struct ep_handle {
   int64_t* summary_dev;
   int64_t* summary_host = nullptr;  // pinned
   hipEvent_t done = nullptr;        // end of the last layout's work
+  hipEvent_t summary_ready = nullptr;  // the last layout's host summary has landed
   size_t lds_count, lds_scan, lds_finalize, lds_rank;
 };
 
@@ -178,6 +179,8 @@ ep_status allocate(ep_handle* h) {
   }
   e = hipHostMalloc((void**)&h->summary_host, (size_t)((kSummaryHeader + 3 * P + 1) * 8), hipHostMallocDefault);
   if (e != hipSuccess) return fail(EP_ERR_NOMEM, "hipHostMalloc: %s", hipGetErrorString(e));
+  e = hipEventCreateWithFlags(&h->summary_ready, hipEventDisableTiming);
+  if (e != hipSuccess) return fail(EP_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
   e = hipEventCreateWithFlags(&h->done, hipEventDisableTiming);
   if (e != hipSuccess) return fail(EP_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
 
@@ -197,6 +200,7 @@ ep_status allocate(ep_handle* h) {
 
 void release(ep_handle* h) {
   if (!h) return;
+  if (h->summary_ready) (void)hipEventDestroy(h->summary_ready);
   if (h->done) {
     (void)hipEventSynchronize(h->done);
     (void)hipEventDestroy(h->done);
@@ -226,6 +230,7 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
   EP_LAUNCHED("layout_finalize_kernel");
   EP_HIP(hipMemcpyAsync(h->summary_host, h->summary_dev, (size_t)(kSummaryHeader + 3 * d.P + 1) * 8,
                         hipMemcpyDeviceToHost, s));
+  EP_HIP(hipEventRecord(h->summary_ready, s));
   {
     // at least one workgroup per expert, so that the padding rows are written even when T = 0
     RankOut ro{h->dst_slot, h->dst_row, h->row_slot, h->send_head, h->recv_src_idx, h->pad_rows};
@@ -242,7 +247,9 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
     if (total_rows) *total_rows = h->total_rows;
     return EP_OK;
   }
-  EP_HIP(hipEventSynchronize(h->done));
+  // The host needs only the summary; the rank kernel keeps running meanwhile,
+  // so the caller's next launches queue up behind it without a gap.
+  EP_HIP(hipEventSynchronize(h->summary_ready));
   const int64_t* sm = h->summary_host;
   if (sm[2] != 0) return fail(EP_ERR_ROUTING, "topk_idx holds an expert id outside {-1} U [0, %d)", d.E);
   if (sm[0] >= ((int64_t)1 << 31))
@@ -265,7 +272,7 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
 ep_status ensure_counts(const ep_handle* hc) {
   ep_handle* h = const_cast<ep_handle*>(hc);
   if (h->counts_known) return EP_OK;
-  EP_HIP(hipEventSynchronize(h->done));
+  EP_HIP(hipEventSynchronize(h->summary_ready));
   const int64_t* sm = h->summary_host;
   h->total_pad = sm[1];
   h->sum_recv = sm[3];

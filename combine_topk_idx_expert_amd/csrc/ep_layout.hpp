@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
 // [4] tail rows of fixed windows  [5] rows dropped past fixed windows' ends
 // [6, 6+P) num_expanded  [6+P, 6+2P) num_recv_tokens  [6+2P, 7+3P) window_row_base.
 constexpr int kSummaryHeader = 6;
-constexpr int kFinalizeThreads = 1024;
+constexpr int kFinalizeThreads = 256;
 
 struct FinalizeOut {
   int32_t* n_e;             // [E]

@@ -21,8 +21,8 @@
  *    bf16 / fp8 row tensors (x, x_codes, recv_x, y, bias, out) must be 16-byte aligned, other
  *    arrays aligned to their element size (else EP_ERR_SHAPE).
  *  - `stream` is a hipStream_t (0 = the null stream).  All device work of a
- *    call is enqueued on it; calls other than ep_get_layout / ep_relayout
- *    return without waiting for it.
+ *    call is enqueued on it; calls return without waiting for it, except that
+ *    ep_get_layout / ep_relayout in exact mode wait for the row counts.
  *  - Token u = s * S + t is token t of virtual rank s (the tutorial's source
  *    token global index, section 2.1); T = P * S.
  *  - Expert e lives on rank e / E_l, E_l = E / P (contiguous blocks; the
@@ -107,8 +107,9 @@ typedef struct ep_handle ep_handle; /* opaque; owns its device arrays */
  * "What the six handle entries store"; TileLang tutorial ch. 38, sections 2.2,
  * 2.4 and 3.5).
  *
- *   topk_idx  device, int64 [T, K]; read during the call only (the handle
- *             keeps what it needs, so later writes to topk_idx are harmless).
+ *   topk_idx  device, int64 [T, K]; read by the work this call enqueues on
+ *             `stream` (the handle keeps what it needs, so writes to topk_idx
+ *             ordered after that work are harmless).
  *   out       receives a new handle (NULL on error); free with ep_handle_free.
  *   total_rows  host, receives the row count the caller must allocate for the
  *             expanded tensors (recv_x, recv_scales, recv_weights,
@@ -124,9 +125,10 @@ typedef struct ep_handle ep_handle; /* opaque; owns its device arrays */
  *   recv_src_idx (per destination, the local token index of each received
  *   token).  Receive lists are ordered by source rank then token; the rows of
  *   one expert are ordered by (u, j) -- the tutorial's deterministic order.
- * Allocates the handle's device memory (hipMalloc).  Exact mode: synchronizes
- * `stream` once to read back the per-window row counts (the pages' do_cpu_sync
- * mode).  Fixed mode: returns as soon as the work is enqueued, with
+ * Allocates the handle's device memory (hipMalloc).  Exact mode: waits once
+ * for the per-window row counts to reach the host (the pages' do_cpu_sync
+ * mode); the last layout kernel may still be running on `stream` when the call
+ * returns, and later work on `stream` is ordered after it.  Fixed mode: returns as soon as the work is enqueued, with
  * total_rows = P * num_worst_rows; a routing error does not fail the call
  * (the bad slots are treated as unused) and is reported by ep_handle_status.
  * Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_OVERFLOW, EP_ERR_ROUTING (exact
