@@ -492,7 +492,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the P "
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); the P "
               "expert-parallel ranks are virtual windows in one GPU's HBM.", file=sys.stderr)
         return 2
     if args.calls:

@@ -59,7 +59,7 @@ extern "C" {
 
 #define EP_ABI_VERSION 3
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define EP_MAX_RANKS 1024
 #define EP_MAX_EXPERTS 4096
 #define EP_MAX_TOPK 32
