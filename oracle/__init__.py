@@ -24,6 +24,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
+_HDR = os.path.join(_HERE, "oracle.h")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math"]
 
@@ -32,9 +33,10 @@ OK, ERR_SHAPE, ERR_ROUTING = 0, -2, -3
 
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
+            os.path.getmtime(_SRC), os.path.getmtime(_HDR)):
         tmp = _LIB_PATH + ".tmp"
-        subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        subprocess.run(["gcc", *CFLAGS, "-I", _HERE, "-o", tmp, _SRC, "-lm"], check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -45,7 +47,8 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
+                os.path.getmtime(_SRC), os.path.getmtime(_HDR)):
             build(force=True)
         L = ctypes.CDLL(_LIB_PATH)
         P_ = ctypes.c_void_p

@@ -37,9 +37,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_OK 0
-#define ORACLE_ERR_SHAPE (-2)
-#define ORACLE_ERR_ROUTING (-3)
+#include "oracle.h"
 
 /* ------------------------------------------------------------------------ */
 /* Scalar encodings                                                          */

@@ -115,3 +115,22 @@ def test_python_binding_rejects_host_tensors():
         ep.get_layout(cfg, torch.zeros((8, 2), dtype=torch.int32))
     with pytest.raises(TypeError):
         ep.get_layout(cfg, [[0, 1]] * 8)
+
+
+def test_c_program_links_against_the_library():
+    """tests/c_abi/roundtrip (built by __graft_entry__.build()) drives the C ABI from C++
+    alone; on the CPU check that it resolves the library and the oracle."""
+    import subprocess
+
+    exe = os.path.join(ROOT, "tests", "c_abi", "roundtrip")
+    if not os.path.exists(exe):
+        import importlib.util
+
+        spec = importlib.util.spec_from_file_location("c_abi_build", os.path.join(ROOT, "tests", "c_abi", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    out = subprocess.run(["ldd", exe], capture_output=True, text=True, check=True).stdout
+    for lib in ("libep_mi355x.so", "liboracle.so"):
+        line = next(ln for ln in out.splitlines() if lib in ln)
+        assert "not found" not in line, line

@@ -792,3 +792,17 @@ def test_debug_copy_is_a_copy():
     ep.debug_copy(dst, src)
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
+
+
+def test_c_abi_program_roundtrip():
+    """The C ABI from C++ alone (tests/c_abi/roundtrip.cpp): layout, bf16 / fp8 / cached
+    dispatch and combine against the oracle, run as a child process."""
+    import os
+    import subprocess
+
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "roundtrip")
+    assert os.path.exists(exe), "build tests/c_abi/roundtrip first (__graft_entry__.build())"
+    say("c abi roundtrip")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    print(r.stdout, r.stderr)
+    assert r.returncode == 0 and "ok" in r.stdout, (r.returncode, r.stdout, r.stderr)
