@@ -148,9 +148,20 @@ __device__ __forceinline__ void store_pacing() {
   }
 }
 
+// scales: fp8 row-major scales to zero with the row (null: none)
 template <int NC, bool FP8>
 __device__ __forceinline__ void zero_row_part(uint8_t* recv, int64_t row, int part, int64_t out_row_bytes,
-                                              int nchunk, int lane) {
+                                              int nchunk, int lane, float* scales) {
+  if constexpr (FP8) {
+    if (scales) {
+      const int nblk = nchunk >> 4;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int blk = (part * NC * kWave + c * kWave) / 16 + lane;
+        if (lane < 4 && blk < nblk) scales[row * nblk + blk] = 0.0f;
+      }
+    }
+  }
   uint8_t* dst = recv + row * out_row_bytes;
   const int tile = part * NC * kWave;
 #pragma unroll
@@ -219,6 +230,12 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
       }
     } else {
       const int nblk = a.H >> 7;
+      // Quantised here with row-major scales: the waves also write each row's
+      // scales, lanes 0..3 holding the scales of the part's four 128-channel
+      // blocks.  Otherwise dispatch_scales_kernel writes them afterwards from
+      // tok_scales (column-major) or the caller's scales (pre-quantised).
+      const bool fused_scales = !PREQ && !a.scales_cm;
+      float sc[NC];
 #pragma unroll
       for (int c = 0; c < NC && !PREQ; ++c) {
         uint32_t m = 0;
@@ -228,7 +245,8 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
         const float scale = __uint_as_float(m << 16) / 448.0f;
         codes[c] = quantize8(v[c], scale, m == 0);
         const int q = tile + c * kWave + lane;
-        if ((lane & 15) == 0 && q < nchunk) a.tok_scales[(int64_t)u * nblk + (q >> 4)] = scale;
+        if (!fused_scales && (lane & 15) == 0 && q < nchunk) a.tok_scales[(int64_t)u * nblk + (q >> 4)] = scale;
+        sc[c] = __shfl(scale, (lane & 3) * 16, kWave);
       }
       for (int j = 0; j < a.K; ++j) {
         const int row = __builtin_amdgcn_readlane(my_row, j);
@@ -238,15 +256,18 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
         for (int c = 0; c < NC; ++c) {
           const int q = tile + c * kWave + lane;
           if (q < nchunk) stream_store(dst + q, codes[c]);
+          const int blk = (tile + c * kWave) / 16 + lane;
+          if (fused_scales && lane < 4 && blk < nblk) a.recv_scales[(int64_t)row * nblk + blk] = sc[c];
         }
         store_pacing<NC>();
       }
     }
   } else if (gw < token_items + pad_items) {
+    float* zero_scales = (FP8 && !PREQ && !a.scales_cm) ? a.recv_scales : nullptr;  // fused scales only
     if constexpr (!FIXED) {
       const int p = (gw - token_items) / a.split;
       const int part = (gw - token_items) - p * a.split;
-      zero_row_part<NC, FP8>(recv, a.pad_rows[p], part, out_row_bytes, nchunk, lane);
+      zero_row_part<NC, FP8>(recv, a.pad_rows[p], part, out_row_bytes, nchunk, lane, zero_scales);
     } else {
       // Fixed windows: padding rows (if asked) then tail rows (always),
       // counted on the device.  Wave w zeroes whole rows z = z0 + w, z0 + w +
@@ -269,7 +290,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
           row = (int64_t)win * a.cap + a.cap - (a.tail_base[win + 1] - a.tail_base[win]) + (k - a.tail_base[win]);
         }
         for (int part = 0; part < a.split; ++part)
-          zero_row_part<NC, FP8>(recv, row, part, out_row_bytes, nchunk, lane);
+          zero_row_part<NC, FP8>(recv, row, part, out_row_bytes, nchunk, lane, zero_scales);
       }
     }
   } else if (META) {
@@ -293,7 +314,9 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
 
 // fp8 row scales: recv_scales[row][b] (or [b][row] column-major) = scale of
 // the row's source token (0 for padding rows with zero padding, otherwise
-// untouched; 0 for the tail rows of fixed windows).
+// untouched; 0 for the tail rows of fixed windows).  Launched for column-major
+// scales and for pre-quantised input; row-major scales of data quantised by
+// the dispatch kernel are written by its own waves.
 // Row-major: one thread per (row, block), consecutive threads walk a row's
 // blocks.  Column-major: one thread per row, walking the blocks: each thread
 // reads its token's scales contiguously and, for every block, consecutive
