@@ -806,3 +806,56 @@ def test_c_abi_program_roundtrip():
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     print(r.stdout, r.stderr)
     assert r.returncode == 0 and "ok" in r.stdout, (r.returncode, r.stdout, r.stderr)
+
+
+def test_fixed_windows_capture_in_a_graph():
+    """Fixed windows never wait on the host, so relayout + dispatch + combine can be captured
+    in one graph.  Each replay (new x copied into the captured input between replays, with
+    eager work and synchronisations in between) must match the eager calls."""
+    w = SMALL[1]
+    topk = synth.gen_routing(w)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    W = int(lay.num_expanded.max()) + 64
+    topk_d = torch.from_numpy(topk).to(DEV)
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A, num_worst_rows=W), topk_d)
+    wt = synth.gen_weights(w)
+    wd = torch.from_numpy(wt).to(DEV)
+    x_static = dev_bf16(synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H))
+    R = h.total_rows
+    rx = torch.empty((R, w.H), dtype=torch.bfloat16, device=DEV)
+    rw = torch.empty(R, dtype=torch.float32, device=DEV)
+    rm = torch.empty((R, 2), dtype=torch.int32, device=DEV)
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        ep.relayout(h, topk_d)
+        ep.dispatch(h, x_static, wd, zero_padding=True, out=(rx, None, rw, rm))
+        ep.combine(h, rx, wd, out=out)
+
+    step()  # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("capture fixed-window step")
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for it in range(3):
+        xi = dev_bf16(synth.gen_bf16_rows(w.seed + 100 + it, wl.STREAM_X, w.T, w.H))
+        x_static.copy_(xi)
+        torch.cuda.synchronize()
+        say("graph replay", it)
+        g.replay()
+        torch.cuda.synchronize()
+        got = (rx.clone(), rw.clone(), rm.clone(), out.clone())
+        step()  # eager reference on the same input
+        torch.cuda.synchronize()
+        assert torch.equal(got[0].view(torch.int16), rx.view(torch.int16))
+        assert torch.equal(got[1].view(torch.int32), rw.view(torch.int32))
+        assert torch.equal(got[2], rm)
+        assert torch.equal(got[3].view(torch.int16), out.view(torch.int16))
+        # and against the oracle
+        np.testing.assert_array_equal(host_u16(got[3]), oracle.combine_identity(w.K, w.H, False, topk,
+                                                                                 host_u16(xi), wt, 0, w.T))
+    assert h.status() == (0, 0)
+    del g
+    h.free()
