@@ -202,6 +202,15 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
     const int my_row = lane < a.K ? a.dst_row[(int64_t)u * a.K + lane] : -1;
     u32x4 v[NC];
     u32x2 codes[NC];
+    float pq_sc[NC];  // pre-quantised: lanes 0..3 load the part's four block scales up front
+    if constexpr (PREQ) {
+      const int nb = a.H >> 7;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int blk = (tile + c * kWave) / 16 + lane;
+        pq_sc[c] = (!a.scales_cm && lane < 4 && blk < nb) ? a.tok_scales[(int64_t)u * nb + blk] : 0.0f;
+      }
+    }
     if constexpr (PREQ) {  // 8 code bytes per 16-byte bf16 chunk position
       const u32x2* csrc = (const u32x2*)(a.x_codes + (int64_t)u * a.H);
 #pragma unroll
@@ -230,12 +239,14 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
       }
     } else {
       const int nblk = a.H >> 7;
-      // Quantised here with row-major scales: the waves also write each row's
-      // scales, lanes 0..3 holding the scales of the part's four 128-channel
-      // blocks.  Otherwise dispatch_scales_kernel writes them afterwards from
-      // tok_scales (column-major) or the caller's scales (pre-quantised).
-      const bool fused_scales = !PREQ && !a.scales_cm;
+      // Row-major scales: the waves also write each row's scales, lanes 0..3
+      // holding the scales of the part's four 128-channel blocks (computed
+      // here, or the caller's, loaded up front).  Column-major scales are
+      // written afterwards by dispatch_scales_kernel from tok_scales.
+      const bool fused_scales = !a.scales_cm;
       float sc[NC];
+#pragma unroll
+      for (int c = 0; c < NC && PREQ; ++c) sc[c] = pq_sc[c];
 #pragma unroll
       for (int c = 0; c < NC && !PREQ; ++c) {
         uint32_t m = 0;
@@ -263,7 +274,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
       }
     }
   } else if (gw < token_items + pad_items) {
-    float* zero_scales = (FP8 && !PREQ && !a.scales_cm) ? a.recv_scales : nullptr;  // fused scales only
+    float* zero_scales = (FP8 && !a.scales_cm) ? a.recv_scales : nullptr;  // fused scales only
     if constexpr (!FIXED) {
       const int p = (gw - token_items) / a.split;
       const int part = (gw - token_items) - p * a.split;
@@ -315,8 +326,8 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
 // fp8 row scales: recv_scales[row][b] (or [b][row] column-major) = scale of
 // the row's source token (0 for padding rows with zero padding, otherwise
 // untouched; 0 for the tail rows of fixed windows).  Launched for column-major
-// scales and for pre-quantised input; row-major scales of data quantised by
-// the dispatch kernel are written by its own waves.
+// scales only; row-major scales are written by the dispatch kernel's own
+// waves.
 // Row-major: one thread per (row, block), consecutive threads walk a row's
 // blocks.  Column-major: one thread per row, walking the blocks: each thread
 // reads its token's scales contiguously and, for every block, consecutive

@@ -68,8 +68,8 @@ ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
     dispatch_kernel<nc, FP8, META, PREQ, FIXED><<<blocks, threads, lds, s>>>(a);
     EP_LAUNCHED("dispatch_kernel");
   }
-  // row-major scales of data quantised here are written by the dispatch waves
-  if (FP8 && (PREQ || a.scales_cm)) {
+  // row-major scales are written by the dispatch waves themselves
+  if (FP8 && a.scales_cm) {
     const int64_t n = a.scales_cm ? out_rows : out_rows * (a.H >> 7);  // threads
     if (n > 0) {
       if (n >= ((int64_t)1 << 31)) return fail(EP_ERR_OVERFLOW, "scale grid too large");
