@@ -21,18 +21,16 @@
 
 namespace ep {
 
-constexpr int kRowThreads = 256;  // 4 waves per workgroup
-constexpr int kRowWaves = kRowThreads / kWave;
-
 // Rows are split into column parts of NC 16-byte chunks per lane (NC KiB of
 // bf16 per wave); a wave handles one (row, part).  Short-lived waves that
 // each move a few KiB keep more of HBM's write bandwidth than long-lived
 // waves that move whole rows (measured on MI355X).
 //
-// Row metadata (weights, source slot, fp8 scales) is written in row order by
-// waves that each own 64 consecutive expanded rows, so every store is
-// coalesced; scattering it per token would issue millions of partial-line
-// writes.
+// Row metadata (weight, source slot) is written in row order by waves that
+// each own 64 consecutive expanded rows, so every store is coalesced; that
+// measured faster than letting the token waves scatter it.  The fp8 scales of
+// a row, by contrast, are written by the token waves next to its codes, which
+// measured faster than a separate row-order pass.
 struct DispatchArgs {
   const uint16_t* x;             // [T][H] bf16
   const float* w;                // [T][K]           (fresh only)
@@ -121,8 +119,8 @@ __device__ __forceinline__ int fixed_row_slot(const DispatchArgs& a, int64_t g) 
 //   [.., + total_pad*split)           zero payload of (padding row, part)   if zero_pad
 //   [.., + ceil(sum_expanded / 64))   row metadata of 64 rows               if META
 //   fixed windows (cap > 0), counts read on the device:
-//   [.., + zero_waves)                waves striding over (padding row, part) if zero_pad
-//                                     and (tail row, part)
+//   [.., + zero_waves)                waves striding over whole padding rows (if zero_pad)
+//                                     and tail rows
 //   [.., + ceil(P * cap / 64))        row metadata of 64 rows               if META
 // NC: 16-byte chunks per lane per wave (the column part is 64 * NC chunks).
 // Store pacing: after each destination row, wait until at most
