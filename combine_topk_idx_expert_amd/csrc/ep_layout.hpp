@@ -14,7 +14,9 @@
 //  2. layout_scan   -- one workgroup per histogram column (E experts + P
 //     ranks): exclusive scan over chunks in order, per-source-rank sums.
 //  3. layout_finalize -- one workgroup: aligned expert sizes, window offsets,
-//     window bases, receive-list bases, padding-row list, host summary.
+//     window bases, receive-list bases, where each expert's padding rows go
+//     in the padding list, host summary (fixed windows: clipped padding,
+//     tail bases, dropped rows).
 //  4. layout_rank   -- one 4-wave workgroup per chunk again; wave w owns the
 //     chunk's tokens [16w, 16w + 16).  Each wave counts its slots per key
 //     (expert, first-seen destination rank); a prefix over the waves, seeded
@@ -23,7 +25,8 @@
 //     in memory order; lanes holding the same key are found with ballots,
 //     their order within the step is their lane order, and the wave's
 //     running counter per key carries the order across steps.  This yields
-//     the global stable order by (u, j).
+//     the global stable order by (u, j).  The same kernel writes the
+//     padding-row list and send_head.
 #pragma once
 
 #include "ep_device.hpp"
