@@ -490,7 +490,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
       u32x4 o;
 #pragma unroll
       for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(acc[c][2 * k], acc[c][2 * k + 1]);
-      dst[q] = o;
+      stream_store(dst + q, o);  // nontemporal: measured 3-4% faster
     }
   }
 }
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(512) void combine_lds_kernel(CombineArgs a) {
     u32x4 o;
 #pragma unroll
     for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(acc[2 * k], acc[2 * k + 1]);
-    dst[q] = o;
+    stream_store(dst + q, o);  // nontemporal: measured 3-4% faster
   }
 }
 
