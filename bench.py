@@ -16,7 +16,9 @@ Prints ONE JSON line.  Usage:
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME] [--no-cpu] [--no-fixed]
 
 `python bench.py --calls` instead times every call of the library on every
-workload (median of 10 back-to-back calls each, HIP events) and prints one
+workload (HIP events; median and minimum of 20 calls, each timed alone after
+3 untimed ones, once right after the previous call and once with the L2s and
+the memory-side cache flushed by a 1 GiB scratch buffer) and prints one
 JSON line per workload: layout, dispatch, cached dispatch, combine, combine
 with a bias, fixed-window dispatch, and for fp8 workloads the pre-quantised
 and column-major-scale dispatches, each with its ledger bytes and % of HBM.
@@ -263,16 +265,22 @@ def device_ceilings(dev) -> dict:
 _last_min_us = [0.0]
 
 
-def _median_us(fn, reps: int = 10) -> float:
-    """Median of `reps` timed calls (HIP events); the minimum is kept in _last_min_us."""
+def _median_us(fn, reps: int = 20, warmup: int = 3, flush=None) -> float:
+    """Median of `reps` timed calls (HIP events), each timed alone between two
+    synchronisations, after `warmup` untimed ones; the minimum is kept in
+    _last_min_us.  `flush`, if given, runs before every timed call, outside the
+    events."""
     import statistics
 
     import torch
 
-    fn()
+    for _ in range(warmup):
+        fn()
     torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
+        if flush is not None:
+            flush()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         fn()
@@ -281,6 +289,21 @@ def _median_us(fn, reps: int = 10) -> float:
         ts.append(a.elapsed_time(b))
     _last_min_us[0] = min(ts) * 1e3
     return statistics.median(ts) * 1e3
+
+
+def _cache_flusher(dev):
+    """Writes, then reads, a 1 GiB scratch buffer: every line of the L2s and of the
+    256 MB memory-side cache is then someone else's, and clean, when the timed call
+    starts."""
+    import torch
+
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def flush():
+        scratch.fill_(1.0)
+        scratch.sum()
+
+    return flush
 
 
 def calls_table() -> int:
@@ -294,6 +317,7 @@ def calls_table() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    flush = _cache_flusher(dev)
     for name in synth.CONFIG_ORDER:
         w = synth.CONFIGS[name]
         T, K, H = w.T, w.K, w.H
@@ -313,11 +337,17 @@ def calls_table() -> int:
         nb = H // 128
         r = {"workload": name, "T": T, "rows": rows, "pad": pad, "dtype": "fp8" if fp8 else "bf16"}
 
-        def put(key, us, nbytes):
+        def put(key, fn, nbytes):
+            # each call twice: right after the previous one, and with the caches flushed first
+            us = _median_us(fn)
             r[key + "_us"] = round(us, 1)
             r[key + "_min_us"] = round(_last_min_us[0], 1)
             r[key + "_GBps"] = round(nbytes / us / 1e3, 1)
             r[key + "_frac_hbm"] = round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)
+            us = _median_us(fn, flush=flush)
+            r[key + "_flushed_us"] = round(us, 1)
+            r[key + "_flushed_min_us"] = round(_last_min_us[0], 1)
+            r[key + "_flushed_frac_hbm"] = round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)
 
         torch.cuda.synchronize()
         lt = []
@@ -333,7 +363,7 @@ def calls_table() -> int:
         rw = torch.empty(R, dtype=torch.float32, device=dev)
         rm = torch.empty((R, 2), dtype=torch.int32, device=dev)
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        put("dispatch", _median_us(lambda: ep.dispatch(h, x_d, w_d, fp8, w.zero_padding, out=(rx, sc, rw, rm))),
+        put("dispatch", lambda: ep.dispatch(h, x_d, w_d, fp8, w.zero_padding, out=(rx, sc, rw, rm)),
             led["dispatch"])
         # fresh end to end: layout with its read-back, then dispatch (host wall clock)
         torch.cuda.synchronize()
@@ -348,23 +378,21 @@ def calls_table() -> int:
         b = 1 if fp8 else 2
         sf = 4 * nb if fp8 else 0
         cached = T * H * 2 + 4 * T * K + rows * (H * b + sf) + (pad * (H * b + sf) if w.zero_padding else 0)
-        put("cached", _median_us(lambda: ep.dispatch_cached(h, x_d, fp8, w.zero_padding, out=(rx, sc))), cached)
+        put("cached", lambda: ep.dispatch_cached(h, x_d, fp8, w.zero_padding, out=(rx, sc)), cached)
         y = torch.empty((R, H), dtype=torch.bfloat16, device=dev).normal_()
-        put("combine", _median_us(lambda: ep.combine(h, y, w_d, out=out)), led["combine"])
+        put("combine", lambda: ep.combine(h, y, w_d, out=out), led["combine"])
         bias = torch.empty((T, H), dtype=torch.bfloat16, device=dev).normal_()
-        put("combine_bias", _median_us(lambda: ep.combine(h, y, w_d, bias=bias, out=out)),
-            led["combine"] + T * H * 2)
+        put("combine_bias", lambda: ep.combine(h, y, w_d, bias=bias, out=out), led["combine"] + T * H * 2)
         if fp8:
             codes = torch.randint(0, 256, (T, H), dtype=torch.uint8, device=dev)
             xs = torch.rand((T, nb), dtype=torch.float32, device=dev)
             pre = T * H + T * nb * 4 + 8 * T * K + (led["dispatch"] - led["dispatch_read"])
             put("dispatch_prequant",
-                _median_us(lambda: ep.dispatch(h, (codes, xs), w_d, zero_padding=w.zero_padding,
-                                               out=(rx, sc, rw, rm))), pre)
+                lambda: ep.dispatch(h, (codes, xs), w_d, zero_padding=w.zero_padding, out=(rx, sc, rw, rm)), pre)
             sc_cm = torch.empty((nb, R), dtype=torch.float32, device=dev)
             put("dispatch_col_major_scales",
-                _median_us(lambda: ep.dispatch(h, x_d, w_d, True, w.zero_padding, scales_col_major=True,
-                                               out=(rx, sc_cm, rw, rm))), led["dispatch"])
+                lambda: ep.dispatch(h, x_d, w_d, True, w.zero_padding, scales_col_major=True,
+                                    out=(rx, sc_cm, rw, rm)), led["dispatch"])
             del codes, xs, sc_cm
         del rx, sc, rw, rm, y, bias
         torch.cuda.empty_cache()
@@ -389,8 +417,7 @@ def calls_table() -> int:
         tail = int(np.maximum(W - ne, 0).sum())
         zeroed = (pad if w.zero_padding else 0) + tail
         fixed_bytes = (T * H * 2 + 8 * T * K + rows * (H * b + sf) + RF * 12 + zeroed * (H * b + sf))
-        put("fixed_dispatch",
-            _median_us(lambda: ep.dispatch(hf, x_d, w_d, fp8, w.zero_padding, out=(rxf, scf, rwf, rmf))),
+        put("fixed_dispatch", lambda: ep.dispatch(hf, x_d, w_d, fp8, w.zero_padding, out=(rxf, scf, rwf, rmf)),
             fixed_bytes)
         hf.free()
         h.free()
