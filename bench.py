@@ -12,6 +12,11 @@ The same step is also timed with fixed-length windows (num_worst_rows: every
 window a 1024-row bucket above the largest one, no read-back), reported under
 "fixed_windows"; the headline value is the exact-length step.
 
+Before the timed steps, the outputs of the last warm-up step are checked at
+full size with plain torch ops on a seeded sample of tokens (expanded rows,
+their weights and metadata, zero padding, and the combine bit for bit);
+"parity" in the JSON line says what was checked.
+
 Prints ONE JSON line.  Usage:
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME] [--no-cpu] [--no-fixed]
 
@@ -216,6 +221,54 @@ def fixed_leg(ep, h_exact, w, topk, topk_d, x_d, w_d, out, steps: int, warmup: i
 # ---------------------------------------------------------------------------
 # device ceilings
 # ---------------------------------------------------------------------------
+
+def full_size_check(h, w, x_d, w_d, recv_x, recv_w, recv_m, out, n_sample: int = 4096) -> dict:
+    """Checks the last step's outputs at full size with plain torch ops, before
+    timing: for a seeded sample of tokens, every expanded row holds its token's
+    x row bit for bit with its weight and (u, j); every padding row is zero
+    with metadata (-1, -1) and weight 0; and the combine of the identity experts'
+    outputs equals, bit for bit, the fp32 sum of w_j * x over the slots in
+    order (separate multiply and add, from +0), rounded once to bf16.  Raises
+    on any mismatch."""
+    import numpy as np
+    import torch
+
+    T, K = w.T, w.K
+    dev = recv_x.device
+    dst = h.tensor("dst_row").view(T, K).long()
+    rng = np.random.default_rng(12345)
+    idx = torch.from_numpy(np.sort(rng.choice(T, size=min(n_sample, T), replace=False))).to(dev)
+    rows = dst[idx]  # [n, K]
+    acc = torch.zeros((idx.numel(), w.H), dtype=torch.float32, device=dev)
+    xs = x_d[idx]
+    for j in range(K):
+        r = rows[:, j]
+        ok = r >= 0
+        rv, iv = r[ok], idx[ok]
+        if not torch.equal(recv_x[rv].view(torch.int16), x_d[iv].view(torch.int16)):
+            raise AssertionError(f"dispatch: expanded rows differ from x (slot {j})")
+        if not torch.equal(recv_w[rv], w_d[iv, j]):
+            raise AssertionError(f"dispatch: row weights differ (slot {j})")
+        meta = torch.stack([iv.int(), torch.full_like(iv, j).int()], 1)
+        if not torch.equal(recv_m[rv], meta):
+            raise AssertionError(f"dispatch: row metadata differs (slot {j})")
+        prod = w_d[idx, j:j + 1] * xs.float()  # identity experts: y = recv_x
+        acc = torch.where(ok[:, None], acc + prod, acc)
+    if not torch.equal(out[idx].view(torch.int16), acc.to(torch.bfloat16).view(torch.int16)):
+        raise AssertionError("combine: output differs from the in-order fp32 sum rounded to bf16")
+    used = torch.zeros(recv_x.shape[0], dtype=torch.bool, device=dev)
+    flat = dst.reshape(-1)
+    used[flat[flat >= 0]] = True
+    pad = torch.nonzero(~used).reshape(-1)
+    if w.zero_padding and pad.numel():
+        for c in range(0, pad.numel(), 4096):
+            if torch.count_nonzero(recv_x[pad[c:c + 4096]].view(torch.int16)).item():
+                raise AssertionError("dispatch: a padding row is not zero")
+    if pad.numel() and not (bool((recv_m[pad] == -1).all()) and bool((recv_w[pad] == 0).all())):
+        raise AssertionError("dispatch: padding-row metadata is not (-1, -1) / 0")
+    return {"sampled_tokens": int(idx.numel()), "rows_checked": int((rows >= 0).sum()),
+            "padding_rows_checked": int(pad.numel()), "dispatch_bitwise": True, "combine_bitwise": True}
+
 
 def device_ceilings(dev) -> dict:
     """Context for the roofline: the memory clock and bus width the device reports,
@@ -581,6 +634,11 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    check = None
+    if args.warmup > 0:  # otherwise checked after the timed steps
+        log("full-size check of the last warm-up step's outputs")
+        check = full_size_check(h, w, x_d, w_d, recv_x, recv_w, recv_m, out)
+        torch.cuda.synchronize()
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     log("timing", args.steps, "steps")
@@ -590,6 +648,9 @@ def main() -> int:
         step(events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    if check is None:
+        log("full-size check of the last timed step's outputs")
+        check = full_size_check(h, w, x_d, w_d, recv_x, recv_w, recv_m, out)
     d_ms = [e[0].elapsed_time(e[1]) for e in events]
     c_ms = [e[1].elapsed_time(e[2]) for e in events]
 
@@ -641,6 +702,7 @@ def main() -> int:
         },
     }
 
+    result["parity"] = check
     result["device"] = device_ceilings(dev)
 
     if not args.no_fixed:
