@@ -240,7 +240,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
       // Row-major scales: the waves also write each row's scales, lanes 0..3
       // holding the scales of the part's four 128-channel blocks (computed
       // here, or the caller's, loaded up front).  Column-major scales are
-      // written afterwards by dispatch_scales_kernel from tok_scales.
+      // written afterwards by dispatch_scales_cm_kernel from tok_scales.
       const bool fused_scales = !a.scales_cm;
       float sc[NC];
 #pragma unroll
@@ -321,15 +321,13 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
   }
 }
 
-// fp8 row scales: recv_scales[row][b] (or [b][row] column-major) = scale of
-// the row's source token (0 for padding rows with zero padding, otherwise
-// untouched; 0 for the tail rows of fixed windows).  Launched for column-major
-// scales only; row-major scales are written by the dispatch kernel's own
-// waves.
-// Row-major: one thread per (row, block), consecutive threads walk a row's
-// blocks.  Column-major: one thread per row, walking the blocks: each thread
-// reads its token's scales contiguously and, for every block, consecutive
-// threads store to consecutive rows.
+// Column-major fp8 scales: recv_scales[b][row] = scale b of the row's source
+// token (0 for padding rows with zero padding, otherwise untouched; 0 for the
+// tail rows of fixed windows).  Row-major scales are written by the dispatch
+// kernel's own waves; this runs after it for column-major scales only.  One
+// thread per row, walking the blocks: each thread reads its token's scales
+// contiguously and, for every block, consecutive threads store to
+// consecutive rows.
 __device__ __forceinline__ void row_source(const DispatchArgs& a, int64_t pr, int& slot, int64_t& row,
                                            bool& tail) {
   tail = false;
@@ -343,24 +341,6 @@ __device__ __forceinline__ void row_source(const DispatchArgs& a, int64_t pr, in
     tail = l >= a.num_expanded[r];
     slot = tail ? -1 : a.row_slot[a.packed_base[r] + l];
   }
-}
-
-__global__ __launch_bounds__(256) void dispatch_scales_kernel(DispatchArgs a) {
-  const int nblk = a.H >> 7;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t rows = a.cap > 0 ? (int64_t)a.P * a.cap : (int64_t)a.sum_expanded;
-  if (i >= rows * nblk) return;
-  const int64_t pr = i / nblk;
-  const int b = (int)(i - pr * nblk);
-  int slot;
-  int64_t row;
-  bool tail;
-  row_source(a, pr, slot, row, tail);
-  float* dst = a.recv_scales + row * nblk + b;
-  if (slot >= 0)
-    *dst = a.tok_scales[(int64_t)(slot / a.K) * nblk + b];
-  else if (a.zero_pad || tail)
-    *dst = 0.0f;
 }
 
 __global__ __launch_bounds__(256) void dispatch_scales_cm_kernel(DispatchArgs a) {

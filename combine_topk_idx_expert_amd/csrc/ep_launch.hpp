@@ -69,16 +69,10 @@ ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
     EP_LAUNCHED("dispatch_kernel");
   }
   // row-major scales are written by the dispatch waves themselves
-  if (FP8 && a.scales_cm) {
-    const int64_t n = a.scales_cm ? out_rows : out_rows * (a.H >> 7);  // threads
-    if (n > 0) {
-      if (n >= ((int64_t)1 << 31)) return fail(EP_ERR_OVERFLOW, "scale grid too large");
-      if (a.scales_cm)
-        dispatch_scales_cm_kernel<<<(int)((n + 255) / 256), 256, 0, s>>>(a);
-      else
-        dispatch_scales_kernel<<<(int)((n + 255) / 256), 256, 0, s>>>(a);
-      EP_LAUNCHED("dispatch_scales_kernel");
-    }
+  if (FP8 && a.scales_cm && out_rows > 0) {
+    if (out_rows >= ((int64_t)1 << 31)) return fail(EP_ERR_OVERFLOW, "scale grid too large");
+    dispatch_scales_cm_kernel<<<(int)((out_rows + 255) / 256), 256, 0, s>>>(a);
+    EP_LAUNCHED("dispatch_scales_cm_kernel");
   }
   return EP_OK;
 }

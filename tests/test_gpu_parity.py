@@ -859,3 +859,57 @@ def test_fixed_windows_capture_in_a_graph():
     assert h.status() == (0, 0)
     del g
     h.free()
+
+
+def test_exact_windows_dispatch_and_combine_capture_in_a_graph():
+    """With exact windows the layout waits on the host once, so it stays outside; the
+    dispatches (bf16 fresh, fp8 cached) and the combine with a bias are captured.  Each replay
+    (new x and bias copied into the captured inputs, with eager work and synchronisations in
+    between) must match the eager calls, and the combine the oracle."""
+    w = SMALL[1]
+    topk = synth.gen_routing(w)
+    topk_d = torch.from_numpy(topk).to(DEV)
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A), topk_d)
+    wt = synth.gen_weights(w)
+    wd = torch.from_numpy(wt).to(DEV)
+    x_static = dev_bf16(synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H))
+    b_static = dev_bf16(synth.gen_bf16_rows(w.seed + 7, wl.STREAM_X, w.T, w.H))
+    R = h.total_rows
+    rx = torch.empty((R, w.H), dtype=torch.bfloat16, device=DEV)
+    rw = torch.empty(R, dtype=torch.float32, device=DEV)
+    rm = torch.empty((R, 2), dtype=torch.int32, device=DEV)
+    q8 = torch.empty((R, w.H), dtype=torch.uint8, device=DEV)
+    s8 = torch.empty((R, w.H // 128), dtype=torch.float32, device=DEV)
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        ep.dispatch(h, x_static, wd, zero_padding=True, out=(rx, None, rw, rm))
+        ep.dispatch_cached(h, x_static, fp8=True, zero_padding=True, out=(q8, s8))
+        ep.combine(h, rx, wd, bias=b_static, out=out)
+
+    step()  # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("capture exact-window dispatch + combine")
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for it in range(3):
+        xi = dev_bf16(synth.gen_bf16_rows(w.seed + 200 + it, wl.STREAM_X, w.T, w.H))
+        bi = dev_bf16(synth.gen_bf16_rows(w.seed + 300 + it, wl.STREAM_X, w.T, w.H))
+        x_static.copy_(xi)
+        b_static.copy_(bi)
+        torch.cuda.synchronize()
+        say("graph replay", it)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (rx, rw, rm, q8, s8, out)]
+        step()  # eager reference on the same inputs
+        torch.cuda.synchronize()
+        for a, b in zip(got, (rx, rw, rm, q8, s8, out)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+        np.testing.assert_array_equal(
+            host_u16(got[5]),
+            oracle.combine_identity(w.K, w.H, False, topk, host_u16(xi), wt, 0, w.T, bias=host_u16(bi)))
+    del g
+    h.free()
