@@ -77,7 +77,9 @@ struct ep_handle {
   int64_t* tail_base;
   float* tok_scales = nullptr;  // fp8 per-token scales (H % 128 == 0 only)
   int64_t* summary_dev;
-  int64_t* summary_host = nullptr;  // pinned
+  int64_t* summary_host = nullptr;      // pinned; the finalize kernel writes it directly
+  int64_t* summary_host_dev = nullptr;  // its device address
+  int64_t layout_seq = 0;               // sequence number of the last enqueued layout
   hipEvent_t done = nullptr;        // end of the last layout's work
   hipEvent_t summary_ready = nullptr;  // the last layout's host summary has landed
   size_t lds_count, lds_scan, lds_finalize, lds_rank;
@@ -177,8 +179,12 @@ ep_status allocate(ep_handle* h) {
     *it.ptr = (uint8_t*)h->arena + off;
     off += align_up(std::max<size_t>(it.bytes, 1));
   }
-  e = hipHostMalloc((void**)&h->summary_host, (size_t)((kSummaryHeader + 3 * P + 1) * 8), hipHostMallocDefault);
+  e = hipHostMalloc((void**)&h->summary_host, (size_t)((kSummaryHeader + 3 * P + 2) * 8),
+                    hipHostMallocMapped | hipHostMallocCoherent);
   if (e != hipSuccess) return fail(EP_ERR_NOMEM, "hipHostMalloc: %s", hipGetErrorString(e));
+  std::memset(h->summary_host, 0, (size_t)((kSummaryHeader + 3 * P + 2) * 8));
+  e = hipHostGetDevicePointer((void**)&h->summary_host_dev, h->summary_host, 0);
+  if (e != hipSuccess) return fail(EP_ERR_HIP, "hipHostGetDevicePointer: %s", hipGetErrorString(e));
   e = hipEventCreateWithFlags(&h->summary_ready, hipEventDisableTiming);
   if (e != hipSuccess) return fail(EP_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
   e = hipEventCreateWithFlags(&h->done, hipEventDisableTiming);
@@ -210,6 +216,25 @@ void release(ep_handle* h) {
   delete h;
 }
 
+// Wait until the last enqueued layout's finalize kernel has written the host
+// summary: spin on the sequence number it writes last (coherent pinned
+// memory), asking the event now and then, so that a stream that fails or has
+// already passed the kernel also ends the wait.
+ep_status wait_summary(ep_handle* h) {
+  int64_t* flag = h->summary_host + kSummaryHeader + 3 * h->dims.P + 1;
+  for (uint32_t i = 1;; ++i) {
+    if (__atomic_load_n(flag, __ATOMIC_ACQUIRE) == h->layout_seq) return EP_OK;
+    if ((i & 255) == 0) {
+      const hipError_t e = hipEventQuery(h->summary_ready);
+      if (e == hipSuccess) break;
+      if (e != hipErrorNotReady) return fail(EP_ERR_HIP, "layout: %s", hipGetErrorString(e));
+    }
+  }
+  if (__atomic_load_n(flag, __ATOMIC_ACQUIRE) != h->layout_seq)
+    return fail(EP_ERR_HIP, "layout finished without publishing its summary");
+  return EP_OK;
+}
+
 // Enqueue the layout for the handle's config and read back the summary.
 ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64_t* total_rows) {
   h->valid = false;
@@ -225,12 +250,10 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
   EP_LAUNCHED("layout_scan_kernel");
   FinalizeOut fo{h->n_e, h->expert_offset, h->num_expanded, h->window_row_base, h->num_recv,
                  h->recv_src_base, h->pad_base, h->pad_rows, h->packed_base, h->row_slot, h->tail_base,
-                 h->summary_dev};
+                 h->summary_dev, h->summary_host_dev, ++h->layout_seq};
   layout_finalize_kernel<<<1, kFinalizeThreads, h->lds_finalize, s>>>(d, h->col_total, fo);
   EP_LAUNCHED("layout_finalize_kernel");
-  EP_HIP(hipMemcpyAsync(h->summary_host, h->summary_dev, (size_t)(kSummaryHeader + 3 * d.P + 1) * 8,
-                        hipMemcpyDeviceToHost, s));
-  EP_HIP(hipEventRecord(h->summary_ready, s));
+  EP_HIP(hipEventRecord(h->summary_ready, s));  // the finalize kernel wrote the host summary
   {
     // at least one workgroup per expert, so that the padding rows are written even when T = 0
     RankOut ro{h->dst_slot, h->dst_row, h->row_slot, h->send_head, h->recv_src_idx, h->pad_rows};
@@ -249,7 +272,7 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
   }
   // The host needs only the summary; the rank kernel keeps running meanwhile,
   // so the caller's next launches queue up behind it without a gap.
-  EP_HIP(hipEventSynchronize(h->summary_ready));
+  if (ep_status st = wait_summary(h); st != EP_OK) return st;
   const int64_t* sm = h->summary_host;
   if (sm[2] != 0) return fail(EP_ERR_ROUTING, "topk_idx holds an expert id outside {-1} U [0, %d)", d.E);
   if (sm[0] >= ((int64_t)1 << 31))
@@ -272,7 +295,7 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
 ep_status ensure_counts(const ep_handle* hc) {
   ep_handle* h = const_cast<ep_handle*>(hc);
   if (h->counts_known) return EP_OK;
-  EP_HIP(hipEventSynchronize(h->summary_ready));
+  if (ep_status st = wait_summary(h); st != EP_OK) return st;
   const int64_t* sm = h->summary_host;
   h->total_pad = sm[1];
   h->sum_recv = sm[3];

@@ -270,8 +270,16 @@ struct FinalizeOut {
   int64_t* packed_base;     // [P+1] windows laid end to end (row_slot index space)
   int32_t* row_slot;        // [sum num_expanded] source slot u*K+j of each row, -1 padding
   int64_t* tail_base;       // [P+1] fixed windows: prefix of the tail row counts
-  int64_t* summary;         // host summary, see above
+  int64_t* summary;         // summary, see above (device copy, read by later kernels)
+  int64_t* summary_host;    // the same, written straight into pinned host memory,
+                            // followed by [7+3P] = seq, written last
+  int64_t seq;              // the layout's sequence number (the host waits for it)
 };
+
+__device__ __forceinline__ void put_summary(const FinalizeOut& o, int i, int64_t v) {
+  o.summary[i] = v;
+  o.summary_host[i] = v;
+}
 
 // LDS: g[E+1] int64 (global prefix of aligned sizes) | pad_base[E+1] int32 |
 //      wave sums [16] int64 | column totals [E+P+1] int32
@@ -337,7 +345,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
   for (int r = tid; r < d.P; r += kFinalizeThreads) {
     const int64_t ne = g[(r + 1) * d.El] - g[r * d.El];
     o.num_expanded[r] = ne;
-    o.summary[kSummaryHeader + r] = ne;
+    put_summary(o, kSummaryHeader + r, ne);
     my_max = ne > my_max ? ne : my_max;
   }
   for (int e = tid; e <= d.E; e += kFinalizeThreads) o.pad_base[e] = pb[e];
@@ -356,7 +364,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
     const int64_t base = d.cap > 0 ? (int64_t)r * d.cap : d.symmetric ? (int64_t)r * wmax : g[min(r, d.P) * d.El];
     o.window_row_base[r] = base;
     o.packed_base[r] = g[r * d.El];
-    o.summary[kSummaryHeader + 2 * d.P + r] = base;
+    put_summary(o, kSummaryHeader + 2 * d.P + r, base);
   }
   for (int x = tid; x < d.P * (d.El + 1); x += kFinalizeThreads) {
     const int r = x / (d.El + 1), l = x - r * (d.El + 1);
@@ -373,16 +381,16 @@ __global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
     if (r < d.P) {
       o.num_recv[r] = (int32_t)nr;
       o.recv_src_base[r] = carry_r + xr;
-      o.summary[kSummaryHeader + d.P + r] = nr;
+      put_summary(o, kSummaryHeader + d.P + r, nr);
     }
     carry_r += tr;
   }
   if (tid == 0) {
     o.recv_src_base[d.P] = carry_r;
-    o.summary[0] = d.cap > 0 ? (int64_t)d.P * d.cap : d.symmetric ? (int64_t)d.P * wmax : g[d.E];
-    o.summary[1] = pb[d.E];
-    o.summary[2] = col_total[d.E + d.P];
-    o.summary[3] = carry_r;
+    put_summary(o, 0, d.cap > 0 ? (int64_t)d.P * d.cap : d.symmetric ? (int64_t)d.P * wmax : g[d.E]);
+    put_summary(o, 1, pb[d.E]);
+    put_summary(o, 2, col_total[d.E + d.P]);
+    put_summary(o, 3, carry_r);
   }
 
   // fixed windows: tail rows [min(ne, cap), cap) of each window, and the rows
@@ -404,8 +412,16 @@ __global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
   }
   if (tid == 0) {
     o.tail_base[d.P] = carry_t;
-    o.summary[4] = carry_t;
-    o.summary[5] = carry_d;
+    put_summary(o, 4, carry_t);
+    put_summary(o, 5, carry_d);
+  }
+  // Publish: every thread's summary writes reach the host before the sequence
+  // number that the host spins on.
+  __threadfence_system();
+  __syncthreads();
+  if (tid == 0) {
+    o.summary_host[kSummaryHeader + 3 * d.P + 1] = o.seq;
+    __threadfence_system();
   }
 
 }
