@@ -167,19 +167,36 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _require(t, dtype, shape, name):
+def _require(t, dtype, shape, name, device=None):
+    """Every tensor handed to the library is checked here: the C ABI takes bare
+    pointers, so a wrong size or device would only show up as a memory fault."""
     import torch
 
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the handle on {device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _require_recv(h, recv_x, recv_scales, fp8: bool, scales_col_major: bool):
+    """Caller-provided expanded outputs: [total_rows, H] payload and, for fp8, the scales."""
+    import torch
+
+    H, R = h.cfg.H, h.total_rows
+    _require(recv_x, torch.uint8 if fp8 else torch.bfloat16, (R, H), "recv_x", h.device)
+    if fp8:
+        if recv_scales is None:
+            raise ValueError("recv_scales is required for fp8 output")
+        shape = (H // 128, R) if scales_col_major else (R, H // 128)
+        _require(recv_scales, torch.float32, shape, "recv_scales", h.device)
 
 
 class Handle:
@@ -329,7 +346,7 @@ def relayout(h: Handle, topk_idx) -> Handle:
     """ep_relayout: new routing for an existing handle of the same config (no allocation)."""
     import torch
 
-    _require(topk_idx, torch.int64, (h.cfg.T, h.cfg.K), "topk_idx")
+    _require(topk_idx, torch.int64, (h.cfg.T, h.cfg.K), "topk_idx", h.device)
     rows = ctypes.c_int64()
     with torch.cuda.device(topk_idx.device):
         _check(lib().ep_relayout(h.ptr, _ptr(topk_idx), _stream(topk_idx.device), ctypes.byref(rows)))
@@ -360,10 +377,10 @@ def _input(h: Handle, x):
     cfg = h.cfg
     if isinstance(x, tuple):
         codes, scales = x
-        _require(codes, torch.uint8, (cfg.T, cfg.H), "x codes")
-        _require(scales, torch.float32, (cfg.T, cfg.H // 128), "x scales")
+        _require(codes, torch.uint8, (cfg.T, cfg.H), "x codes", h.device)
+        _require(scales, torch.float32, (cfg.T, cfg.H // 128), "x scales", h.device)
         return codes, scales, codes.device
-    _require(x, torch.bfloat16, (cfg.T, cfg.H), "x")
+    _require(x, torch.bfloat16, (cfg.T, cfg.H), "x", h.device)
     return x, None, x.device
 
 
@@ -382,13 +399,16 @@ def dispatch(h: Handle, x, topk_weights, fp8: bool = False, zero_padding: bool =
     cfg = h.cfg
     xin, xs, device = _input(h, x)
     fp8 = fp8 or xs is not None
-    _require(topk_weights, torch.float32, (cfg.T, cfg.K), "topk_weights")
+    _require(topk_weights, torch.float32, (cfg.T, cfg.K), "topk_weights", h.device)
     if out is None:
         recv_x, recv_scales = _alloc_recv(h, fp8, device, scales_col_major)
         recv_w = torch.empty(h.total_rows, dtype=torch.float32, device=device)
         recv_meta = torch.empty((h.total_rows, 2), dtype=torch.int32, device=device)
     else:
         recv_x, recv_scales, recv_w, recv_meta = out
+        _require_recv(h, recv_x, recv_scales, fp8, scales_col_major)
+        _require(recv_w, torch.float32, (h.total_rows,), "recv_weights", h.device)
+        _require(recv_meta, torch.int32, (h.total_rows, 2), "recv_src_meta", h.device)
     flags = _flags(fp8, zero_padding, scales_col_major)
 
     def launch():
@@ -416,7 +436,11 @@ def dispatch_cached(h: Handle, x, fp8: bool = False, zero_padding: bool = False,
 
     xin, xs, device = _input(h, x)
     fp8 = fp8 or xs is not None
-    recv_x, recv_scales = _alloc_recv(h, fp8, device, scales_col_major) if out is None else out
+    if out is None:
+        recv_x, recv_scales = _alloc_recv(h, fp8, device, scales_col_major)
+    else:
+        recv_x, recv_scales = out
+        _require_recv(h, recv_x, recv_scales, fp8, scales_col_major)
     flags = _flags(fp8, zero_padding, scales_col_major)
 
     def launch():
@@ -441,13 +465,15 @@ def combine(h: Handle, y, topk_weights=None, bias=None, out=None, async_with_com
     import torch
 
     cfg = h.cfg
-    _require(y, torch.bfloat16, (h.total_rows, cfg.H), "y")
+    _require(y, torch.bfloat16, (h.total_rows, cfg.H), "y", h.device)
     if topk_weights is not None:
-        _require(topk_weights, torch.float32, (cfg.T, cfg.K), "topk_weights")
+        _require(topk_weights, torch.float32, (cfg.T, cfg.K), "topk_weights", h.device)
     if bias is not None:
-        _require(bias, torch.bfloat16, (cfg.T, cfg.H), "bias")
+        _require(bias, torch.bfloat16, (cfg.T, cfg.H), "bias", h.device)
     if out is None:
         out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=y.device)
+    else:
+        _require(out, torch.bfloat16, (cfg.T, cfg.H), "out", h.device)
 
     def launch():
         with torch.cuda.device(y.device):
@@ -476,5 +502,7 @@ def debug_copy(dst, src):
     n = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != n or not (src.is_cuda and dst.is_cuda):
         raise ValueError("dst and src must be device tensors of the same byte size")
+    if not (src.is_contiguous() and dst.is_contiguous()) or src.device != dst.device:
+        raise ValueError("dst and src must be contiguous and on one device")
     _check(lib().ep_debug_copy(_ptr(dst), _ptr(src), n, _stream(src.device)))
     return dst

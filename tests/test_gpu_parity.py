@@ -913,3 +913,42 @@ def test_exact_windows_dispatch_and_combine_capture_in_a_graph():
             oracle.combine_identity(w.K, w.H, False, topk, host_u16(xi), wt, 0, w.T, bias=host_u16(bi)))
     del g
     h.free()
+
+
+def test_binding_rejects_wrong_output_tensors():
+    """The C ABI takes bare pointers, so the binding checks every caller-provided tensor
+    (dtype, shape, contiguity, device) before anything is launched."""
+    w = D["tiny-p4-s64-e16-k2-h512"]
+    topk_d = torch.from_numpy(synth.gen_routing(w)).to(DEV)
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A), topk_d)
+    R = h.total_rows
+    xd = dev_bf16(synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H))
+    wd = torch.from_numpy(synth.gen_weights(w)).to(DEV)
+    good = (torch.empty((R, w.H), dtype=torch.bfloat16, device=DEV), None,
+            torch.empty(R, dtype=torch.float32, device=DEV), torch.empty((R, 2), dtype=torch.int32, device=DEV))
+    bad_cases = [
+        ((torch.empty((R - 1, w.H), dtype=torch.bfloat16, device=DEV),) + good[1:], ValueError),  # one row short
+        ((torch.empty((R, w.H), dtype=torch.float16, device=DEV),) + good[1:], TypeError),
+        ((torch.empty((w.H, R), dtype=torch.bfloat16, device=DEV).T,) + good[1:], ValueError),  # not contiguous
+        (good[:2] + (torch.empty(R - 1, dtype=torch.float32, device=DEV), good[3]), ValueError),
+        (good[:3] + (torch.empty((R, 3), dtype=torch.int32, device=DEV),), ValueError),
+        ((good[0].cpu(),) + good[1:], ValueError),
+    ]
+    for out, exc in bad_cases:
+        with pytest.raises(exc):
+            ep.dispatch(h, xd, wd, zero_padding=True, out=out)
+    # fp8: scales required, in the layout the flags ask for
+    q8 = torch.empty((R, w.H), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        ep.dispatch(h, xd, wd, fp8=True, out=(q8, None, good[2], good[3]))
+    with pytest.raises(ValueError):
+        ep.dispatch_cached(h, xd, fp8=True, scales_col_major=True,
+                           out=(q8, torch.empty((R, w.H // 128), dtype=torch.float32, device=DEV)))
+    with pytest.raises(ValueError):
+        ep.combine(h, good[0], wd, out=torch.empty((w.T - 1, w.H), dtype=torch.bfloat16, device=DEV))
+    # and the well-formed call still works
+    rx, _, _, _ = ep.dispatch(h, xd, wd, zero_padding=True, out=good)
+    out = ep.combine(h, rx, wd)
+    torch.cuda.synchronize()
+    assert out.shape == (w.T, w.H)
+    h.free()
