@@ -144,7 +144,13 @@ def cpu_baseline(w, topk, x, wt, budget_s: float = 12.0, max_steps: int = 5) -> 
         del rx
     total = time.perf_counter() - t_start
     step = statistics.median(sum(s) for s in steps)
-    return {"value": T / step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": T / step, "unit": "tokens/s", "cores": 1, "kind": "oracle", "cpu_model": cpu_model,
             "sample": (f"the whole step on the full workload ({T} tokens, {rows} expanded rows: layout, "
                        f"dispatch of every row, combine of every token), {len(steps)} repetitions in "
                        f"{total:.1f} s, median step; single thread"),
