@@ -47,10 +47,17 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
-                os.path.getmtime(_SRC), os.path.getmtime(_HDR)):
-            build(force=True)
-        L = ctypes.CDLL(_LIB_PATH)
+        # EP_ORACLE_LIB: load another build of oracle.c instead (the planted-mistake
+        # builds of tests/test_oracle_mutants.py); nothing else sets it
+        override = os.environ.get("EP_ORACLE_LIB")
+        if override:
+            path = override
+        else:
+            path = _LIB_PATH
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
+                    os.path.getmtime(_SRC), os.path.getmtime(_HDR)):
+                build(force=True)
+        L = ctypes.CDLL(path)
         P_ = ctypes.c_void_p
         i32, i64 = ctypes.c_int, ctypes.c_int64
         L.oracle_layout.argtypes = [i32] * 6 + [P_] * 14

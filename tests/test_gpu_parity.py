@@ -952,3 +952,35 @@ def test_binding_rejects_wrong_output_tensors():
     torch.cuda.synchronize()
     assert out.shape == (w.T, w.H)
     h.free()
+
+
+@pytest.mark.parametrize("H", [8, 4104], ids=["lds-kernel", "register-kernel"])
+def test_combine_arithmetic_order_on_adversarial_values(H):
+    """Values for which another summation order, a fused multiply-add, or adding the bias
+    first changes the bf16 result (the oracle's pins derive each expected value by hand):
+    both combine kernels must give exactly these."""
+    B = float(np.float32(2.0**25 + 2.0**17))
+    cases = [  # (weights, y row bits per slot, bias bits or None, expected out bits)
+        ([B, 1.0, 1.0, 1.0], None, None, 0x4C00),
+        ([1.0, 1.0, 1.0, B], None, None, 0x4C01),
+        ([-(1.0 + 2.0**-7 + 2.0**-23), 1.0 + 2.0**-23], [0x3F80, 0x3F81], None, 0x0000),
+        ([1.0, 1.0, B], None, 0x3F80, 0x4C00),
+    ]
+    for weights, rows, bias, expect in cases:
+        K = len(weights)
+        topk = np.arange(K, dtype=np.int64)[None, :]
+        h = ep.get_layout(ep.Config(1, 1, H, K, K, 1), torch.from_numpy(topk).to(DEV))
+        assert h.total_rows == K
+        rows = [0x3F80] * K if rows is None else rows
+        y = np.repeat(np.asarray(rows, np.uint16)[:, None], H, 1)
+        wd = torch.tensor([weights], dtype=torch.float32, device=DEV)
+        bd = None if bias is None else dev_bf16(np.full((1, H), bias, np.uint16))
+        say("adversarial combine", H, K, expect)
+        out = ep.combine(h, dev_bf16(y), wd, bias=bd)
+        torch.cuda.synchronize()
+        got = host_u16(out)
+        assert np.all(got == expect), (weights, hex(int(got[0, 0])), hex(expect))
+        lay = oracle.layout(1, 1, K, K, 1, topk)
+        np.testing.assert_array_equal(got, oracle.combine_general(
+            lay, H, y, np.asarray([weights], np.float32), bias=None if bias is None else np.full((1, H), bias, np.uint16)))
+        h.free()

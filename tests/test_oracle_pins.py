@@ -550,7 +550,8 @@ def test_fixed_length_is_exact_window_plus_tail(fp8, zero_padding):
 
 
 @pytest.mark.parametrize("A", [1, 8])
-def test_fixed_length_truncation_drops_tail_rows_and_their_slots(A):
+@pytest.mark.parametrize("which", ["median", "small"])
+def test_fixed_length_truncation_drops_tail_rows_and_their_slots(A, which):
     """A capacity below some window's row count publishes the first W rows of each window;
     the dropped count is sum_d max(0, num_expanded[d] - W) (num_expanded from its closed
     form); combine then equals the exact combine with the dropped slots' weights zeroed."""
@@ -558,8 +559,12 @@ def test_fixed_length_truncation_drops_tail_rows_and_their_slots(A):
     topk = synth.gen_routing(w)
     n = np.bincount(topk[topk >= 0], minlength=w.E)
     ne = (-(-n // A) * A).reshape(w.P, -1).sum(1)
-    W = int(np.sort(ne)[w.P // 2])  # about half the windows overflow
-    assert (ne > W).any() and (ne < W).any()
+    if which == "median":
+        W = int(np.sort(ne)[w.P // 2])  # about half the windows overflow
+        assert (ne > W).any() and (ne < W).any()
+    else:
+        W = max(1, int(ne.min()) // 2)  # every window overflows, the first ones too: a row
+        assert (ne > W).all()            # index reaching W must not land in the next window
     lay, x, wt, (erx, _, erw, emeta), (frx, _, frw, fmeta, dropped) = _exact_and_fixed(
         w, topk, W, False, True, 34)
     assert dropped == int(np.maximum(ne - W, 0).sum())
@@ -685,3 +690,53 @@ def test_combine_bias_general_within_one_ulp():
     assert d.max() <= 1 and (d == 0).mean() > 0.99
     # a dropped bias term is caught
     assert (bf16_ulp_diff(out, oracle.combine_general(lay, w.H, y, wt)) > 1).mean() > 0.5
+
+
+# --------------------------------------------------------------------------
+# Combine arithmetic order, pinned by values chosen so that another order
+# (or a fused multiply-add) changes the bf16 result, not just the last fp32 bit.
+# --------------------------------------------------------------------------
+
+_B = float(np.float32(2.0**25 + 2.0**17))  # exactly halfway between bf16 2^25 and 2^25 + 2^18
+
+
+def _one_token_combine(weights, y_rows=None, bias=None):
+    """One token whose K slots go to K distinct experts (P = 1, A = 1, so expert k owns row k);
+    y row k is y_rows[k] (bf16 bits, default 1.0) across 8 channels; returns out[0][0]."""
+    K = len(weights)
+    topk = np.arange(K, dtype=np.int64)[None, :]
+    lay = oracle.layout(1, 1, K, K, 1, topk)
+    H = 8
+    rows = [0x3F80] * K if y_rows is None else list(y_rows)
+    y = np.repeat(np.asarray(rows, np.uint16)[:, None], H, 1)
+    w = np.asarray(weights, np.float32)[None, :]
+    b = None if bias is None else np.full((1, H), bias, np.uint16)
+    return int(oracle.combine_general(lay, H, y, w, bias=b)[0, 0])
+
+
+def test_combine_slot_order_is_ascending():
+    """From acc = +0 the slots are added in order j = 0..K-1.  With w = (B, 1, 1, 1) on unit
+    rows each +1 is lost against B (fp32 spacing 4 there, B even), so the sum stays at B, a
+    bf16 tie, which rounds to even: 2^25 (0x4C00).  The same terms in the order (1, 1, 1, B)
+    reach 3 + B -> B + 4 and round up to 2^25 + 2^18 (0x4C01)."""
+    assert _one_token_combine([_B, 1.0, 1.0, 1.0]) == 0x4C00
+    assert _one_token_combine([1.0, 1.0, 1.0, _B]) == 0x4C01
+
+
+def test_combine_multiplies_and_adds_separately():
+    """acc = fl(acc + fl(w * y)), no fused multiply-add.  w0 = -(1 + 2^-7 + 2^-23) on y0 = 1,
+    then w1 = 1 + 2^-23 on y1 = 1 + 2^-7: the product 1 + 2^-7 + 2^-23 + 2^-30 rounds to
+    1 + 2^-7 + 2^-23 and cancels acc exactly, giving +0.  A fused multiply-add would keep
+    2^-30 (bf16 0x3080)."""
+    w0 = -(1.0 + 2.0**-7 + 2.0**-23)
+    w1 = 1.0 + 2.0**-23
+    assert np.float32(w0) == w0 and np.float32(w1) == w1
+    assert _one_token_combine([w0, w1], y_rows=[0x3F80, 0x3F81]) == 0x0000
+
+
+def test_combine_bias_is_added_after_the_slots():
+    """With w = (1, 1, B) on unit rows and a bias of 1: (1 + 1) + B = B + 2 -> B (ties to even),
+    then + 1 -> B, the bf16 tie that rounds to 2^25 (0x4C00).  Adding the bias before the slots
+    would give 1 + 1 + 1 + B -> B + 4, which rounds up (0x4C01)."""
+    assert _one_token_combine([1.0, 1.0, _B], bias=0x3F80) == 0x4C00
+    assert _one_token_combine([1.0, 1.0, 1.0, _B]) == 0x4C01  # the bias-first sum, for contrast
