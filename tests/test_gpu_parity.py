@@ -164,11 +164,26 @@ def test_relayout_reuses_handle():
 DISPATCH_CASES = [w for w in SMALL if w.T > 0]
 
 
+def _fp8_needs_hidden_multiple_of_128(w, W):
+    """fp8 output has one scale per 128 channels, so a hidden size that is not a multiple of
+    128 must be refused (EP_ERR_SHAPE) before anything is launched, fresh and cached."""
+    topk_d = torch.from_numpy(synth.gen_routing(w)).to(DEV)
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A, num_worst_rows=W), topk_d)
+    xd = dev_bf16(synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H))
+    wd = torch.from_numpy(synth.gen_weights(w)).to(DEV)
+    for call in (lambda: ep.dispatch(h, xd, wd, fp8=True), lambda: ep.dispatch_cached(h, xd, fp8=True)):
+        with pytest.raises(ep.EpError) as ei:
+            call()
+        assert ei.value.status == ep.Status.ERR_SHAPE
+    h.free()
+
+
 @pytest.mark.parametrize("w", DISPATCH_CASES, ids=lambda w: w.name)
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
 def test_dispatch_and_combine_small(w, fp8):
     if fp8 and w.H % 128:
-        pytest.skip("fp8 needs H % 128 == 0")
+        _fp8_needs_hidden_multiple_of_128(w, 0)
+        return
     topk = routing_with_holes(w, 12)
     x = synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H)
     x[:3, :128] = 0  # an all-zero 128-channel block (amax == 0)
@@ -413,7 +428,8 @@ FIXED_CASES = [SMALL[0], SMALL[1], SMALL[2], SMALL[4], SMALL[6], SMALL[7]]
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
 def test_fixed_windows_small(w, fit, fp8):
     if fp8 and w.H % 128:
-        pytest.skip("fp8 needs H % 128 == 0")
+        _fp8_needs_hidden_multiple_of_128(w, {"roomy": 4096, "tight": 8, "one": 1}[fit])
+        return
     topk = routing_with_holes(w, 13)
     ne = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk).num_expanded
     W = {"roomy": int(ne.max()) + 37, "tight": max(1, int(np.median(ne))), "one": 1}[fit]
