@@ -324,10 +324,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
 // Column-major fp8 scales: recv_scales[b][row] = scale b of the row's source
 // token (0 for padding rows with zero padding, otherwise untouched; 0 for the
 // tail rows of fixed windows).  Row-major scales are written by the dispatch
-// kernel's own waves; this runs after it for column-major scales only.  One
-// thread per row, walking the blocks: each thread reads its token's scales
-// contiguously and, for every block, consecutive threads store to
-// consecutive rows.
+// kernel's own waves; this runs after it for column-major scales only.
 __device__ __forceinline__ void row_source(const DispatchArgs& a, int64_t pr, int& slot, int64_t& row,
                                            bool& tail) {
   tail = false;
@@ -343,21 +340,49 @@ __device__ __forceinline__ void row_source(const DispatchArgs& a, int64_t pr, in
   }
 }
 
+// One workgroup per 64 consecutive rows, transposing through LDS 64 blocks at
+// a time: the loads read each row's scales contiguously (a row's token scales
+// are 4 * H/128 contiguous bytes), the stores write each block's 64 rows
+// contiguously.
+constexpr int kCmRows = 64;
 __global__ __launch_bounds__(256) void dispatch_scales_cm_kernel(DispatchArgs a) {
+  __shared__ float tile[kCmRows][kCmRows + 1];
+  __shared__ int64_t src_tok[kCmRows];  // source token, -1: zero, -2: untouched
+  __shared__ int64_t dst_row[kCmRows];
   const int nblk = a.H >> 7;
-  const int64_t pr = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int tid = threadIdx.x;
   const int64_t rows = a.cap > 0 ? (int64_t)a.P * a.cap : (int64_t)a.sum_expanded;
-  if (pr >= rows) return;
-  int slot;
-  int64_t row;
-  bool tail;
-  row_source(a, pr, slot, row, tail);
-  float* dst = a.recv_scales + row;
-  if (slot >= 0) {
-    const float* src = a.tok_scales + (int64_t)(slot / a.K) * nblk;
-    for (int b = 0; b < nblk; ++b) dst[(int64_t)b * a.scale_rows] = src[b];
-  } else if (a.zero_pad || tail) {
-    for (int b = 0; b < nblk; ++b) dst[(int64_t)b * a.scale_rows] = 0.0f;
+  const int64_t pr0 = (int64_t)blockIdx.x * kCmRows;
+  if (tid < kCmRows) {
+    const int64_t pr = pr0 + tid;
+    int64_t tok = -2, row = 0;
+    if (pr < rows) {
+      int slot;
+      bool tail;
+      row_source(a, pr, slot, row, tail);
+      tok = slot >= 0 ? (int64_t)(slot / a.K) : (a.zero_pad || tail) ? -1 : -2;
+    }
+    src_tok[tid] = tok;
+    dst_row[tid] = row;
+  }
+  __syncthreads();
+  for (int b0 = 0; b0 < nblk; b0 += kCmRows) {
+    // load: element (i, k) = scale b0 + k of row i; consecutive threads take consecutive k
+    for (int e = tid; e < kCmRows * kCmRows; e += 256) {
+      const int i = e / kCmRows, k = e - i * kCmRows;
+      const int64_t tok = src_tok[i];
+      float v = 0.0f;
+      if (tok >= 0 && b0 + k < nblk) v = a.tok_scales[tok * nblk + b0 + k];
+      tile[i][k] = v;
+    }
+    __syncthreads();
+    // store: element (k, i); consecutive threads take consecutive rows i
+    for (int e = tid; e < kCmRows * kCmRows; e += 256) {
+      const int k = e / kCmRows, i = e - k * kCmRows;
+      if (b0 + k < nblk && src_tok[i] != -2)
+        a.recv_scales[(int64_t)(b0 + k) * a.scale_rows + dst_row[i]] = tile[i][k];
+    }
+    __syncthreads();
   }
 }
 

@@ -71,7 +71,7 @@ ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
   // row-major scales are written by the dispatch waves themselves
   if (FP8 && a.scales_cm && out_rows > 0) {
     if (out_rows >= ((int64_t)1 << 31)) return fail(EP_ERR_OVERFLOW, "scale grid too large");
-    dispatch_scales_cm_kernel<<<(int)((out_rows + 255) / 256), 256, 0, s>>>(a);
+    dispatch_scales_cm_kernel<<<(int)((out_rows + kCmRows - 1) / kCmRows), 256, 0, s>>>(a);
     EP_LAUNCHED("dispatch_scales_cm_kernel");
   }
   return EP_OK;
