@@ -207,6 +207,7 @@ class Handle:
         self.cfg = cfg
         self.total_rows = total_rows
         self.device = device
+        self._pending = []  # completion events of async calls that read the handle
 
     @property
     def ptr(self) -> int:
@@ -215,7 +216,16 @@ class Handle:
         return self._ptr
 
     def free(self) -> None:
+        """Release the handle's device memory.  Work already enqueued with it may still read
+        it, so the device's current stream and the handle's pending async calls are waited for
+        first (also when the handle is garbage collected)."""
         if self._ptr:
+            import torch
+
+            for ev in self._pending:
+                ev.synchronize()
+            self._pending.clear()
+            torch.cuda.current_stream(self.device).synchronize()
             lib().ep_handle_free(self._ptr)
             self._ptr = None
 
@@ -304,7 +314,7 @@ def comm_stream(device):
     return _comm_streams[idx]
 
 
-def _overlapped(device, tensors, launch, previous_event):
+def _overlapped(h, device, tensors, launch, previous_event):
     """Run ``launch`` on the communication stream after ``previous_event`` (default: all
     work enqueued so far on the current stream); return an EventOverlap.  The tensors the
     call reads or writes are marked as used on the communication stream, so that torch's
@@ -324,6 +334,8 @@ def _overlapped(device, tensors, launch, previous_event):
             t.record_stream(comm)
     done = torch.cuda.Event()
     done.record(comm)
+    h._pending = [e for e in h._pending if not e.query()]
+    h._pending.append(done)  # h.free() waits for it
     return EventOverlap(done, result)
 
 
@@ -347,6 +359,13 @@ def relayout(h: Handle, topk_idx) -> Handle:
     import torch
 
     _require(topk_idx, torch.int64, (h.cfg.T, h.cfg.K), "topk_idx", h.device)
+    # the new layout overwrites the handle's arrays: order it after the async calls still
+    # reading them (a stream wait, no host synchronisation)
+    if h._pending:
+        cur = torch.cuda.current_stream(h.device)
+        for ev in h._pending:
+            cur.wait_event(ev)
+        h._pending.clear()
     rows = ctypes.c_int64()
     with torch.cuda.device(topk_idx.device):
         _check(lib().ep_relayout(h.ptr, _ptr(topk_idx), _stream(topk_idx.device), ctypes.byref(rows)))
@@ -424,7 +443,7 @@ def dispatch(h: Handle, x, topk_weights, fp8: bool = False, zero_padding: bool =
 
     if not async_with_compute_stream:
         return launch()
-    return _overlapped(device, [xin, xs, topk_weights, recv_x, recv_scales, recv_w, recv_meta], launch,
+    return _overlapped(h, device, [xin, xs, topk_weights, recv_x, recv_scales, recv_w, recv_meta], launch,
                        previous_event)
 
 
@@ -455,7 +474,7 @@ def dispatch_cached(h: Handle, x, fp8: bool = False, zero_padding: bool = False,
 
     if not async_with_compute_stream:
         return launch()
-    return _overlapped(device, [xin, xs, recv_x, recv_scales], launch, previous_event)
+    return _overlapped(h, device, [xin, xs, recv_x, recv_scales], launch, previous_event)
 
 
 def combine(h: Handle, y, topk_weights=None, bias=None, out=None, async_with_compute_stream: bool = False,
@@ -482,7 +501,7 @@ def combine(h: Handle, y, topk_weights=None, bias=None, out=None, async_with_com
 
     if not async_with_compute_stream:
         return launch()
-    return _overlapped(y.device, [y, topk_weights, bias, out], launch, previous_event)
+    return _overlapped(h, y.device, [y, topk_weights, bias, out], launch, previous_event)
 
 
 def debug_e4m3_encode(q):

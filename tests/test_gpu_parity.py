@@ -1000,3 +1000,33 @@ def test_combine_arithmetic_order_on_adversarial_values(H):
         np.testing.assert_array_equal(got, oracle.combine_general(
             lay, H, y, np.asarray([weights], np.float32), bias=None if bias is None else np.full((1, H), bias, np.uint16)))
         h.free()
+
+
+def test_relayout_and_free_wait_for_pending_async_calls():
+    """An async dispatch reads the handle on the communication stream.  A relayout enqueued
+    right after it must not overwrite the arrays under it, and free() must not release them:
+    the binding orders the relayout after the pending call and waits for it in free()."""
+    w = SMALL[1]
+    topk_a = synth.gen_routing(w)
+    topk_b = synth.gen_routing(wl.Workload(w.name, w.P, w.S, w.E, w.K, w.H, w.A, True, "uniform", seed=99))
+    x = synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    lay_a = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk_a)
+    ox, _, _, om = oracle.dispatch(lay_a, w.H, x, wt, False, True)
+    for action in ("relayout", "free"):
+        h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A), torch.from_numpy(topk_a).to(DEV))
+        say("async dispatch then", action)
+        pending = ep.dispatch(h, xd, wd, zero_padding=True, async_with_compute_stream=True)
+        if action == "relayout":
+            ep.relayout(h, torch.from_numpy(topk_b).to(DEV))
+        else:
+            h.free()
+        rx, _, _, rm = pending.wait()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_u16(rx), ox)
+        np.testing.assert_array_equal(rm.cpu().numpy(), om)
+        if action == "relayout":
+            lay_b = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk_b)
+            np.testing.assert_array_equal(h.tensor("dst_slot").cpu().numpy(), lay_b.dst_slot.reshape(-1))
+            h.free()
