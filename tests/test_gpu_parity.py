@@ -1030,3 +1030,29 @@ def test_relayout_and_free_wait_for_pending_async_calls():
             lay_b = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk_b)
             np.testing.assert_array_equal(h.tensor("dst_slot").cpu().numpy(), lay_b.dst_slot.reshape(-1))
             h.free()
+
+
+def test_column_major_fp8_calls_on_two_streams_do_not_share_scratch():
+    """fp8 dispatch with column-major scales stages per-token scales in the handle.  An async
+    call on the communication stream followed at once by a synchronous one on the current
+    stream must each keep their own scales: the binding orders the second after the first."""
+    w = SMALL[1]
+    topk = synth.gen_routing(w)
+    wt = synth.gen_weights(w)
+    wd = torch.from_numpy(wt).to(DEV)
+    x1 = synth.gen_bf16_rows(w.seed + 1, wl.STREAM_X, w.T, w.H)
+    x2 = synth.gen_bf16_rows(w.seed + 2, wl.STREAM_X, w.T, w.H)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A), torch.from_numpy(topk).to(DEV))
+    say("async col-major fp8 then sync col-major fp8")
+    pending = ep.dispatch(h, dev_bf16(x1), wd, fp8=True, zero_padding=True, scales_col_major=True,
+                          async_with_compute_stream=True)
+    r2 = ep.dispatch(h, dev_bf16(x2), wd, fp8=True, zero_padding=True, scales_col_major=True)
+    r1 = pending.wait()
+    torch.cuda.synchronize()
+    for (rx, sc, _, _), x in ((r1, x1), (r2, x2)):
+        ox, osc, _, _, _ = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=True, topk_weights=wt, x=x,
+                                                   scales_col_major=True)
+        np.testing.assert_array_equal(rx.cpu().numpy(), ox)
+        np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    h.free()
