@@ -33,6 +33,9 @@
  *    before anything is enqueued.  ep_last_error() gives a message.
  *  - One handle may be used by any number of ep_dispatch_cached / ep_combine
  *    calls; ep_handle_free and ep_relayout require that none is in flight.
+ *    One exception: fp8 dispatch with EP_DISPATCH_SCALES_COL_MAJOR (not the
+ *    pre-quantised form) stages per-token scales in the handle, so two such
+ *    calls on one handle must be ordered (one stream, or an event between).
  *  - A handle belongs to the device that was current at ep_get_layout; calls
  *    that launch work with another device current return
  *    EP_ERR_HANDLE_MISMATCH.
