@@ -158,9 +158,26 @@ def _check(status: int) -> None:
 
 
 def _stream(device) -> int:
+    """torch's current stream on ``device`` as a hipStream_t.  torch's raw accessor is used
+    when present: it skips building a Stream object (~0.2 against ~1.8 us per call)."""
     import torch
 
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None and device.index is not None:
+        return raw(device.index)
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def _on(device):
+    """``torch.cuda.device(device)``, or nothing when it is already the current device (the
+    usual case; entering the context costs ~1 us)."""
+    import contextlib
+
+    import torch
+
+    if device.index is not None and torch.cuda.current_device() == device.index:
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
 
 
 def _ptr(t) -> int | None:
@@ -359,7 +376,7 @@ def get_layout(cfg: Config, topk_idx) -> Handle:
     c = cfg._c()
     h = ctypes.c_void_p()
     rows = ctypes.c_int64()
-    with torch.cuda.device(topk_idx.device):
+    with _on(topk_idx.device):
         _check(lib().ep_get_layout(ctypes.byref(c), _ptr(topk_idx), _stream(topk_idx.device), ctypes.byref(h),
                                    ctypes.byref(rows)))
     return Handle(h.value, cfg, rows.value, topk_idx.device)
@@ -378,7 +395,7 @@ def relayout(h: Handle, topk_idx) -> Handle:
             cur.wait_event(ev)
         h._pending.clear()
     rows = ctypes.c_int64()
-    with torch.cuda.device(topk_idx.device):
+    with _on(topk_idx.device):
         _check(lib().ep_relayout(h.ptr, _ptr(topk_idx), _stream(topk_idx.device), ctypes.byref(rows)))
     h.total_rows = rows.value
     return h
@@ -442,7 +459,7 @@ def dispatch(h: Handle, x, topk_weights, fp8: bool = False, zero_padding: bool =
     flags = _flags(fp8, zero_padding, scales_col_major)
 
     def launch():
-        with torch.cuda.device(device):
+        with _on(device):
             if fp8 and scales_col_major and xs is None:
                 _after_pending_scratch_users(h, device)
             if xs is None:
@@ -476,7 +493,7 @@ def dispatch_cached(h: Handle, x, fp8: bool = False, zero_padding: bool = False,
     flags = _flags(fp8, zero_padding, scales_col_major)
 
     def launch():
-        with torch.cuda.device(device):
+        with _on(device):
             if fp8 and scales_col_major and xs is None:
                 _after_pending_scratch_users(h, device)
             if xs is None:
@@ -510,7 +527,7 @@ def combine(h: Handle, y, topk_weights=None, bias=None, out=None, async_with_com
         _require(out, torch.bfloat16, (cfg.T, cfg.H), "out", h.device)
 
     def launch():
-        with torch.cuda.device(y.device):
+        with _on(y.device):
             _check(lib().ep_combine(h.ptr, _ptr(y), _ptr(topk_weights), _ptr(bias), _ptr(out), _stream(y.device)))
         return out
 
