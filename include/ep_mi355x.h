@@ -144,7 +144,9 @@ ep_status ep_get_layout(const ep_config *cfg, const int64_t *topk_idx, void *str
  * the same config, without allocating (one long-lived buffer reused across
  * layers, TileLang tutorial ch. 38, section 2.6).  No call using `h` may be
  * in flight.  On error the handle's layout is invalid until a successful
- * ep_relayout. */
+ * ep_relayout.  Errors: EP_ERR_NULL, EP_ERR_SHAPE (misaligned topk_idx),
+ * EP_ERR_HANDLE_MISMATCH (another device is current), EP_ERR_ROUTING (exact
+ * mode), EP_ERR_OVERFLOW (symmetric windows reaching 2^31 rows), EP_ERR_HIP. */
 ep_status ep_relayout(ep_handle *h, const int64_t *topk_idx, void *stream, int64_t *total_rows);
 
 /* --------------------------------------------------------------------------
@@ -174,7 +176,9 @@ ep_status ep_relayout(ep_handle *h, const int64_t *topk_idx, void *stream, int64
  * Rows past num_expanded in symmetric windows are not touched; in fixed mode
  * they are the tail (zero payload and scales, weight 0, meta (-1, -1)) and
  * slots whose row would lie past the window are not written.
- * Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_HIP.
+ * Errors: EP_ERR_NULL, EP_ERR_SHAPE (flags, alignment, fp8 with H % 128 != 0),
+ * EP_ERR_HANDLE_MISMATCH (no valid layout, or another device is current),
+ * EP_ERR_OVERFLOW (launch grid too large), EP_ERR_HIP.
  */
 ep_status ep_dispatch(const ep_handle *h, uint32_t flags, const void *x, const float *topk_weights,
                       void *recv_x, float *recv_scales, float *recv_weights,
@@ -184,7 +188,8 @@ ep_status ep_dispatch(const ep_handle *h, uint32_t flags, const void *x, const f
  * x; only the payload (and fp8 scales) move, padding is re-zeroed when asked
  * ("Ascend DeepEP MoE Dispatch Optimization", section "Entering the real call
  * chain from the Python interface", cached dispatch; tutorial 2.4).  Its
- * payload equals ep_dispatch's for the same x and flags. */
+ * payload equals ep_dispatch's for the same x and flags.  Errors as for
+ * ep_dispatch. */
 ep_status ep_dispatch_cached(const ep_handle *h, uint32_t flags, const void *x, void *recv_x,
                              float *recv_scales, void *stream);
 
@@ -197,7 +202,7 @@ ep_status ep_dispatch_cached(const ep_handle *h, uint32_t flags, const void *x, 
  * The output is fp8 whatever EP_DISPATCH_FP8 says: every valid row gets its
  * token's bytes and scales; everything else is as in ep_dispatch /
  * ep_dispatch_cached (padding, tails, metadata, EP_DISPATCH_SCALES_COL_MAJOR).
- * H % 128 == 0.  Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_HIP. */
+ * H % 128 == 0.  Errors as for ep_dispatch. */
 ep_status ep_dispatch_prequant(const ep_handle *h, uint32_t flags, const uint8_t *x_codes,
                                const float *x_scales, const float *topk_weights, void *recv_x,
                                float *recv_scales, float *recv_weights, int32_t *recv_src_meta,
@@ -224,7 +229,9 @@ ep_status ep_dispatch_prequant_cached(const ep_handle *h, uint32_t flags, const 
  * whose row was dropped counts as unused.
  * The backward of dispatch is this call and the backward of combine is
  * ep_dispatch_cached, with the same handle (tutorial 2.3).
- * Errors: EP_ERR_NULL, EP_ERR_HIP.
+ * Errors: EP_ERR_NULL, EP_ERR_SHAPE (alignment), EP_ERR_HANDLE_MISMATCH (no
+ * valid layout, or another device is current), EP_ERR_OVERFLOW (launch grid
+ * too large), EP_ERR_HIP.
  */
 ep_status ep_combine(const ep_handle *h, const void *y, const float *topk_weights, const void *bias,
                      void *out, void *stream);
