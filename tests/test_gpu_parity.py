@@ -161,6 +161,71 @@ def test_relayout_reuses_handle():
     h.free()
 
 
+
+SEQ = wl.Workload("seq-p8-s100-e32-k4", 8, 100, 32, 4, 256, 8, True, "uniform", seed=11)
+
+
+def _routing_sequence(w):
+    """Routings of very different shapes on one config, ordered so that state left
+    over from one layout (padding lists, counters, status flags) would show in the next."""
+    T, K, E = w.T, w.K, w.E
+    one = np.full((T, K), -1, np.int64)
+    one[:, 0] = 0  # every token to expert 0: one full window, all others empty
+    none = np.full((T, K), -1, np.int64)  # no valid slot at all: zero expanded rows
+    dup = np.full((T, K), E - 1, np.int64)  # K copies of the last expert in every token
+    return [("uniform", synth.gen_routing(w)), ("one-expert", one),
+            ("uniform-2", synth.gen_routing(synth.scaled(w, seed=w.seed + 77))), ("none", none),
+            ("duplicates", dup), ("holes", routing_with_holes(w, 21)), ("uniform-again", synth.gen_routing(w))]
+
+
+@pytest.mark.parametrize("fixed", [False, True], ids=["exact", "fixed"])
+def test_relayout_sequence_leaves_no_stale_state(fixed):
+    """One handle, relaid out for each routing in turn; after every relayout the layout,
+    a fresh dispatch (bf16 then fp8, zero padding) and a combine match the oracle.  In
+    fixed mode W = 512 rows per window: the one-expert and duplicate routings overflow
+    a window and report truncation, and the routings after them must clear it."""
+    w = SEQ
+    x = synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    seq = _routing_sequence(w)
+    W = 512 if fixed else 0
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A, num_worst_rows=W), torch.from_numpy(seq[0][1]).to(DEV))
+    for i, (name, topk) in enumerate(seq):
+        say("relayout sequence", "fixed" if fixed else "exact", i, name)
+        ep.relayout(h, torch.from_numpy(topk).to(DEV))
+        torch.cuda.synchronize()
+        lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+        if fixed:
+            check_fixed_layout(lay, h, W)
+            exp_drop = int(np.maximum(lay.num_expanded - W, 0).sum())
+            assert h.status() == (ep.STATUS_TRUNCATED if exp_drop else 0, exp_drop), name
+            R = w.P * W
+        else:
+            check_layout(lay, h)
+            assert h.status() == (0, 0)
+            R = lay.total_rows
+        fp8 = i % 2 == 1
+        rx, sc, rw, rm = ep.dispatch(h, xd, wd, fp8=fp8, zero_padding=True)
+        torch.cuda.synchronize()
+        if fixed:
+            ox, osc, ow, om, _ = oracle.dispatch_fixed(lay, w.H, W, x, wt, fp8, True)
+        else:
+            ox, osc, ow, om = oracle.dispatch(lay, w.H, x, wt, fp8, True)
+        assert rx.shape[0] == R
+        np.testing.assert_array_equal(rx.cpu().numpy() if fp8 else host_u16(rx), ox, err_msg=name)
+        np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ow.view(np.uint32), err_msg=name)
+        np.testing.assert_array_equal(rm.cpu().numpy(), om, err_msg=name)
+        if fp8:
+            np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32), err_msg=name)
+        y = synth.gen_expert_out(w, R)
+        out = ep.combine(h, dev_bf16(y), wd)
+        torch.cuda.synchronize()
+        exp = oracle.combine_fixed(lay, w.H, W, y, wt) if fixed else oracle.combine(lay, w.H, y, wt)
+        np.testing.assert_array_equal(host_u16(out), exp, err_msg=name)
+    h.free()
+
+
 DISPATCH_CASES = [w for w in SMALL if w.T > 0]
 
 
