@@ -866,6 +866,64 @@ def test_symmetric_windows_dispatch_and_combine(fp8):
     h.free()
 
 
+
+def test_symmetric_windows_fp8_variants():
+    """Symmetric windows with the fp8 variants: fused quantisation or pre-quantised input,
+    row- or column-major scales, with and without zero padding, fresh then cached.  The
+    column-major scales pass maps packed rows to window rows by its own search over the
+    window bases; rows past each window's num_expanded must stay untouched."""
+    w = SMALL[2]  # 128 ranks, Zipf: very uneven windows
+    topk = routing_with_holes(w, 23)
+    lay, h = layout_both(w, topk, symmetric=True)
+    check_layout(lay, h)
+    R, nb = h.total_rows, w.H // 128
+    x = synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    rng = np.random.default_rng(24)
+    codes = rng.integers(0, 256, (w.T, w.H), dtype=np.uint8)
+    scales = rng.standard_normal((w.T, nb)).astype(np.float32)
+    used = np.zeros(R, bool)
+    for d in range(w.P):
+        b = int(lay.window_row_base[d])
+        used[b:b + int(lay.num_expanded[d])] = True
+    for src in ("fused", "prequant"):
+        xin = xd if src == "fused" else (_dev_u8(codes), torch.from_numpy(scales).to(DEV))
+        kw = dict(x=x) if src == "fused" else dict(x_codes=codes, x_scales=scales)
+        for cm in (False, True):
+            for zp in (False, True):
+                say("symmetric fp8 variant", src, "col-major" if cm else "row-major", "zp" if zp else "")
+                rx = torch.full((R, w.H), 0x7F, dtype=torch.uint8, device=DEV)
+                sc = torch.full((nb, R) if cm else (R, nb), float("nan"), dtype=torch.float32, device=DEV)
+                rw = torch.full((R,), float("nan"), dtype=torch.float32, device=DEV)
+                rm = torch.full((R, 2), 77, dtype=torch.int32, device=DEV)
+                ep.dispatch(h, xin, wd, fp8=True, zero_padding=zp, scales_col_major=cm, out=(rx, sc, rw, rm))
+                torch.cuda.synchronize()
+                ox, osc, ow, om, _ = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=zp, topk_weights=wt,
+                                                             scales_col_major=cm, fill=0x7F, **kw)
+                np.testing.assert_array_equal(rx.cpu().numpy(), ox)
+                gm = rm.cpu().numpy()
+                np.testing.assert_array_equal(gm[used], om[used])
+                assert np.all(gm[~used] == 77)
+                np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32)[used], ow.view(np.uint32)[used])
+                written = used & ((om[:, 0] >= 0) | zp)  # rows whose scales dispatch writes
+                gs = sc.cpu().numpy()
+                gs_rows, os_rows = (gs.T, osc.T) if cm else (gs, osc)
+                np.testing.assert_array_equal(gs_rows[written].view(np.uint32), os_rows[written].view(np.uint32))
+                assert np.all(np.isnan(gs_rows[~written]))
+                # cached dispatch of the same input reproduces payload and scales
+                cx = rx.clone()
+                wmask = torch.from_numpy(written).to(DEV)
+                cx[wmask] = 0x55
+                csc = sc.clone()
+                (csc.T if cm else csc)[wmask] = 3.0
+                ep.dispatch_cached(h, xin, fp8=True, zero_padding=zp, scales_col_major=cm, out=(cx, csc))
+                torch.cuda.synchronize()
+                assert torch.equal(cx, rx)
+                assert torch.equal(csc.view(torch.int32), sc.view(torch.int32))
+    h.free()
+
+
 def test_debug_copy_is_a_copy():
     """The calibration copy moves every byte (a few MiB, an odd number of KiB)."""
     src = torch.randint(0, 256, ((4 << 20) + 3 * 1024,), dtype=torch.uint8, device=DEV)
