@@ -1000,6 +1000,65 @@ def test_fixed_windows_capture_in_a_graph():
     h.free()
 
 
+
+def test_fixed_windows_fp8_graph_replays_with_new_routing():
+    """Fixed windows, fp8 with column-major scales, captured as relayout + dispatch in one
+    graph.  Before each replay a new routing and new x are copied into the captured inputs,
+    so every replay recomputes the whole layout; each replay must match the eager calls and
+    the oracle."""
+    w = SMALL[1]
+    nb = w.H // 128
+    routings = [synth.gen_routing(synth.scaled(w, seed=w.seed + 200 + i)) for i in range(4)]
+    lays = [oracle.layout(w.P, w.S, w.E, w.K, w.A, r) for r in routings]
+    W = max(int(l.num_expanded.max()) for l in lays) + 64
+    topk_d = torch.from_numpy(routings[0]).to(DEV)
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A, num_worst_rows=W), topk_d)
+    wt = synth.gen_weights(w)
+    wd = torch.from_numpy(wt).to(DEV)
+    x_static = dev_bf16(synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H))
+    R = h.total_rows
+    rq = torch.empty((R, w.H), dtype=torch.uint8, device=DEV)
+    scm = torch.empty((nb, R), dtype=torch.float32, device=DEV)
+    rw = torch.empty(R, dtype=torch.float32, device=DEV)
+    rm = torch.empty((R, 2), dtype=torch.int32, device=DEV)
+
+    def step():
+        ep.relayout(h, topk_d)
+        ep.dispatch(h, x_static, wd, fp8=True, zero_padding=True, scales_col_major=True, out=(rq, scm, rw, rm))
+
+    step()  # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("capture fixed-window fp8 step")
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for it in range(1, 4):
+        xi = synth.gen_bf16_rows(w.seed + 300 + it, wl.STREAM_X, w.T, w.H)
+        topk_d.copy_(torch.from_numpy(routings[it]).to(DEV))
+        x_static.copy_(dev_bf16(xi))
+        torch.cuda.synchronize()
+        say("fp8 graph replay", it)
+        g.replay()
+        torch.cuda.synchronize()
+        got = (rq.clone(), scm.clone(), rw.clone(), rm.clone())
+        ox, osc, ow, om, dropped = oracle.dispatch_general(lays[it], w.H, fp8=True, zero_padding=True,
+                                                           topk_weights=wt, x=xi, capacity=W, scales_col_major=True)
+        assert dropped == 0
+        np.testing.assert_array_equal(got[0].cpu().numpy(), ox)
+        np.testing.assert_array_equal(got[1].cpu().numpy().view(np.uint32), osc.view(np.uint32))
+        np.testing.assert_array_equal(got[2].cpu().numpy().view(np.uint32), ow.view(np.uint32))
+        np.testing.assert_array_equal(got[3].cpu().numpy(), om)
+        step()  # eager on the same inputs
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], rq) and torch.equal(got[1].view(torch.int32), scm.view(torch.int32))
+        assert torch.equal(got[2].view(torch.int32), rw.view(torch.int32)) and torch.equal(got[3], rm)
+        check_fixed_layout(lays[it], h, W)
+    assert h.status() == (0, 0)
+    del g
+    h.free()
+
+
 def test_exact_windows_dispatch_and_combine_capture_in_a_graph():
     """With exact windows the layout waits on the host once, so it stays outside; the
     dispatches (bf16 fresh, fp8 cached) and the combine with a bias are captured.  Each replay
