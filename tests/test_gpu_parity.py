@@ -924,6 +924,52 @@ def test_symmetric_windows_fp8_variants():
     h.free()
 
 
+
+def test_two_handles_on_two_streams():
+    """Calls are re-entrant across distinct handles: two handles of different shapes (an fp8
+    dispatch with column-major scales on one, a bf16 dispatch on the other, then a combine
+    on each) enqueued interleaved on two streams with nothing ordering them; each result
+    must match the oracle."""
+    wa = SMALL[1]                                                             # P=8, E=256, H=7168
+    wb = wl.Workload("two-handles-b", 16, 96, 64, 4, 512, 8, True, "uniform", seed=31)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    runs = []
+    for w, stream, fp8 in ((wa, s1, True), (wb, s2, False)):
+        topk = routing_with_holes(w, 32)
+        lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+        x = synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H)
+        wt = synth.gen_weights(w)
+        y = synth.gen_expert_out(w, lay.total_rows)
+        with torch.cuda.stream(stream):
+            h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A), torch.from_numpy(topk).to(DEV))
+        torch.cuda.synchronize()
+        runs.append(dict(w=w, s=stream, fp8=fp8, lay=lay, h=h, x=x, wt=wt, y=y, xd=dev_bf16(x),
+                         wd=torch.from_numpy(wt).to(DEV), yd=dev_bf16(y)))
+    torch.cuda.synchronize()
+    for step in ("dispatch", "combine"):
+        for r in runs:  # interleaved: a's call, then b's, each on its own stream
+            with torch.cuda.stream(r["s"]):
+                if step == "dispatch":
+                    r["out"] = ep.dispatch(r["h"], r["xd"], r["wd"], fp8=r["fp8"], zero_padding=True,
+                                           scales_col_major=r["fp8"])
+                else:
+                    r["comb"] = ep.combine(r["h"], r["yd"], r["wd"])
+    torch.cuda.synchronize()
+    for r in runs:
+        w, lay = r["w"], r["lay"]
+        say("two handles", w.name, "fp8" if r["fp8"] else "bf16")
+        ox, osc, ow, om, _ = oracle.dispatch_general(lay, w.H, fp8=r["fp8"], zero_padding=True, topk_weights=r["wt"],
+                                                     x=r["x"], scales_col_major=r["fp8"])
+        rx, sc, rw, rm = r["out"]
+        np.testing.assert_array_equal(rx.cpu().numpy() if r["fp8"] else host_u16(rx), ox)
+        np.testing.assert_array_equal(rm.cpu().numpy(), om)
+        np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+        if r["fp8"]:
+            np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+        np.testing.assert_array_equal(host_u16(r["comb"]), oracle.combine(lay, w.H, r["y"], r["wt"]))
+        r["h"].free()
+
+
 def test_debug_copy_is_a_copy():
     """The calibration copy moves every byte (a few MiB, an odd number of KiB)."""
     src = torch.randint(0, 256, ((4 << 20) + 3 * 1024,), dtype=torch.uint8, device=DEV)
