@@ -970,6 +970,59 @@ def test_two_handles_on_two_streams():
         r["h"].free()
 
 
+
+def _edge_value_rows(T, H, seed):
+    """bf16 rows whose 128-channel blocks stress the fp8 arithmetic: all subnormal (the
+    scale amax / 448 is then an fp32 subnormal), one normal value among subnormals (codes
+    that underflow to zero or to E4M3 subnormals), magnitudes spread over many binades, the
+    largest finite bf16 (0x7F7F), and signed zeros."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((T, H), np.uint16)
+    for u in range(T):
+        for b in range(H // 128):
+            kind = (u + b) % 5
+            blk = np.zeros(128, np.uint16)
+            sign = rng.integers(0, 2, 128).astype(np.uint16) << 15
+            if kind == 0:    # all subnormal: exponent 0, random non-zero mantissas
+                blk = sign | rng.integers(1, 0x80, 128).astype(np.uint16)
+            elif kind == 1:  # one normal value, the rest subnormal
+                blk = sign | rng.integers(1, 0x80, 128).astype(np.uint16)
+                blk[rng.integers(0, 128)] = 0x3F80 | sign[0]
+            elif kind == 2:  # magnitudes across ~60 binades
+                e = rng.integers(60, 121, 128).astype(np.uint16)
+                blk = sign | (e << 7) | rng.integers(0, 0x80, 128).astype(np.uint16)
+            elif kind == 3:  # the largest finite bf16 and small neighbours
+                blk = sign | rng.integers(0x3000, 0x4000, 128).astype(np.uint16)
+                blk[rng.integers(0, 128)] = 0x7F7F
+            else:            # signed zeros with one tiny subnormal
+                blk = sign.copy()
+                blk[rng.integers(0, 128)] |= 0x0001
+            x[u, 128 * b:128 * (b + 1)] = blk
+    return x
+
+
+@pytest.mark.parametrize("cm", [False, True], ids=["row-major", "col-major"])
+def test_fp8_dispatch_on_subnormal_and_extreme_values(cm):
+    """The fp8 dispatch's scale (amax / 448) and codes (x / scale, E4M3 RNE) on blocks the
+    synthetic workloads never produce, bit for bit against the oracle."""
+    w = D["tiny-p4-s64-e16-k2-h512"]
+    topk = synth.gen_routing(w)
+    x = _edge_value_rows(w.T, w.H, 41)
+    wt = synth.gen_weights(w)
+    lay, h = layout_both(w, topk)
+    rx, sc, rw, rm = ep.dispatch(h, dev_bf16(x), torch.from_numpy(wt).to(DEV), fp8=True, zero_padding=True,
+                                 scales_col_major=cm)
+    torch.cuda.synchronize()
+    ox, osc, _, _, _ = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=True, topk_weights=wt, x=x,
+                                               scales_col_major=cm)
+    gs = sc.cpu().numpy()
+    # scales first: a flushed subnormal scale would show here
+    np.testing.assert_array_equal(gs.view(np.uint32), osc.view(np.uint32))
+    np.testing.assert_array_equal(rx.cpu().numpy(), ox)
+    assert np.any((osc.view(np.uint32) & 0x7F800000) == 0) and np.any(osc > 0)  # subnormal scales were exercised
+    h.free()
+
+
 def test_debug_copy_is_a_copy():
     """The calibration copy moves every byte (a few MiB, an odd number of KiB)."""
     src = torch.randint(0, 256, ((4 << 20) + 3 * 1024,), dtype=torch.uint8, device=DEV)
@@ -1228,6 +1281,39 @@ def test_combine_arithmetic_order_on_adversarial_values(H):
         np.testing.assert_array_equal(got, oracle.combine_general(
             lay, H, y, np.asarray([weights], np.float32), bias=None if bias is None else np.full((1, H), bias, np.uint16)))
         h.free()
+
+
+
+@pytest.mark.parametrize("H", [512, 4104], ids=["lds-kernel", "register-kernel"])
+def test_combine_on_subnormal_and_extreme_values(H):
+    """Combine where products and sums reach the fp32 and bf16 subnormal ranges: expert rows
+    mixing bf16 subnormals, tiny, moderate and large (up to 2^120) values, weights down to
+    2^-120.  Magnitudes stay low enough that no sum overflows, so the result has no NaN.
+    Bit for bit against the oracle, through both combine kernels."""
+    P, S, E, K, A = 4, 40, 16, 4, 4
+    w = wl.Workload(f"extreme-combine-h{H}", P, S, E, K, H, A, True, "uniform", seed=51)
+    topk = synth.gen_routing(w)
+    lay, h = layout_both(w, topk)
+    rng = np.random.default_rng(52)
+    R = lay.total_rows
+    cls = rng.integers(0, 5, (R, H))
+    sign = (rng.integers(0, 2, (R, H)) << 15).astype(np.uint16)
+    mant = rng.integers(0, 0x80, (R, H)).astype(np.uint16)
+    expo = np.select([cls == 0, cls == 1, cls == 2, cls == 3], [0, rng.integers(1, 20, (R, H)),
+                     rng.integers(100, 150, (R, H)), rng.integers(200, 247, (R, H))], 0).astype(np.uint16)
+    y = sign | (expo << 7) | np.where(cls == 0, np.maximum(mant, 1), mant).astype(np.uint16)
+    y[cls == 4] = sign[cls == 4]  # signed zeros
+    wt = synth.gen_weights(w).copy()
+    tiny = rng.random(wt.shape) < 0.3
+    wt[tiny] = np.ldexp(np.float32(1.0), -rng.integers(60, 121, int(tiny.sum()))).astype(np.float32)
+    out = ep.combine(h, dev_bf16(y), torch.from_numpy(wt).to(DEV))
+    torch.cuda.synchronize()
+    exp = oracle.combine(lay, H, y, wt)
+    got = host_u16(out)
+    assert not np.any(((exp & 0x7F80) == 0x7F80) & ((exp & 0x7F) != 0))  # no NaN expected
+    assert np.any(((exp & 0x7F80) == 0) & ((exp & 0x7F) != 0))  # subnormal outputs were exercised
+    np.testing.assert_array_equal(got, exp)
+    h.free()
 
 
 def test_relayout_and_free_wait_for_pending_async_calls():
