@@ -1023,6 +1023,54 @@ def test_fp8_dispatch_on_subnormal_and_extreme_values(cm):
     h.free()
 
 
+
+@pytest.mark.parametrize("H", [8320, 16384], ids=["h8320-65-blocks", "h16384-128-blocks"])
+@pytest.mark.parametrize("mode", ["exact", "fixed"])
+def test_large_hidden_sizes(H, mode):
+    """Hidden sizes above the workloads' 7168: more column parts per row, and more than 64
+    fp8 scale blocks, so the column-major scales pass transposes in several slabs (8320: a
+    second slab of one block; 16384: two full slabs).  bf16 and fp8 (fused and pre-quantised,
+    row- and column-major scales), then combine, against the oracle."""
+    w = wl.Workload(f"large-h{H}", 4, 40, 16, 4, H, 4, True, "uniform", seed=61)
+    topk = routing_with_holes(w, 62)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    W = max(1, int(np.median(lay.num_expanded))) if mode == "fixed" else 0
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A, num_worst_rows=W), torch.from_numpy(topk).to(DEV))
+    R, nb = h.total_rows, H // 128
+    x = synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, H)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    rng = np.random.default_rng(63)
+    codes = rng.integers(0, 256, (w.T, H), dtype=np.uint8)
+    scales = rng.standard_normal((w.T, nb)).astype(np.float32)
+    # bf16
+    rx, _, rw, rm = ep.dispatch(h, xd, wd, zero_padding=True)
+    torch.cuda.synchronize()
+    ox, _, ow, om, _ = oracle.dispatch_general(lay, H, fp8=False, zero_padding=True, topk_weights=wt, x=x, capacity=W)
+    np.testing.assert_array_equal(host_u16(rx), ox)
+    np.testing.assert_array_equal(rm.cpu().numpy(), om)
+    np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+    # fp8 variants
+    for src in ("fused", "prequant"):
+        xin = xd if src == "fused" else (_dev_u8(codes), torch.from_numpy(scales).to(DEV))
+        kw = dict(x=x) if src == "fused" else dict(x_codes=codes, x_scales=scales)
+        for cm in (False, True):
+            say("large hidden", H, mode, src, "col-major" if cm else "row-major")
+            qx, qs, _, _ = ep.dispatch(h, xin, wd, fp8=True, zero_padding=True, scales_col_major=cm)
+            torch.cuda.synchronize()
+            ox, osc, _, _, _ = oracle.dispatch_general(lay, H, fp8=True, zero_padding=True, topk_weights=wt,
+                                                       capacity=W, scales_col_major=cm, **kw)
+            np.testing.assert_array_equal(qx.cpu().numpy(), ox)
+            np.testing.assert_array_equal(qs.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    # combine
+    y = synth.gen_expert_out(w, R)
+    out = ep.combine(h, dev_bf16(y), wd)
+    torch.cuda.synchronize()
+    exp = oracle.combine_general(lay, H, y, wt, capacity=W)
+    np.testing.assert_array_equal(host_u16(out), exp)
+    h.free()
+
+
 def test_debug_copy_is_a_copy():
     """The calibration copy moves every byte (a few MiB, an odd number of KiB)."""
     src = torch.randint(0, 256, ((4 << 20) + 3 * 1024,), dtype=torch.uint8, device=DEV)
