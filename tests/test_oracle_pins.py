@@ -346,7 +346,13 @@ def test_quantize_row_scale_codes_and_error_bound():
     x[1, 130] = 0x8000  # -0.0 inside it
     x[2, 256:384] = torch_bf16_bits(rng.normal(0, 1e-3, 128).astype(np.float32))
     x[3, 0:128] = torch_bf16_bits((rng.normal(0, 1, 128) * 2.0 ** -120).astype(np.float32))  # tiny
-    for r in range(4):
+    # bf16 subnormal inputs (exponent field 0): an all-subnormal block, and one normal value
+    # among subnormals, so that the scale and most codes fall in the subnormal ranges
+    sub = np.zeros((1, H), np.uint16)
+    sub[0, :256] = (rng.integers(0, 2, 256) << 15).astype(np.uint16) | rng.integers(1, 0x80, 256).astype(np.uint16)
+    sub[0, 200] = 0x3F80
+    x = np.vstack([x, sub])
+    for r in range(5):
         codes, scales = oracle.quantize_row(x[r])
         xf = bf16_bits_to_f64(x[r]).astype(np.float32)
         for b in range(H // 128):
