@@ -430,6 +430,28 @@ def test_combine_unit_weights_is_exact_k_times_x():
     assert np.all(out[::10] == 0)
 
 
+
+def test_combine_unit_weights_on_subnormals_closed_form():
+    """K equal bf16 subnormal rows with unit weights: K*v is exact in fp32, and below 2^-125
+    a bf16 value's bit pattern, read as an integer, is the value in units of 2^-133 (the
+    subnormals, then the first normal binade, continue the same integer scale).  So the
+    output bits are sign | (mantissa * K) whenever that stays below 256: a closed form that
+    no floating-point arithmetic enters."""
+    H = 128
+    rng = np.random.default_rng(71)
+    for K in (1, 2, 3, 4, 8):
+        topk = np.arange(K, dtype=np.int64)[None, :]
+        lay = oracle.layout(1, 1, K, K, 1, topk)
+        top = min(127, 255 // K)  # inputs subnormal (7-bit mantissa), sums below 2^-125
+        mant = rng.integers(1, top + 1, H).astype(np.uint16)
+        mant[:4] = [1, 2, top, max(1, 127 // K)]
+        sign = (rng.integers(0, 2, H) << 15).astype(np.uint16)
+        v = sign | mant  # exponent field 0: bf16 subnormals
+        y = np.repeat(v[None, :], K, 0)
+        out = oracle.combine(lay, H, y, None)
+        np.testing.assert_array_equal(out[0], sign | (mant * K).astype(np.uint16), err_msg=f"K={K}")
+
+
 def test_combine_general_rows_within_one_ulp_of_exact_sum():
     w = small_workload(P=4, S=96, E=32, K=8, H=256, A=8, seed=22)
     topk = synth.gen_routing(w)
