@@ -55,6 +55,13 @@ MUTANTS = [
      [("float scale = amax / 448.0f;", "float scale = amax / 447.0f;")]),
     ("codes_by_reciprocal",
      [("codes[h] = oracle_e4m3_encode(xf / scale);", "codes[h] = oracle_e4m3_encode(xf * (1.0f / scale));")]),
+    ("amax_flushes_subnormal_inputs",
+     [("      float v = fabsf(oracle_bf16_to_float(x[h]));",
+       "      float v = fabsf(oracle_bf16_to_float(x[h]));\n      if (v < 1.17549435e-38f) v = 0.0f;")]),
+    ("combine_flushes_subnormal_products",
+     [("        float prod = w * oracle_bf16_to_float(y[r * H + h]);\n        acc = acc + prod;",
+       "        float prod = w * oracle_bf16_to_float(y[r * H + h]);\n"
+       "        if (fabsf(prod) < 1.17549435e-38f) prod = copysignf(0.0f, prod);\n        acc = acc + prod;")]),
     ("amax_skips_last_channel",
      [("    for (int h = 128 * b; h < 128 * b + 128; h++) {\n      float v = fabsf",
        "    for (int h = 128 * b; h < 128 * b + 127; h++) {\n      float v = fabsf")]),
