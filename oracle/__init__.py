@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_combine_identity.restype = i32
         L.oracle_quantize_row.argtypes = [P_, i32, P_, P_]
         L.oracle_quantize_row.restype = None
+        L.oracle_quantize_rows.argtypes = [P_, i32, i64, i64, P_, P_]
+        L.oracle_quantize_rows.restype = None
         for fn in ("oracle_e4m3_encode_array", "oracle_e4m3_decode_array", "oracle_bf16_round_array"):
             getattr(L, fn).argtypes = [P_, i64, P_]
             getattr(L, fn).restype = None
@@ -334,6 +336,18 @@ def quantize_row(x_row: np.ndarray):
     codes = np.zeros(H, np.uint8)
     scales = np.zeros(H // 128, np.float32)
     lib().oracle_quantize_row(_p(x_row), H, _p(codes), _p(scales))
+    return codes, scales
+
+
+def quantize_rows(x: np.ndarray, H: int, row_begin: int = 0, row_end: int | None = None):
+    """``oracle_quantize_row`` on rows [row_begin, row_end) of x [T, H] -> (codes, scales)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16).reshape(-1, H)
+    if row_end is None:
+        row_end = x.shape[0]
+    n = row_end - row_begin
+    codes = np.zeros((n, H), np.uint8)
+    scales = np.zeros((n, H // 128), np.float32)
+    lib().oracle_quantize_rows(_p(x), H, row_begin, row_end, _p(codes), _p(scales))
     return codes, scales
 
 

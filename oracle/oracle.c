@@ -257,24 +257,47 @@ int oracle_layout(int P, int S, int E, int K, int A, int symmetric, const int64_
 
 /* Per-token FP8 quantisation ([TUT] 3.6): one fp32 scale per 128 channels,
  * scale = amax / 448, code = E4M3(x / scale), both divisions IEEE fp32.
- * codes [H] u8, scales [H/128] f32. */
+ * codes [H] u8, scales [H/128] f32.
+ *
+ * Non-finite inputs (the pages say nothing; this is the stated reading): the
+ * block maximum is NaN as soon as one |x| is NaN, else the largest |x|, +Inf
+ * included.  A NaN maximum gives the scale 0x7FC00000 (the quiet NaN with a
+ * clear sign and payload), an infinite one the scale +Inf.  Codes are still
+ * E4M3(x / scale), except that a NaN quotient (x / NaN, or +-Inf / +Inf) is
+ * written as 0x7F, the E4M3FN NaN with a clear sign bit.  A finite x over an
+ * infinite scale is the signed zero of the quotient. */
 void oracle_quantize_row(const uint16_t *x, int H, uint8_t *codes, float *scales) {
   for (int b = 0; b < H / 128; b++) {
     float amax = 0.0f;
+    int has_nan = 0;
     for (int h = 128 * b; h < 128 * b + 128; h++) {
       float v = fabsf(oracle_bf16_to_float(x[h]));
-      if (v > amax) amax = v;
+      if (isnan(v))
+        has_nan = 1;
+      else if (v > amax)
+        amax = v;
     }
-    float scale = amax / 448.0f;
+    float scale = has_nan ? f32_from_bits(0x7FC00000u) : amax / 448.0f;
     scales[b] = scale;
     for (int h = 128 * b; h < 128 * b + 128; h++) {
       float xf = oracle_bf16_to_float(x[h]);
-      if (amax == 0.0f)
+      if (amax == 0.0f && !has_nan) {
         codes[h] = signbit(xf) ? 0x80 : 0x00;
-      else
-        codes[h] = oracle_e4m3_encode(xf / scale);
+      } else {
+        float q = xf / scale;
+        codes[h] = isnan(q) ? 0x7F : oracle_e4m3_encode(q);
+      }
     }
   }
+}
+
+/* oracle_quantize_row applied to rows [row_begin, row_end) of x [T][H]; the
+ * outputs hold only those rows. */
+void oracle_quantize_rows(const uint16_t *x, int H, int64_t row_begin, int64_t row_end,
+                          uint8_t *codes, float *scales) {
+  for (int64_t u = row_begin; u < row_end; u++)
+    oracle_quantize_row(x + u * H, H, codes + (u - row_begin) * H,
+                        scales + (u - row_begin) * (H / 128));
 }
 
 /* Dispatch rows [row_begin, row_end) of the expanded output ([TUT] 2.2).

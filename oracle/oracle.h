@@ -29,6 +29,8 @@ int oracle_layout(int P, int S, int E, int K, int A, int symmetric, const int64_
                   int32_t *dst_slot, int32_t *send_head, int32_t *recv_src_idx,
                   int64_t *recv_src_base);
 void oracle_quantize_row(const uint16_t *x, int H, uint8_t *codes, float *scales);
+void oracle_quantize_rows(const uint16_t *x, int H, int64_t row_begin, int64_t row_end,
+                          uint8_t *codes, float *scales);
 int oracle_dispatch(int P, int S, int E, int K, int H, int A, int fp8, int zero_padding,
                     const int64_t *topk_idx, const int32_t *dst_slot,
                     const int32_t *num_tokens_per_expert_total, const int64_t *expert_offset,

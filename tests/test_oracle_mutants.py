@@ -52,9 +52,14 @@ MUTANTS = [
      [("window_row_base[d + 1] = symmetric ? (int64_t)(d + 1) * max_expanded",
        "window_row_base[d + 1] = 0 ? (int64_t)(d + 1) * max_expanded")]),
     ("scale_divides_by_447",
-     [("float scale = amax / 448.0f;", "float scale = amax / 447.0f;")]),
+     [("f32_from_bits(0x7FC00000u) : amax / 448.0f;", "f32_from_bits(0x7FC00000u) : amax / 447.0f;")]),
     ("codes_by_reciprocal",
-     [("codes[h] = oracle_e4m3_encode(xf / scale);", "codes[h] = oracle_e4m3_encode(xf * (1.0f / scale));")]),
+     [("float q = xf / scale;", "float q = xf * (1.0f / scale);")]),
+    ("amax_skips_nan",
+     [("      if (isnan(v))\n        has_nan = 1;\n      else if (v > amax)",
+       "      if (0)\n        has_nan = 1;\n      else if (v > amax)")]),
+    ("nan_codes_keep_sign",
+     [("codes[h] = isnan(q) ? 0x7F : oracle_e4m3_encode(q);", "codes[h] = oracle_e4m3_encode(q);")]),
     ("amax_flushes_subnormal_inputs",
      [("      float v = fabsf(oracle_bf16_to_float(x[h]));",
        "      float v = fabsf(oracle_bf16_to_float(x[h]));\n      if (v < 1.17549435e-38f) v = 0.0f;")]),

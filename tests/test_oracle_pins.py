@@ -374,6 +374,67 @@ def test_quantize_row_scale_codes_and_error_bound():
             assert np.all(err[~normal] <= (2.0 ** -10 + 2.0 ** -30) * scales[b])
 
 
+def test_quantize_row_non_finite_blocks():
+    """Blocks holding NaN or +-Inf follow the stated rule, written here from numpy alone: the
+    block maximum is numpy's max of |x| (NaN wins over everything), the scale is that
+    maximum / 448 in fp32 with a NaN maximum giving the quiet NaN 0x7FC00000, and each code
+    is the E4M3 code of x / scale with every NaN quotient written 0x7F.  Finite blocks of the
+    same rows are unaffected.  Also the batched form equals the per-row form."""
+    rng = np.random.default_rng(11)
+    H = 768
+    x = synth.gen_bf16_rows(4, 1, 6, H)
+    NAN_P, NAN_N, NAN_PAYLOAD, INF_P, INF_N = 0x7FC0, 0xFFC0, 0x7F81, 0x7F80, 0xFF80
+    x[0, 5] = NAN_P                     # one positive NaN in block 0
+    x[1, 128 + 7] = NAN_N               # one negative NaN in block 1
+    x[1, 128 + 9] = INF_N
+    x[2, 256:384] = 0
+    x[2, 300] = NAN_PAYLOAD             # NaN among zeros, signalling payload
+    x[3, 384 + 1] = INF_P               # +Inf among finite values
+    x[3, 384 + 2] = INF_N               # and -Inf
+    x[4, 512:640] = INF_N               # a block of -Inf only
+    x[5, 640 + rng.integers(0, 128)] = INF_P
+    x[5, 0] = 0x8000
+    for r in range(x.shape[0]):
+        codes, scales = oracle.quantize_row(x[r])
+        xf = bf16_bits_to_f64(x[r]).astype(np.float32)
+        for b in range(H // 128):
+            blk = xf[128 * b:128 * (b + 1)]
+            with np.errstate(invalid="ignore", divide="ignore"):
+                amax = np.abs(blk).max()  # numpy's max propagates NaN
+                exp_scale = np.float32(np.nan) if np.isnan(amax) else np.float32(amax) / np.float32(448.0)
+                if np.isnan(amax):
+                    assert scales[b].view(np.uint32) == 0x7FC00000, (r, b)
+                else:
+                    assert scales[b].view(np.uint32) == exp_scale.view(np.uint32), (r, b)
+                cb = codes[128 * b:128 * (b + 1)]
+                if amax == 0:
+                    np.testing.assert_array_equal(cb, np.where(np.signbit(blk), 0x80, 0x00))
+                    continue
+                q = blk / exp_scale
+            nanq = np.isnan(q)
+            exp = np.full(128, 0x7F, np.uint8)
+            if (~nanq).any():
+                exp[~nanq] = brute_force_e4m3(q[~nanq])
+            np.testing.assert_array_equal(cb, exp, err_msg=f"row {r} block {b}")
+            if not np.isfinite(amax):
+                # the rule in words: NaN blocks are all 0x7F; Inf blocks give signed zeros for
+                # finite x and 0x7F for the infinities
+                fin = np.isfinite(blk)
+                if np.isnan(amax):
+                    assert (cb == 0x7F).all()
+                else:
+                    np.testing.assert_array_equal(cb[fin], np.where(np.signbit(blk[fin]), 0x80, 0x00))
+                    assert (cb[~fin] == 0x7F).all()
+    bc, bs = oracle.quantize_rows(x, H)
+    for r in range(x.shape[0]):
+        c1, s1 = oracle.quantize_row(x[r])
+        np.testing.assert_array_equal(bc[r], c1)
+        np.testing.assert_array_equal(bs[r].view(np.uint32), s1.view(np.uint32))
+    bc2, bs2 = oracle.quantize_rows(x, H, 2, 5)
+    np.testing.assert_array_equal(bc2, bc[2:5])
+    np.testing.assert_array_equal(bs2.view(np.uint32), bs[2:5].view(np.uint32))
+
+
 def test_dispatch_fp8_rows_and_zero_padding():
     w = small_workload(P=4, S=32, E=8, K=2, H=384, A=8, seed=12)
     topk = synth.gen_routing(w)
