@@ -356,17 +356,6 @@ def _overlapped(h, device, tensors, launch, previous_event):
     return EventOverlap(done, result)
 
 
-def _after_pending_scratch_users(h, device):
-    """fp8 with column-major scales stages per-token scales in the handle's scratch: order the
-    launch stream after the handle's pending async calls, which may be staging theirs."""
-    import torch
-
-    if h._pending:
-        cur = torch.cuda.current_stream(device)
-        for ev in h._pending:
-            cur.wait_event(ev)
-
-
 def get_layout(cfg: Config, topk_idx) -> Handle:
     """ep_get_layout: topk_idx int64 [T, K] on the device -> Handle (synchronizes once in exact
     mode; only enqueues with cfg.num_worst_rows > 0)."""
@@ -460,8 +449,6 @@ def dispatch(h: Handle, x, topk_weights, fp8: bool = False, zero_padding: bool =
 
     def launch():
         with _on(device):
-            if fp8 and scales_col_major and xs is None:
-                _after_pending_scratch_users(h, device)
             if xs is None:
                 _check(lib().ep_dispatch(h.ptr, flags, _ptr(xin), _ptr(topk_weights), _ptr(recv_x),
                                          _ptr(recv_scales), _ptr(recv_w), _ptr(recv_meta), _stream(device)))
@@ -494,8 +481,6 @@ def dispatch_cached(h: Handle, x, fp8: bool = False, zero_padding: bool = False,
 
     def launch():
         with _on(device):
-            if fp8 and scales_col_major and xs is None:
-                _after_pending_scratch_users(h, device)
             if xs is None:
                 _check(lib().ep_dispatch_cached(h.ptr, flags, _ptr(xin), _ptr(recv_x), _ptr(recv_scales),
                                                 _stream(device)))

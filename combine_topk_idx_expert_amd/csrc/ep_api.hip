@@ -58,7 +58,7 @@ struct ep_handle {
   LayoutDims dims;
   int64_t T;
   int device;
-  // read back by the layout (fixed windows: on first use, see ensure_counts)
+  // read back by the layout (fixed windows: on every query, see ensure_counts)
   int64_t total_rows = 0, total_pad = 0, sum_recv = 0, sum_expanded = 0;
   int64_t dropped = 0;
   uint32_t status = 0;  // EP_STATUS_* of the last layout
@@ -80,8 +80,11 @@ struct ep_handle {
   int64_t* summary_host = nullptr;      // pinned; the finalize kernel writes it directly
   int64_t* summary_host_dev = nullptr;  // its device address
   int64_t layout_seq = 0;               // sequence number of the last enqueued layout
-  hipEvent_t done = nullptr;        // end of the last layout's work
+  bool done_recorded = false;       // `done` marks an eager layout (not one captured in a graph)
+  hipEvent_t done = nullptr;        // end of the last eager layout's work
   hipEvent_t summary_ready = nullptr;  // the last layout's host summary has landed
+  hipEvent_t cm_done = nullptr;     // end of the last column-major fp8 dispatch (tok_scales free again)
+  bool cm_recorded = false;
   size_t lds_count, lds_scan, lds_finalize, lds_rank;
 };
 
@@ -189,6 +192,8 @@ ep_status allocate(ep_handle* h) {
   if (e != hipSuccess) return fail(EP_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
   e = hipEventCreateWithFlags(&h->done, hipEventDisableTiming);
   if (e != hipSuccess) return fail(EP_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+  e = hipEventCreateWithFlags(&h->cm_done, hipEventDisableTiming);
+  if (e != hipSuccess) return fail(EP_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
 
   h->lds_count = (size_t)(d.ncols + kChunk * ((d.P + 31) / 32) + kChunk * d.K) * 4;
   h->lds_scan = (size_t)(((d.P + 2) & ~1) * 4 + (kScanThreads / 64) * 8);
@@ -207,8 +212,12 @@ ep_status allocate(ep_handle* h) {
 void release(ep_handle* h) {
   if (!h) return;
   if (h->summary_ready) (void)hipEventDestroy(h->summary_ready);
+  if (h->cm_done) {
+    if (h->cm_recorded) (void)hipEventSynchronize(h->cm_done);
+    (void)hipEventDestroy(h->cm_done);
+  }
   if (h->done) {
-    (void)hipEventSynchronize(h->done);
+    if (h->done_recorded) (void)hipEventSynchronize(h->done);
     (void)hipEventDestroy(h->done);
   }
   if (h->arena) (void)hipFree(h->arena);
@@ -235,10 +244,31 @@ ep_status wait_summary(ep_handle* h) {
   return EP_OK;
 }
 
+// True when `s` is capturing into a graph.  A failing query (for instance of
+// the null stream while another stream captures) counts as "not capturing"
+// and its error is cleared so that the launch checks below do not see it.
+bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
+
 // Enqueue the layout for the handle's config and read back the summary.
+// Exact windows wait for the row counts on the host, so they cannot be
+// captured; fixed windows only enqueue, so they can.  A captured layout
+// records no events: the graph's replays publish their summaries into the
+// pinned host buffer, which status queries read after the caller has waited
+// for the replay.
 ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64_t* total_rows) {
   h->valid = false;
   const LayoutDims& d = h->dims;
+  const bool capturing = stream_capturing(s);
+  if (capturing && !h->fixed)
+    return fail(EP_ERR_HIP, "exact windows read the row counts back to the host and cannot be captured in a "
+                            "graph; use fixed windows (num_worst_rows > 0)");
   if (d.num_chunks > 0) {
     layout_count_kernel<<<d.num_chunks, kLayoutThreads, h->lds_count, s>>>(d, topk_idx, h->is_token_in_rank,
                                                                    h->chunk_hist);
@@ -253,7 +283,7 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
                  h->summary_dev, h->summary_host_dev, ++h->layout_seq};
   layout_finalize_kernel<<<1, kFinalizeThreads, h->lds_finalize, s>>>(d, h->col_total, fo);
   EP_LAUNCHED("layout_finalize_kernel");
-  EP_HIP(hipEventRecord(h->summary_ready, s));  // the finalize kernel wrote the host summary
+  if (!capturing) EP_HIP(hipEventRecord(h->summary_ready, s));  // the finalize kernel wrote the host summary
   {
     // at least one workgroup per expert, so that the padding rows are written even when T = 0
     RankOut ro{h->dst_slot, h->dst_row, h->row_slot, h->send_head, h->recv_src_idx, h->pad_rows};
@@ -262,7 +292,8 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
     layout_rank_kernel<<<std::max(d.num_chunks, 1), kLayoutThreads, h->lds_rank, s>>>(d, topk_idx, ri, ro);
     EP_LAUNCHED("layout_rank_kernel");
   }
-  EP_HIP(hipEventRecord(h->done, s));
+  if (!capturing) EP_HIP(hipEventRecord(h->done, s));
+  h->done_recorded = !capturing;
   h->counts_known = false;
   if (h->fixed) {  // fixed windows: nothing to wait for
     h->total_rows = (int64_t)d.P * d.cap;
@@ -290,12 +321,18 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
   return EP_OK;
 }
 
-// Fixed windows: wait for the last layout and take its summary (host fields
-// are mutable caches of device results).
+// Host copies of the layout summary (mutable caches of device results).
+// Exact windows read it once, in run_layout.  Fixed windows read it on every
+// query: after waiting for the last eager layout, the pinned buffer holds the
+// summary of the last layout that ran, which may be a graph replay enqueued
+// after it (the caller waits for a replay before asking), so nothing is cached.
 ep_status ensure_counts(const ep_handle* hc) {
   ep_handle* h = const_cast<ep_handle*>(hc);
   if (h->counts_known) return EP_OK;
-  if (ep_status st = wait_summary(h); st != EP_OK) return st;
+  if (h->done_recorded) {
+    const hipError_t e = hipEventSynchronize(h->done);
+    if (e != hipSuccess) return fail(EP_ERR_HIP, "layout: %s", hipGetErrorString(e));
+  }
   const int64_t* sm = h->summary_host;
   h->total_pad = sm[1];
   h->sum_recv = sm[3];
@@ -303,7 +340,6 @@ ep_status ensure_counts(const ep_handle* hc) {
   for (int r = 0; r < h->dims.P; ++r) h->sum_expanded += sm[kSummaryHeader + r];
   h->dropped = sm[5];
   h->status = (sm[2] != 0 ? EP_STATUS_ROUTING : 0u) | (sm[5] > 0 ? EP_STATUS_TRUNCATED : 0u);
-  h->counts_known = true;
   return EP_OK;
 }
 
@@ -393,6 +429,21 @@ ep_status dispatch_common(const ep_handle* h, uint32_t flags, const void* x, con
     a.x = nullptr;
     a.tok_scales = const_cast<float*>(x_scales);  // read only: the rows' scales come from here
     return meta ? launch_dispatch_mode<true, true, true>(a, s) : launch_dispatch_mode<true, false, true>(a, s);
+  }
+  if (fp8 && a.scales_cm) {
+    // The per-token scales are staged in the handle's tok_scales: order this
+    // call after the previous such call on the handle, whatever its stream
+    // (an event wait on the device, no host synchronisation).  A graph capture
+    // neither waits nor records; calls inside one graph are ordered by it.
+    ep_handle* hm = const_cast<ep_handle*>(h);
+    const bool capturing = stream_capturing(s);
+    if (!capturing && hm->cm_recorded) EP_HIP(hipStreamWaitEvent(s, hm->cm_done, 0));
+    st = meta ? launch_dispatch_mode<true, true, false>(a, s) : launch_dispatch_mode<true, false, false>(a, s);
+    if (st == EP_OK && !capturing) {
+      EP_HIP(hipEventRecord(hm->cm_done, s));
+      hm->cm_recorded = true;
+    }
+    return st;
   }
   if (fp8) return meta ? launch_dispatch_mode<true, true, false>(a, s) : launch_dispatch_mode<true, false, false>(a, s);
   return meta ? launch_dispatch_mode<false, true, false>(a, s) : launch_dispatch_mode<false, false, false>(a, s);

@@ -94,6 +94,28 @@ __device__ __forceinline__ u32x2 quantize8(u32x4 v, float scale, bool zero_block
   return out;
 }
 
+// Codes of 8 bf16 values (packed in v) of a block whose maximum is not
+// finite, byte order as in quantize8.  A NaN block (some |x| is NaN) codes
+// every value 0x7F; an Inf block codes its infinities 0x7F (Inf / Inf is NaN)
+// and every finite value as the signed zero of x / Inf.  NaN codes carry a
+// clear sign bit, so the result does not depend on which NaN a division makes.
+__device__ __forceinline__ u32x2 nonfinite_codes8(u32x4 v, bool nan_block) {
+  u32x2 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t word = v[2 * h + (k >> 1)];
+      const uint32_t b = (k & 1) ? (word >> 16) : (word & 0xFFFFu);
+      const uint32_t code = (nan_block || (b & 0x7FFFu) >= 0x7F80u) ? 0x7Fu : ((b >> 8) & 0x80u);
+      w |= code << (8 * k);
+    }
+    out[h] = w;
+  }
+  return out;
+}
+
 // Row of the k-th tail row of fixed windows: tail rows are the last
 // tail_base[r+1] - tail_base[r] rows of window r.
 __device__ __forceinline__ int64_t tail_row(const DispatchArgs& a, int64_t k) {
@@ -251,8 +273,14 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) m = max(m, max(v[c][k] & 0x7FFFu, (v[c][k] >> 16) & 0x7FFFu));
         m = row16_max_u32(m);  // one DPP row = 16 lanes = one 128-channel block
-        const float scale = __uint_as_float(m << 16) / 448.0f;
+        // |x| patterns order like the magnitudes, NaN above +Inf, so m is the
+        // block maximum with NaN propagated; a non-finite maximum gives the
+        // scale 0x7FC00000 (NaN) or +Inf and the codes of nonfinite_codes8
+        const bool nonfinite = m >= 0x7F80u;
+        float scale = __uint_as_float(m << 16) / 448.0f;
+        if (nonfinite) scale = __uint_as_float(m > 0x7F80u ? 0x7FC00000u : 0x7F800000u);
         codes[c] = quantize8(v[c], scale, m == 0);
+        if (__builtin_expect(nonfinite, 0)) codes[c] = nonfinite_codes8(v[c], m > 0x7F80u);
         const int q = tile + c * kWave + lane;
         if (!fused_scales && (lane & 15) == 0 && q < nchunk) a.tok_scales[(int64_t)u * nblk + (q >> 4)] = scale;
         sc[c] = __shfl(scale, (lane & 3) * 16, kWave);

@@ -86,22 +86,27 @@ ep_status launch_dispatch_mode(const DispatchArgs& a, hipStream_t s) {
 // and two workgroups per CU) go through the LDS kernel, where every wave
 // streams one slot's full row; measured faster than the register kernel at
 // hidden 4096 and not at 7168, where a token's rows no longer fit twice per
-// CU.  Everything else uses the register kernel.
+// CU.  Everything else uses the register kernel, and so does a token count
+// whose LDS grid (one 8-wave workgroup per token) would pass the 2^31
+// work-item limit: the register kernel covers every shape, with its own
+// guard.
 ep_status launch_combine(CombineArgs a, hipStream_t s) {
   if (a.T <= 0) return EP_OK;
-  if (a.K <= 8 && a.H <= 4096) {
+  constexpr int kLdsWaves = 8;
+  const bool lds_grid_fits = (int64_t)a.T * kLdsWaves < ((int64_t)1 << 31) / kWave;
+  if (a.K <= 8 && a.H <= 4096 && lds_grid_fits) {
     const int need = ((a.H >> 3) + kWave - 1) / kWave;  // chunks per lane for a whole row
     const size_t lds_row = (size_t)a.K * kWave * 16;     // per chunk per lane
     a.split = 1;
     const int grid = a.T;
     if (need <= 1)
-      combine_lds_kernel<1><<<grid, 512, lds_row * 1, s>>>(a);
+      combine_lds_kernel<1><<<grid, kLdsWaves * kWave, lds_row * 1, s>>>(a);
     else if (need <= 2)
-      combine_lds_kernel<2><<<grid, 512, lds_row * 2, s>>>(a);
+      combine_lds_kernel<2><<<grid, kLdsWaves * kWave, lds_row * 2, s>>>(a);
     else if (need <= 4)
-      combine_lds_kernel<4><<<grid, 512, lds_row * 4, s>>>(a);
+      combine_lds_kernel<4><<<grid, kLdsWaves * kWave, lds_row * 4, s>>>(a);
     else
-      combine_lds_kernel<8><<<grid, 512, lds_row * 8, s>>>(a);
+      combine_lds_kernel<8><<<grid, kLdsWaves * kWave, lds_row * 8, s>>>(a);
     EP_LAUNCHED("combine_lds_kernel");
     return EP_OK;
   }

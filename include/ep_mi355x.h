@@ -33,9 +33,12 @@
  *    before anything is enqueued.  ep_last_error() gives a message.
  *  - One handle may be used by any number of ep_dispatch_cached / ep_combine
  *    calls; ep_handle_free and ep_relayout require that none is in flight.
- *    One exception: fp8 dispatch with EP_DISPATCH_SCALES_COL_MAJOR (not the
- *    pre-quantised form) stages per-token scales in the handle, so two such
- *    calls on one handle must be ordered (one stream, or an event between).
+ *    fp8 dispatch with EP_DISPATCH_SCALES_COL_MAJOR (not the pre-quantised
+ *    form) stages per-token scales in the handle; the library orders such
+ *    calls on one handle itself, on whatever streams, with an event the handle
+ *    owns.  Inside a graph capture it neither waits nor records, so the
+ *    captured graph must order its own such calls, and a replay must not
+ *    overlap such a call made outside the graph.
  *  - A handle belongs to the device that was current at ep_get_layout; calls
  *    that launch work with another device current return
  *    EP_ERR_HANDLE_MISMATCH.
@@ -146,7 +149,9 @@ ep_status ep_get_layout(const ep_config *cfg, const int64_t *topk_idx, void *str
  * in flight.  On error the handle's layout is invalid until a successful
  * ep_relayout.  Errors: EP_ERR_NULL, EP_ERR_SHAPE (misaligned topk_idx),
  * EP_ERR_HANDLE_MISMATCH (another device is current), EP_ERR_ROUTING (exact
- * mode), EP_ERR_OVERFLOW (symmetric windows reaching 2^31 rows), EP_ERR_HIP. */
+ * mode), EP_ERR_OVERFLOW (symmetric windows reaching 2^31 rows), EP_ERR_HIP
+ * (also: exact mode on a stream that is capturing a graph, since the counts
+ * must reach the host; fixed mode can be captured). */
 ep_status ep_relayout(ep_handle *h, const int64_t *topk_idx, void *stream, int64_t *total_rows);
 
 /* --------------------------------------------------------------------------
@@ -255,15 +260,19 @@ ep_status ep_handle_config(const ep_handle *h, ep_config *cfg);
 ep_status ep_handle_check(const ep_handle *h, const ep_config *cfg);
 
 /* Host copies of the read-back counts: num_expanded [P], num_recv_tokens [P],
- * window_row_base [P+1] (int64).  Any pointer may be NULL.  In fixed mode the
- * first call after a layout waits for that layout to finish. */
+ * window_row_base [P+1] (int64).  Any pointer may be NULL.  In fixed mode
+ * every call waits for the last layout enqueued outside a graph capture, then
+ * reads the summary that the last layout to run published (after replaying a
+ * graph that holds a layout, wait for the replay before calling). */
 ep_status ep_handle_counts(const ep_handle *h, int64_t *num_expanded, int64_t *num_recv_tokens,
                            int64_t *window_row_base);
 
 /* Outcome of the handle's last layout.  flags receives EP_STATUS_* bits;
  * dropped_rows (may be NULL) the number of rows past a fixed window's end,
- * sum_d max(0, num_expanded[d] - num_worst_rows).  Waits for the layout to
- * finish (in exact mode it already has, and both are always 0).
+ * sum_d max(0, num_expanded[d] - num_worst_rows).  Waits as ep_handle_counts
+ * does and reads the summary afresh on every call, so a graph replay of the
+ * layout is reported once the caller has waited for it (in exact mode the
+ * layout has already finished, and both are always 0).
  * Errors: EP_ERR_NULL, EP_ERR_HANDLE_MISMATCH (no layout), EP_ERR_HIP. */
 #define EP_STATUS_ROUTING 1u   /* ids outside {-1} U [0, E) were seen and treated as unused */
 #define EP_STATUS_TRUNCATED 2u /* some window needed more than num_worst_rows rows            */

@@ -975,12 +975,14 @@ def _edge_value_rows(T, H, seed):
     """bf16 rows whose 128-channel blocks stress the fp8 arithmetic: all subnormal (the
     scale amax / 448 is then an fp32 subnormal), one normal value among subnormals (codes
     that underflow to zero or to E4M3 subnormals), magnitudes spread over many binades, the
-    largest finite bf16 (0x7F7F), and signed zeros."""
+    largest finite bf16 (0x7F7F), signed zeros, and non-finite blocks: a NaN (either sign,
+    quiet or signalling payload) among normal values, +-Inf among normal values, and a
+    block of -Inf only."""
     rng = np.random.default_rng(seed)
     x = np.zeros((T, H), np.uint16)
     for u in range(T):
         for b in range(H // 128):
-            kind = (u + b) % 5
+            kind = (u + b) % 8
             blk = np.zeros(128, np.uint16)
             sign = rng.integers(0, 2, 128).astype(np.uint16) << 15
             if kind == 0:    # all subnormal: exponent 0, random non-zero mantissas
@@ -994,9 +996,18 @@ def _edge_value_rows(T, H, seed):
             elif kind == 3:  # the largest finite bf16 and small neighbours
                 blk = sign | rng.integers(0x3000, 0x4000, 128).astype(np.uint16)
                 blk[rng.integers(0, 128)] = 0x7F7F
-            else:            # signed zeros with one tiny subnormal
+            elif kind == 4:  # signed zeros with one tiny subnormal
                 blk = sign.copy()
                 blk[rng.integers(0, 128)] |= 0x0001
+            elif kind == 5:  # one NaN among normal values
+                blk = sign | rng.integers(0x3000, 0x4000, 128).astype(np.uint16)
+                blk[rng.integers(0, 128)] = int(rng.choice([0x7FC0, 0xFFC0, 0x7F81, 0xFFFF]))
+            elif kind == 6:  # +Inf and -Inf among normal values
+                blk = sign | rng.integers(0x3000, 0x4000, 128).astype(np.uint16)
+                blk[rng.integers(0, 64)] = 0x7F80
+                blk[64 + rng.integers(0, 64)] = 0xFF80
+            else:            # -Inf only
+                blk = np.full(128, 0xFF80, np.uint16)
             x[u, 128 * b:128 * (b + 1)] = blk
     return x
 
@@ -1004,7 +1015,8 @@ def _edge_value_rows(T, H, seed):
 @pytest.mark.parametrize("cm", [False, True], ids=["row-major", "col-major"])
 def test_fp8_dispatch_on_subnormal_and_extreme_values(cm):
     """The fp8 dispatch's scale (amax / 448) and codes (x / scale, E4M3 RNE) on blocks the
-    synthetic workloads never produce, bit for bit against the oracle."""
+    synthetic workloads never produce, bit for bit against the oracle, NaN and Inf blocks
+    included (their scale and codes follow the oracle's stated rule)."""
     w = D["tiny-p4-s64-e16-k2-h512"]
     topk = synth.gen_routing(w)
     x = _edge_value_rows(w.T, w.H, 41)
@@ -1020,6 +1032,7 @@ def test_fp8_dispatch_on_subnormal_and_extreme_values(cm):
     np.testing.assert_array_equal(gs.view(np.uint32), osc.view(np.uint32))
     np.testing.assert_array_equal(rx.cpu().numpy(), ox)
     assert np.any((osc.view(np.uint32) & 0x7F800000) == 0) and np.any(osc > 0)  # subnormal scales were exercised
+    assert np.any(osc.view(np.uint32) == 0x7FC00000) and np.any(osc.view(np.uint32) == 0x7F800000)  # NaN, Inf
     h.free()
 
 
@@ -1206,6 +1219,84 @@ def test_fixed_windows_fp8_graph_replays_with_new_routing():
     h.free()
 
 
+def test_fixed_windows_status_follows_graph_replays():
+    """A fixed-window relayout captured in a graph, replayed with routings copied into the
+    captured input and no eager layout in between: after each replay (and a wait for it),
+    the handle's status and counts are those of that replay's routing, truncation included,
+    and cleared again by the next replay that fits."""
+    w = SMALL[1]
+    fits = synth.gen_routing(w)
+    hot = fits.copy()
+    hot[:, 0] = 0  # every token's first slot to expert 0: rank 0's window overflows
+    lay_fit = oracle.layout(w.P, w.S, w.E, w.K, w.A, fits)
+    lay_hot = oracle.layout(w.P, w.S, w.E, w.K, w.A, hot)
+    W = int(lay_fit.num_expanded.max()) + 16
+    assert int(lay_hot.num_expanded.max()) > W
+    dropped_hot = int(np.maximum(lay_hot.num_expanded - W, 0).sum())
+    topk_d = torch.from_numpy(fits).to(DEV)
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A, num_worst_rows=W), topk_d)
+    torch.cuda.synchronize()
+    assert h.status() == (0, 0)
+    g = torch.cuda.CUDAGraph()
+    say("capture fixed-window relayout")
+    with torch.cuda.graph(g):
+        ep.relayout(h, topk_d)
+    torch.cuda.synchronize()
+    for it, (routing, lay) in enumerate([(hot, lay_hot), (fits, lay_fit), (hot, lay_hot)]):
+        topk_d.copy_(torch.from_numpy(routing).to(DEV))
+        torch.cuda.synchronize()
+        say("status replay", it)
+        g.replay()
+        torch.cuda.synchronize()
+        exp = (ep.STATUS_TRUNCATED, dropped_hot) if routing is hot else (0, 0)
+        assert h.status() == exp, (it, h.status(), exp)
+        ne, nr, _ = h.counts()
+        np.testing.assert_array_equal(ne, lay.num_expanded)
+        np.testing.assert_array_equal(nr, lay.num_recv_tokens)
+        check_fixed_layout(lay, h, W)
+    del g
+    h.free()
+
+
+def test_exact_windows_layout_refuses_graph_capture():
+    """An exact-window layout waits for the row counts on the host, which a captured graph
+    cannot do: relayout on a capturing stream fails before enqueuing anything, and the
+    handle works again after an eager relayout."""
+    w = SMALL[1]
+    topk = synth.gen_routing(w)
+    lay, h = layout_both(w, topk)
+    topk_d = torch.from_numpy(topk).to(DEV)
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(ep.EpError) as ei:
+        with torch.cuda.graph(g):
+            ep.relayout(h, topk_d)
+    assert "captured" in str(ei.value)
+    del g
+    torch.cuda.synchronize()
+    ep.relayout(h, topk_d)
+    torch.cuda.synchronize()
+    check_layout(lay, h)
+    h.free()
+
+
+def test_combine_lds_grid_limit_falls_back_to_register_kernel():
+    """At 2^22 tokens the LDS combine's grid (one 512-thread workgroup per token) would reach
+    2^31 work-items; combine then runs the register kernel, which is correct for every
+    shape.  P=1, S=2^22, E=1, K=1, H=8: dispatch and combine against the oracle."""
+    w = wl.Workload("lds-grid-limit", 1, 1 << 22, 1, 1, 8, 1, True, "uniform", seed=71)
+    topk = np.zeros((w.T, 1), np.int64)
+    topk[::7, 0] = -1  # some unused slots
+    lay, h = layout_both(w, topk)
+    x = synth.gen_bf16_rows(72, wl.STREAM_X, w.T, w.H)
+    wt = np.random.default_rng(73).random((w.T, 1), dtype=np.float32)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    rx, _, _, _ = ep.dispatch(h, xd, wd, zero_padding=True)
+    out = ep.combine(h, rx, wd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_u16(out), oracle.combine_identity(1, w.H, False, topk, x, wt, 0, w.T))
+    h.free()
+
+
 def test_exact_windows_dispatch_and_combine_capture_in_a_graph():
     """With exact windows the layout waits on the host once, so it stays outside; the
     dispatches (bf16 fresh, fp8 cached) and the combine with a bias are captured.  Each replay
@@ -1364,6 +1455,37 @@ def test_combine_on_subnormal_and_extreme_values(H):
     h.free()
 
 
+@pytest.mark.parametrize("H", [512, 4104], ids=["lds-kernel", "register-kernel"])
+def test_combine_on_non_finite_values(H):
+    """Combine with Inf and NaN among the expert rows and one overflowing sum.  Which NaN an
+    fp32 operation returns is the hardware's choice (the host's default NaN is negative, the
+    GPU's positive), so NaN outputs are compared as NaN; every other output, the infinities
+    included, bit for bit against the oracle, through both combine kernels."""
+    P, S, E, K, A = 4, 40, 16, 4, 4
+    w = wl.Workload(f"nonfinite-combine-h{H}", P, S, E, K, H, A, True, "uniform", seed=61)
+    topk = synth.gen_routing(w)
+    lay, h = layout_both(w, topk)
+    rng = np.random.default_rng(62)
+    R = lay.total_rows
+    y = synth.gen_bf16_rows(63, wl.STREAM_X, R, H)
+    pick = rng.random((R, H))
+    y[pick < 0.01] = 0x7F80                                        # +Inf
+    y[(pick >= 0.01) & (pick < 0.02)] = 0xFF80                     # -Inf
+    y[(pick >= 0.02) & (pick < 0.025)] = 0x7FC0                    # NaN
+    y[(pick >= 0.025) & (pick < 0.03)] = 0x7F7F                    # largest finite: sums overflow
+    wt = synth.gen_weights(w)
+    out = ep.combine(h, dev_bf16(y), torch.from_numpy(wt).to(DEV))
+    torch.cuda.synchronize()
+    exp = oracle.combine(lay, H, y, wt)
+    got = host_u16(out)
+    is_nan = lambda a: ((a & 0x7F80) == 0x7F80) & ((a & 0x7F) != 0)  # noqa: E731
+    np.testing.assert_array_equal(is_nan(got), is_nan(exp))
+    fin = ~is_nan(exp)
+    np.testing.assert_array_equal(got[fin], exp[fin])
+    assert is_nan(exp).any() and ((exp & 0x7FFF) == 0x7F80).any()  # NaN and Inf outputs were exercised
+    h.free()
+
+
 def test_relayout_and_free_wait_for_pending_async_calls():
     """An async dispatch reads the handle on the communication stream.  A relayout enqueued
     right after it must not overwrite the arrays under it, and free() must not release them:
@@ -1397,7 +1519,7 @@ def test_relayout_and_free_wait_for_pending_async_calls():
 def test_column_major_fp8_calls_on_two_streams_do_not_share_scratch():
     """fp8 dispatch with column-major scales stages per-token scales in the handle.  An async
     call on the communication stream followed at once by a synchronous one on the current
-    stream must each keep their own scales: the binding orders the second after the first."""
+    stream must each keep their own scales: the library orders the second after the first."""
     w = SMALL[1]
     topk = synth.gen_routing(w)
     wt = synth.gen_weights(w)
@@ -1417,4 +1539,49 @@ def test_column_major_fp8_calls_on_two_streams_do_not_share_scratch():
                                                    scales_col_major=True)
         np.testing.assert_array_equal(rx.cpu().numpy(), ox)
         np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    h.free()
+
+
+def test_column_major_fp8_calls_through_the_c_abi_on_two_streams():
+    """The same ordering without the Python binding's help: two ep_dispatch calls (fp8,
+    column-major scales) on one handle, issued back to back through the C ABI on two
+    unordered streams, the first with a longer queue ahead of it.  Each call's codes and
+    scales must match the oracle for its own x."""
+    import ctypes
+
+    w = SMALL[1]
+    topk = synth.gen_routing(w)
+    wt = synth.gen_weights(w)
+    wd = torch.from_numpy(wt).to(DEV)
+    xs = [synth.gen_bf16_rows(w.seed + 11 + i, wl.STREAM_X, w.T, w.H) for i in range(2)]
+    xds = [dev_bf16(x) for x in xs]
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A), torch.from_numpy(topk).to(DEV))
+    R, nb = h.total_rows, w.H // 128
+    outs = [(torch.empty((R, w.H), dtype=torch.uint8, device=DEV), torch.empty((nb, R), dtype=torch.float32, device=DEV),
+             torch.empty(R, dtype=torch.float32, device=DEV), torch.empty((R, 2), dtype=torch.int32, device=DEV))
+            for _ in range(2)]
+    streams = [torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)]
+    torch.cuda.synchronize()
+    L = ep.lib()
+    flags = 1 | 2 | 4  # EP_DISPATCH_FP8 | EP_DISPATCH_ZERO_PADDING | EP_DISPATCH_SCALES_COL_MAJOR
+    say("two col-major fp8 dispatches through the C ABI on two streams")
+    with torch.cuda.stream(streams[0]):
+        busy = torch.empty(1 << 26, dtype=torch.float32, device=DEV)
+        for _ in range(4):
+            busy.mul_(1.0001)  # work queued ahead of the first call
+    for i in range(2):
+        rx, sc, rw, rm = outs[i]
+        st = L.ep_dispatch(ctypes.c_void_p(h.ptr), flags, ctypes.c_void_p(xds[i].data_ptr()),
+                           ctypes.c_void_p(wd.data_ptr()), ctypes.c_void_p(rx.data_ptr()),
+                           ctypes.c_void_p(sc.data_ptr()), ctypes.c_void_p(rw.data_ptr()),
+                           ctypes.c_void_p(rm.data_ptr()), ctypes.c_void_p(streams[i].cuda_stream))
+        assert st == 0, L.ep_last_error()
+    torch.cuda.synchronize()
+    for i in range(2):
+        ox, osc, _, _, _ = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=True, topk_weights=wt, x=xs[i],
+                                                   scales_col_major=True)
+        np.testing.assert_array_equal(outs[i][0].cpu().numpy(), ox)
+        np.testing.assert_array_equal(outs[i][1].cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    del busy
     h.free()
