@@ -1,24 +1,36 @@
 """Throughput of the MoE dispatch/combine hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of synthetic tokens:
-fresh layout of the routing (ep_relayout: counts, scans, stable ranks, the
-one D->H read of the window sizes), fresh dispatch of x into the expanded
-expert-grouped layout (bf16, with zero padding), identity experts, and the
-weighted combine back to token order.  Inputs are resident in HBM before the
-timed region; the handle and the expanded tensors are long-lived buffers
-reused every step, as the pages recommend for the EP buffer.
+One step = one pass of the whole path over one batch of synthetic tokens.  On
+the default workload (the forward+backward one: P=32 virtual ranks x S=8192
+tokens, E=256, top-8 group-limited routing, hidden 4096) that is: fresh layout
+of the routing (ep_relayout: counts, scans, stable ranks, the one D->H read of
+the window sizes), fresh dispatch of x into the expanded expert-grouped layout
+(bf16, zero padding), identity experts, weighted combine back to token order;
+then the backward with the same handle: cached dispatch of the upstream
+gradient and its weighted combine.  On a workload without a backward the step
+stops after the forward combine.  Inputs are resident in HBM before the timed
+region; the handle and the expanded tensors are long-lived buffers reused
+every step, as the pages recommend for the EP buffer.
 
-The same step is also timed with fixed-length windows (num_worst_rows: every
-window a 1024-row bucket above the largest one, no read-back), reported under
-"fixed_windows"; the headline value is the exact-length step.
+Beside the headline step the JSON line carries:
+  "configs"        every other full-size workload timed per call (HIP events,
+                   median of 20): fresh dispatch, cached dispatch (for the fp8
+                   workload: 20 iterations, each with new x), combine, each
+                   with its ledger bytes and fraction of the HBM peak;
+  "fixed_windows"  the headline forward step with fixed-length windows
+                   (num_worst_rows: a 1024-row bucket above the largest
+                   window, no read-back);
+  "cpu_baseline"   the CPU oracle on the headline workload, on 1 thread and
+                   on N threads (a bounded sample: see cpu_baseline).
 
 Before the timed steps, the outputs of the last warm-up step are checked at
 full size with plain torch ops on a seeded sample of tokens (expanded rows,
-their weights and metadata, zero padding, and the combine bit for bit);
-"parity" in the JSON line says what was checked.
+their weights and metadata, zero padding, and the combine bit for bit, forward
+and backward); "parity" in the JSON line says what was checked.
 
 Prints ONE JSON line.  Usage:
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME] [--no-cpu] [--no-fixed]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME] [--no-cpu]
+                    [--no-fixed] [--no-configs]
 
 `python bench.py --calls` instead times every call of the library on every
 workload (HIP events; median and minimum of 20 calls, each timed alone after
@@ -48,7 +60,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "dispatch & combine payload GB/s + tokens/s on 1 MI355X; % HBM roofline"
-DEFAULT_WORKLOAD = "dsv3-bf16-p8-s4096-e256-k8-h7168"
+DEFAULT_WORKLOAD = "ep32-group-fwdbwd-p32-s8192-e256-k8-h4096"
+# full-size workloads timed per call beside the headline step
+PER_CONFIG = ["dsv3-bf16-p8-s4096-e256-k8-h7168", "dsv3-fp8-p8-s4096-e256-k8-h7168",
+              "ep128-zipf-p128-s1024-e256-k6-h7168"]
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 # the dispatch / combine kernels and their launch configuration: a committed counter
 # summary counts only while these are unchanged
@@ -118,45 +133,103 @@ def traffic_from_profiles(kernel: str, workload: str):
 # CPU baseline: the oracle, as it stands
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(w, topk, x, wt, budget_s: float = 12.0, max_steps: int = 5) -> dict:
-    """The oracle's whole step on the full workload, as the GPU step does it: layout,
-    dispatch of every expanded row, identity experts (y = the dispatched rows), combine
-    of every token.  Repeated until about budget_s seconds have passed (at least once,
-    at most max_steps times); the median step is reported."""
+def host_threads() -> tuple[int, int]:
+    """(threads used, CPUs in the affinity mask): at most 16, one GPU's share of the box."""
+    n = len(os.sched_getaffinity(0))
+    return max(1, min(16, n)), n
+
+
+def cpu_baseline(w, topk, x, g, wt, threads: int) -> dict:
+    """The CPU oracle (oracle/, as it stands) on the headline workload, on 1 thread and on
+    `threads` threads.  Each oracle call is one ctypes call, which releases the GIL, so the
+    threaded leg runs the calls over disjoint row or token ranges in a thread pool.
+
+    Per leg: the layout (one call; the oracle's layout is one sequential pass), the fresh
+    dispatch of every expanded row and, with a backward, the cached dispatch of the gradient,
+    both streamed one destination window per call (a window's rows are produced and dropped,
+    so host memory stays at one window per thread); and the combine (forward and backward)
+    on a bounded sample, the tokens of the first source ranks, whose time is scaled to all T
+    tokens.  The sample's expert rows are filled with the identity experts' outputs (x, or
+    the gradient, at each of their rows) before the timed call."""
     import statistics
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
 
     import oracle
 
-    T = w.T
-    steps = []
-    t_start = time.perf_counter()
-    rows = 0
-    while not steps or (time.perf_counter() - t_start < budget_s and len(steps) < max_steps):
+    T, K, H, P = w.T, w.K, w.H, w.P
+    lay = oracle.layout(P, w.S, w.E, K, w.A, topk)
+    R = lay.total_rows
+    wrb = lay.window_row_base
+    windows = [(int(wrb[d]), int(wrb[d + 1])) for d in range(P)]
+    t_sample = min(T, 4 * w.S)
+    # expert rows of the sampled tokens, and the identity experts' outputs there
+    El = w.E // P
+    tk = topk[:t_sample]
+    valid = tk >= 0
+    rows = (wrb[np.where(valid, tk // El, 0)] + lay.dst_slot[:t_sample])[valid]
+    src = np.broadcast_to(np.arange(t_sample)[:, None], tk.shape)[valid]
+    y = np.empty((R, H), np.uint16)  # only the sampled tokens' rows are ever touched
+
+    def leg(nt: int) -> dict:
+        pool = ThreadPoolExecutor(nt) if nt > 1 else None
+
+        def run(fn, items):
+            if pool is None:
+                for it in items:
+                    fn(it)
+            else:
+                list(pool.map(fn, items))
+
+        sec = {}
         t0 = time.perf_counter()
-        lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
-        t1 = time.perf_counter()
-        rx, _, _, _ = oracle.dispatch(lay, w.H, x, wt, False, w.zero_padding)
-        t2 = time.perf_counter()
-        oracle.combine(lay, w.H, rx, wt)
-        t3 = time.perf_counter()
-        steps.append((t1 - t0, t2 - t1, t3 - t2))
-        rows = lay.total_rows
-        del rx
-    total = time.perf_counter() - t_start
-    step = statistics.median(sum(s) for s in steps)
+        oracle.layout(P, w.S, w.E, K, w.A, topk)
+        sec["layout"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        run(lambda ab: oracle.dispatch(lay, H, x, wt, False, w.zero_padding, ab[0], ab[1]), windows)
+        sec["dispatch"] = time.perf_counter() - t0
+        tok_ranges = [(a, min(t_sample, a + -(-t_sample // nt))) for a in range(0, t_sample, -(-t_sample // nt))]
+        y[rows] = x[src]
+        t0 = time.perf_counter()
+        run(lambda ab: oracle.combine(lay, H, y, wt, ab[0], ab[1]), tok_ranges)
+        sec["combine_sample"] = time.perf_counter() - t0
+        sec["combine"] = sec["combine_sample"] * T / t_sample
+        if w.backward:
+            t0 = time.perf_counter()
+            run(lambda ab: oracle.dispatch(lay, H, g, None, False, w.zero_padding, ab[0], ab[1], with_meta=False),
+                windows)
+            sec["dispatch_cached_grad"] = time.perf_counter() - t0
+            y[rows] = g[src]
+            t0 = time.perf_counter()
+            run(lambda ab: oracle.combine(lay, H, y, wt, ab[0], ab[1]), tok_ranges)
+            sec["combine_grad_sample"] = time.perf_counter() - t0
+            sec["combine_grad"] = sec["combine_grad_sample"] * T / t_sample
+        if pool is not None:
+            pool.shutdown()
+        sec["step"] = sec["layout"] + sec["dispatch"] + sec["combine"] + \
+            sec.get("dispatch_cached_grad", 0.0) + sec.get("combine_grad", 0.0)
+        return {"value": T / sec["step"], "threads": nt, "seconds": sec}
+
+    one = leg(1)
+    many = leg(threads) if threads > 1 else one
+    del y
     cpu_model = None
     try:
         with open("/proc/cpuinfo") as f:
             cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
     except OSError:
         pass
-    return {"value": T / step, "unit": "tokens/s", "cores": 1, "kind": "oracle", "cpu_model": cpu_model,
-            "sample": (f"the whole step on the full workload ({T} tokens, {rows} expanded rows: layout, "
-                       f"dispatch of every row, combine of every token), {len(steps)} repetitions in "
-                       f"{total:.1f} s, median step; single thread"),
-            "seconds": {"layout": statistics.median(s[0] for s in steps),
-                        "dispatch": statistics.median(s[1] for s in steps),
-                        "combine": statistics.median(s[2] for s in steps), "step": step}}
+    _, affinity = host_threads()
+    steps = "layout, dispatch of every expanded row" + (", cached dispatch of the gradient" if w.backward else "")
+    comb = "forward and backward combine" if w.backward else "combine"
+    return {"value": many["value"], "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model, "affinity_cpus": affinity,
+            "sample": (f"headline workload {w.name} ({T} tokens, {R} expanded rows): {steps} in full, one "
+                       f"destination window per call; {comb} on the tokens of the first "
+                       f"{t_sample // max(w.S, 1)} source ranks ({t_sample} tokens), time scaled to all {T}; "
+                       f"value = tokens/s of the whole step on {threads} threads"),
+            "seconds": many["seconds"], "single_thread": one}
 
 
 # ---------------------------------------------------------------------------
@@ -270,6 +343,34 @@ def full_size_check(h, w, x_d, w_d, recv_x, recv_w, recv_m, out, n_sample: int =
         raise AssertionError("dispatch: padding-row metadata is not (-1, -1) / 0")
     return {"sampled_tokens": int(idx.numel()), "rows_checked": int((rows >= 0).sum()),
             "padding_rows_checked": int(pad.numel()), "dispatch_bitwise": True, "combine_bitwise": True}
+
+
+def backward_check(h, w, g_d, w_d, gy, gx, n_sample: int = 4096) -> dict:
+    """The backward's outputs, as full_size_check checks the forward's: for a seeded sample
+    of tokens every expanded row of the cached dispatch holds the token's gradient row bit
+    for bit, and the backward combine equals the in-order fp32 sum of w_j * g (separate
+    multiply and add, from +0) rounded once to bf16, bit for bit.  Raises on a mismatch."""
+    import numpy as np
+    import torch
+
+    T, K = w.T, w.K
+    dev = gy.device
+    dst = h.tensor("dst_row").view(T, K).long()
+    rng = np.random.default_rng(54321)
+    idx = torch.from_numpy(np.sort(rng.choice(T, size=min(n_sample, T), replace=False))).to(dev)
+    rows = dst[idx]
+    acc = torch.zeros((idx.numel(), w.H), dtype=torch.float32, device=dev)
+    gs = g_d[idx]
+    for j in range(K):
+        r = rows[:, j]
+        ok = r >= 0
+        if not torch.equal(gy[r[ok]].view(torch.int16), g_d[idx[ok]].view(torch.int16)):
+            raise AssertionError(f"backward: cached dispatch rows differ from the gradient (slot {j})")
+        acc = torch.where(ok[:, None], acc + w_d[idx, j:j + 1] * gs.float(), acc)
+    if not torch.equal(gx[idx].view(torch.int16), acc.to(torch.bfloat16).view(torch.int16)):
+        raise AssertionError("backward: combine differs from the in-order fp32 sum rounded to bf16")
+    return {"sampled_tokens": int(idx.numel()), "rows_checked": int((rows >= 0).sum()),
+            "dispatch_cached_bitwise": True, "combine_bitwise": True}
 
 
 def device_ceilings(dev) -> dict:
@@ -556,6 +657,93 @@ def overlap_table(workload: str, steps: int) -> int:
 
 
 # ---------------------------------------------------------------------------
+# the other full-size workloads, per call
+# ---------------------------------------------------------------------------
+
+def per_config(name: str, reps: int) -> dict:
+    """One full-size workload timed per call (HIP events on the launch stream, each call
+    alone between two synchronisations after 3 untimed ones, median of `reps`): fresh
+    dispatch (the workload's dtype), cached dispatch, combine.  A workload with cached
+    iterations times each of them with its own new x (drawn on the device, resident before
+    timing).  Fractions use the same ledger as the headline."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import combine_topk_idx_expert_amd as ep
+    import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.CONFIGS[name]
+    T, K, H = w.T, w.K, w.H
+    log("per-call workload", name)
+    topk = synth.gen_routing(w)
+    topk_d = torch.from_numpy(topk).to(dev)
+    x_d = torch.from_numpy(synth.gen_x(w).view(np.int16)).to(dev).view(torch.bfloat16)
+    w_d = torch.from_numpy(synth.gen_weights(w)).to(dev)
+    h = ep.get_layout(ep.Config(w.P, w.S, H, K, w.E, w.A), topk_d)
+    R = h.total_rows
+    rows = int((topk >= 0).sum())
+    pad = R - rows
+    fp8, nb = w.fp8, H // 128
+    b = 1 if fp8 else 2
+    sf = 4 * nb if fp8 else 0
+    led = ledger(T, K, H, rows, pad, fp8, w.zero_padding)
+    cached_bytes = T * H * 2 + 4 * T * K + rows * (H * b + sf) + (pad * (H * b + sf) if w.zero_padding else 0)
+    rx = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    sc = torch.empty((R, nb), dtype=torch.float32, device=dev) if fp8 else None
+    rw = torch.empty(R, dtype=torch.float32, device=dev)
+    rm = torch.empty((R, 2), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    r = {"workload": name, "T": T, "rows": rows, "padding_rows": pad, "dtype": "fp8" if fp8 else "bf16"}
+
+    def put(key, us, nbytes):
+        r[key + "_us"] = us
+        r[key + "_GBps"] = nbytes / us / 1e3
+        r[key + "_frac_hbm"] = nbytes / us / 1e3 / HBM_PEAK_GBPS
+        r[key + "_tokens_per_s"] = T / (us * 1e-6)
+        r[key + "_bytes"] = nbytes
+
+    put("dispatch", _median_us(lambda: ep.dispatch(h, x_d, w_d, fp8, w.zero_padding, out=(rx, sc, rw, rm)), reps),
+        led["dispatch"])
+    if w.cached_iters:
+        # new x for every iteration, drawn on the device with a seeded generator
+        xs = []
+        for it in range(1, w.cached_iters + 1):
+            gen = torch.Generator(device=dev).manual_seed(1000 + it)
+            xs.append(torch.randn((T, H), generator=gen, device=dev).to(torch.bfloat16))
+        for xi in xs[:3]:  # untimed
+            ep.dispatch_cached(h, xi, fp8, w.zero_padding, out=(rx, sc))
+        torch.cuda.synchronize()
+        ts = []
+        for xi in xs:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ep.dispatch_cached(h, xi, fp8, w.zero_padding, out=(rx, sc))
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        put("cached", statistics.median(ts), cached_bytes)
+        r["cached_iterations"] = len(ts)
+        r["cached_us_each"] = [round(t, 1) for t in ts]
+        del xs
+    else:
+        put("cached", _median_us(lambda: ep.dispatch_cached(h, x_d, fp8, w.zero_padding, out=(rx, sc)), reps),
+            cached_bytes)
+    if fp8:  # expert outputs in bf16 for the combine
+        gen = torch.Generator(device=dev).manual_seed(77)
+        y = torch.randn((R, H), generator=gen, device=dev).to(torch.bfloat16)
+    else:
+        y = rx  # identity experts
+    put("combine", _median_us(lambda: ep.combine(h, y, w_d, out=out), reps), led["combine"])
+    h.free()
+    del rx, sc, rw, rm, out, y, x_d
+    torch.cuda.empty_cache()
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+
+
+# ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
 
@@ -567,6 +755,7 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-fixed", action="store_true", help="skip the fixed-length-window leg")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-call legs of the other workloads")
     ap.add_argument("--calls", action="store_true", help="per-call table over all workloads")
     ap.add_argument("--overlap", action="store_true", help="dispatch overlapped with shared experts")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -593,6 +782,7 @@ def main() -> int:
     torch.cuda.set_device(dev)
     w = synth.CONFIGS[args.workload]
     T, K, H = w.T, w.K, w.H
+    bwd = w.backward
 
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
@@ -606,9 +796,11 @@ def main() -> int:
     topk = synth.gen_routing(w)
     x = synth.gen_x(w)
     wt = synth.gen_weights(w)
+    g = synth.gen_grad_out(w) if bwd else None
     topk_d = torch.from_numpy(topk).to(dev)
     x_d = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
     w_d = torch.from_numpy(wt).to(dev)
+    g_d = torch.from_numpy(g.view(np.int16)).to(dev).view(torch.bfloat16) if bwd else None
 
     h = ep.get_layout(ep.Config(w.P, w.S, H, K, w.E, w.A), topk_d)
     R = h.total_rows
@@ -619,7 +811,10 @@ def main() -> int:
     recv_w = torch.empty(R, dtype=torch.float32, device=dev)
     recv_m = torch.empty((R, 2), dtype=torch.int32, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    gy = torch.empty((R, H), dtype=torch.bfloat16, device=dev) if bwd else None
+    gx = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if bwd else None
     stream = torch.cuda.current_stream(dev)
+    n_ev = 5 if bwd else 3
 
     def step(ev=None):
         ep.relayout(h, topk_d)
@@ -631,18 +826,32 @@ def main() -> int:
         ep.combine(h, recv_x, w_d, out=out)  # identity experts: y = recv_x
         if ev is not None:
             ev[2].record(stream)
+        if bwd:  # backward with the same handle: dispatch of the gradient, then its combine
+            ep.dispatch_cached(h, g_d, fp8=False, zero_padding=w.zero_padding, out=(gy, None))
+            if ev is not None:
+                ev[3].record(stream)
+            ep.combine(h, gy, w_d, out=gx)
+            if ev is not None:
+                ev[4].record(stream)
 
     log("warmup", args.warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    def checks():
+        c = full_size_check(h, w, x_d, w_d, recv_x, recv_w, recv_m, out)
+        if bwd:
+            c["backward"] = backward_check(h, w, g_d, w_d, gy, gx)
+        torch.cuda.synchronize()
+        return c
+
     check = None
     if args.warmup > 0:  # otherwise checked after the timed steps
         log("full-size check of the last warm-up step's outputs")
-        check = full_size_check(h, w, x_d, w_d, recv_x, recv_w, recv_m, out)
-        torch.cuda.synchronize()
+        check = checks()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     log("timing", args.steps, "steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -652,24 +861,58 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     if check is None:
         log("full-size check of the last timed step's outputs")
-        check = full_size_check(h, w, x_d, w_d, recv_x, recv_w, recv_m, out)
-    d_ms = [e[0].elapsed_time(e[1]) for e in events]
-    c_ms = [e[1].elapsed_time(e[2]) for e in events]
+        check = checks()
+
+    def avg_us(i0, i1):
+        v = [1e3 * e[i0].elapsed_time(e[i1]) for e in events]
+        return sum(v) / len(v), sorted(v)[len(v) // 2], min(v)
 
     ms_step = elapsed * 1e3 / args.steps
     led = ledger(T, K, H, rows_valid, pad, False, w.zero_padding)
-    d_us = 1e3 * sum(d_ms) / len(d_ms)
-    c_us = 1e3 * sum(c_ms) / len(c_ms)
-    d_gbps = led["dispatch"] / (d_us * 1e3)
-    c_gbps = led["combine"] / (c_us * 1e3)
-    layout_us = ms_step * 1e3 - d_us - c_us
-    dominant = "dispatch" if d_us >= c_us else "combine"
-    dom_kernel = "dispatch_kernel" if dominant == "dispatch" else "combine_kernel"
-    dom_bytes = led[dominant]
-    dom_us = d_us if dominant == "dispatch" else c_us
+    cached_bytes = T * H * 2 + 4 * T * K + rows_valid * H * 2 + (pad * H * 2 if w.zero_padding else 0)
+    d_us, d_med, d_min = avg_us(0, 1)
+    c_us, c_med, c_min = avg_us(1, 2)
+    launches = {"dispatch": (d_us, led["dispatch"]), "combine": (c_us, led["combine"])}
+    calls = {"dispatch_us": d_us, "dispatch_us_median": d_med, "dispatch_us_min": d_min,
+             "combine_us": c_us, "combine_us_median": c_med, "combine_us_min": c_min}
+    kernel_us = d_us + c_us
+    if bwd:
+        dc_us, dc_med, dc_min = avg_us(2, 3)
+        cb_us, cb_med, cb_min = avg_us(3, 4)
+        launches["dispatch_cached_grad"] = (dc_us, cached_bytes)
+        launches["combine_grad"] = (cb_us, led["combine"])
+        calls.update({"dispatch_cached_grad_us": dc_us, "dispatch_cached_grad_us_median": dc_med,
+                      "dispatch_cached_grad_us_min": dc_min, "combine_grad_us": cb_us,
+                      "combine_grad_us_median": cb_med, "combine_grad_us_min": cb_min})
+        kernel_us += dc_us + cb_us
+    for k, (us, nbytes) in launches.items():
+        calls[k + "_bytes"] = nbytes
+        calls[k + "_GBps"] = nbytes / (us * 1e3)
+        calls[k + "_frac_hbm"] = nbytes / (us * 1e3) / HBM_PEAK_GBPS
+        calls[k + "_tokens_per_s"] = T / (us * 1e-6)
+    calls["layout_us_incl_host_sync"] = ms_step * 1e3 - kernel_us
+    calls["page_style_payload_GBps_dispatch"] = page_style_payload(int(num_recv.sum()), T, K, H, False) / (d_us * 1e3)
+    calls["expanded_rows"] = R
+    calls["padding_rows"] = pad
+
+    # The dominant kernel: the kernel function with the largest share of the step's kernel
+    # time (dispatch_kernel runs the fresh and the cached dispatch, combine the forward and
+    # the backward combine).  Its roofline point is its algorithmic bytes per launch over its
+    # average launch duration, both averaged over its launches in the step.
+    fam = {"dispatch": [k for k in launches if k.startswith("dispatch")],
+           "combine": [k for k in launches if k.startswith("combine")]}
+    fam_us = {f: sum(launches[k][0] for k in ks) for f, ks in fam.items()}
+    dominant = max(fam_us, key=fam_us.get)
+    ks = fam[dominant]
+    dom_us = fam_us[dominant] / len(ks)
+    dom_bytes = sum(launches[k][1] for k in ks) / len(ks)
     achieved = dom_bytes / (dom_us * 1e3)
+    combine_kernel = "combine_lds_kernel" if (K <= 8 and H <= 4096) else "combine_kernel"
+    dom_kernel = "dispatch_kernel" if dominant == "dispatch" else combine_kernel
     traffic = traffic_from_profiles(dom_kernel, w.name)
-    payload = page_style_payload(int(num_recv.sum()), T, K, H, False)
+    step_desc = "relayout + dispatch(bf16) + identity + combine(fp32 acc)"
+    if bwd:
+        step_desc += " + dispatch_cached(grad) + combine(grad)"
 
     result = {
         "metric": METRIC,
@@ -685,35 +928,29 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "P": w.P, "S": w.S, "T": T, "E": w.E, "K": K, "H": H, "A": w.A,
-                   "routing": w.routing, "zero_padding": w.zero_padding, "seed": w.seed,
-                   "step": "relayout + dispatch(bf16) + identity + combine(fp32 acc)"},
-        "roofline": {"bound": "hbm", "kernel": dom_kernel, "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": dom_us},
-        "calls": {
-            "layout_us_incl_host_sync": layout_us,
-            "dispatch_us": d_us, "combine_us": c_us,
-            "dispatch_us_median": 1e3 * sorted(d_ms)[len(d_ms) // 2], "dispatch_us_min": 1e3 * min(d_ms),
-            "combine_us_median": 1e3 * sorted(c_ms)[len(c_ms) // 2], "combine_us_min": 1e3 * min(c_ms),
-            "dispatch_GBps": d_gbps, "combine_GBps": c_gbps,
-            "dispatch_frac_hbm": d_gbps / HBM_PEAK_GBPS, "combine_frac_hbm": c_gbps / HBM_PEAK_GBPS,
-            "dispatch_bytes": led["dispatch"], "combine_bytes": led["combine"],
-            "dispatch_tokens_per_s": T / (d_us * 1e-6), "combine_tokens_per_s": T / (c_us * 1e-6),
-            "page_style_payload_GBps_dispatch": payload / (d_us * 1e3),
-            "expanded_rows": R, "padding_rows": pad,
-        },
+                   "routing": w.routing, "zero_padding": w.zero_padding, "seed": w.seed, "step": step_desc},
+        "roofline": {"bound": "hbm", "kernel": dom_kernel, "launches": ks, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": dom_us,
+                     "share_of_step_kernel_time": fam_us[dominant] / kernel_us},
+        "calls": calls,
+        "parity": check,
     }
-
-    result["parity"] = check
     result["device"] = device_ceilings(dev)
 
     if not args.no_fixed:
         result["fixed_windows"] = fixed_leg(ep, h, w, topk, topk_d, x_d, w_d, out, args.steps, args.warmup)
+    h.free()
+    del recv_x, recv_w, recv_m, out, gy, gx, x_d, g_d
+    torch.cuda.empty_cache()
+
+    if not args.no_configs:
+        result["configs"] = [per_config(n, 20) for n in PER_CONFIG if n != w.name]
 
     if not args.no_cpu:
-        log("cpu baseline (oracle, one thread)")
-        result["cpu_baseline"] = cpu_baseline(w, topk, x, wt)
-    h.free()
+        nt, _ = host_threads()
+        log(f"cpu baseline (oracle, 1 and {nt} threads)")
+        result["cpu_baseline"] = cpu_baseline(w, topk, x, g, wt, nt)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -327,17 +327,55 @@ def dequant_identity(rx: torch.Tensor, sc: torch.Tensor) -> torch.Tensor:
     return (f * sc.repeat_interleave(128, dim=1)).to(torch.bfloat16)
 
 
+def oracle_threads() -> int:
+    """Host threads for the oracle at full size: the affinity mask, at most 16 (one GPU's
+    share of the box).  ctypes releases the GIL during each oracle call, so a thread pool
+    over row or token ranges runs them in parallel."""
+    import os
+
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_over_ranges(fn, n: int, out: np.ndarray, pieces_per_thread: int = 4):
+    """out[a:b] = fn(a, b) over contiguous ranges of [0, n), in a thread pool."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    nt = oracle_threads()
+    step = max(1, -(-n // (nt * pieces_per_thread)))
+
+    def run(a):
+        b = min(n, a + step)
+        out[a:b] = fn(a, b)
+
+    with ThreadPoolExecutor(nt) as ex:
+        list(ex.map(run, range(0, n, step)))
+    return out
+
+
 def quantize_all(x: np.ndarray, H: int):
-    codes = np.empty((x.shape[0], H), np.uint8)
-    scales = np.empty((x.shape[0], H // 128), np.float32)
-    for u in range(x.shape[0]):
-        codes[u], scales[u] = oracle.quantize_row(x[u])
+    """The oracle's per-token fp8 encoding of every row of x (threaded over row ranges)."""
+    T = x.shape[0]
+    codes = np.empty((T, H), np.uint8)
+    scales = np.empty((T, H // 128), np.float32)
+    oracle_over_ranges(lambda a, b: oracle.quantize_rows(x, H, a, b)[0], T, codes)
+    oracle_over_ranges(lambda a, b: oracle.quantize_rows(x, H, a, b)[1], T, scales)
     return codes, scales
 
 
+def combine_identity_all(K, H, fp8, topk, x, wt, bias=None):
+    """The oracle's combine(identity(dispatch(x))) for every token (threaded over token ranges)."""
+    T = topk.shape[0]
+    out = np.empty((T, H), np.uint16)
+    return oracle_over_ranges(lambda a, b: oracle.combine_identity(K, H, fp8, topk, x, wt, a, b, bias=bias), T, out)
+
+
 def check_payload_rows(rx, x_dev, lay, fp8, codes=None, scales=None, sc=None, chunk=4096):
-    """Every valid slot's row equals its token's row (bf16) or the oracle's codes (fp8)."""
+    """Every valid slot's row equals its token's row (bf16) or the oracle's codes and scales
+    (fp8), compared on the device: the oracle's per-token codes and scales are uploaded and
+    gathered by token next to the rows gathered by slot."""
     El = lay.E // lay.P
+    codes_d = torch.from_numpy(codes).to(DEV) if fp8 else None
+    scales_d = torch.from_numpy(scales.view(np.int32)).to(DEV) if fp8 else None
     for u0 in range(0, lay.T, chunk):
         u1 = min(lay.T, u0 + chunk)
         tk = lay.topk_idx[u0:u1]
@@ -352,9 +390,9 @@ def check_payload_rows(rx, x_dev, lay, fp8, codes=None, scales=None, sc=None, ch
                 exp = gather_rows(x_dev, us)
                 assert torch.equal(got.view(torch.int16), exp.view(torch.int16)), (u0, j)
             else:
-                np.testing.assert_array_equal(got.cpu().numpy(), codes[us], err_msg=f"codes {u0} {j}")
-                np.testing.assert_array_equal(gather_rows(sc, rows).cpu().numpy().view(np.uint32),
-                                              scales[us].view(np.uint32), err_msg=f"scales {u0} {j}")
+                assert torch.equal(got, gather_rows(codes_d, us)), f"codes {u0} {j}"
+                assert torch.equal(gather_rows(sc, rows).view(torch.int32), gather_rows(scales_d, us)), \
+                    f"scales {u0} {j}"
 
 
 FULL = [D[n] for n in wl.CONFIG_ORDER]
@@ -389,38 +427,37 @@ def test_full_size(w):
     say("payload rows", w.name)
     check_payload_rows(rx, xd, lay, fp8, codes, scales, sc)
 
-    # combine(identity(dispatch(x))) against the oracle's composition
-    step = 1 if w.T <= 40000 else 8
-    toks = np.arange(0, w.T, step)
-    say("combine", w.name, "tokens", len(toks))
+    # combine(identity(dispatch(x))) against the oracle's composition, every token
+    say("combine", w.name, "tokens", w.T, "oracle threads", oracle_threads())
     y = dequant_identity(rx, sc) if fp8 else rx
     out = ep.combine(h, y, wd)
     torch.cuda.synchronize()
-    got = host_u16(gather_rows(out, toks)) if step > 1 else host_u16(out)
-    exp = np.concatenate([oracle.combine_identity(w.K, w.H, fp8, topk, x, wt, u, u + 1)
-                          for u in toks]) if step > 1 else \
-        oracle.combine_identity(w.K, w.H, fp8, topk, x, wt, 0, w.T)
+    got = host_u16(out)
+    exp = combine_identity_all(w.K, w.H, fp8, topk, x, wt)
     assert ulp_diff(got, exp).max() <= 1
     np.testing.assert_array_equal(got, exp)
-    del y, out
+    del y, out, got, exp
 
     if w.cached_iters:
+        # every cached iteration's payload against the oracle's encoding of its own x
         say("cached iterations", w.cached_iters)
         cx, csc = torch.empty_like(rx), (torch.empty_like(sc) if fp8 else None)
+        pad_d = torch.from_numpy(pad.astype(np.int64)).to(DEV)
         for it in range(1, w.cached_iters + 1):
             xi = synth.workloads.gen_cached_x(w, it)
             xid = dev_bf16(xi)
+            cx.fill_(0x5A if fp8 else 1)  # stale bytes must not survive
+            if fp8:
+                csc.fill_(7.0)
             ep.dispatch_cached(h, xid, fp8=fp8, zero_padding=w.zero_padding, out=(cx, csc))
-            if it in (1, w.cached_iters):
-                ci, si = quantize_all(xi, w.H) if fp8 else (None, None)
-                check_payload_rows(cx, xid, lay, fp8, ci, si, csc)
-            else:
-                fx, fsc, _, _ = ep.dispatch(h, xid, wd, fp8=fp8, zero_padding=w.zero_padding)
-                assert torch.equal(fx.view(torch.uint8), cx.view(torch.uint8))
-                if fp8:
-                    assert torch.equal(fsc[~torch.from_numpy(om[:, 0] < 0).to(DEV)].view(torch.int32),
-                                       csc[~torch.from_numpy(om[:, 0] < 0).to(DEV)].view(torch.int32))
             torch.cuda.synchronize()
+            ci, si = quantize_all(xi, w.H) if fp8 else (None, None)
+            check_payload_rows(cx, xid, lay, fp8, ci, si, csc)
+            if w.zero_padding and len(pad):
+                assert int(cx.view(torch.uint8).index_select(0, pad_d).max()) == 0, it
+                if fp8:
+                    assert float(csc.index_select(0, pad_d).abs().max()) == 0.0, it
+            del xid
 
     if w.backward:
         say("backward", w.name)
@@ -430,10 +467,12 @@ def test_full_size(w):
         check_payload_rows(gy, gd, lay, False)
         gx = ep.combine(h, gy, wd)
         torch.cuda.synchronize()
-        toks = np.arange(0, w.T, 8)
-        got = host_u16(gather_rows(gx, toks))
-        exp = np.concatenate([oracle.combine_identity(w.K, w.H, False, topk, g, wt, u, u + 1) for u in toks])
+        say("backward combine, every token")
+        got = host_u16(gx)
+        exp = combine_identity_all(w.K, w.H, False, topk, g, wt)
+        assert ulp_diff(got, exp).max() <= 1
         np.testing.assert_array_equal(got, exp)
+        del gy, gx, got, exp
     h.free()
     del rx, sc, rw, rm, xd
     torch.cuda.empty_cache()
@@ -757,6 +796,10 @@ def test_async_with_compute_stream_matches_sync(fp8, mode):
     bias = dev_bf16(synth.gen_bf16_rows(w.seed, wl.STREAM_GRAD_OUT, w.T, w.H))
     ref_out = ep.combine(h, y, wd, bias=bias)
     torch.cuda.synchronize()
+    ox, osc, ow, om, dropped = oracle.dispatch_general(lay, w.H, fp8=fp8, zero_padding=True, topk_weights=wt, x=x,
+                                                       capacity=W)
+    assert dropped == 0
+    oout = oracle.combine_general(lay, w.H, host_u16(y), wt, bias=host_u16(bias), capacity=W)
     a = torch.randn((2048, 2048), device=DEV)
     for it in range(3):
         say("async", mode, "fp8" if fp8 else "bf16", "iteration", it)
@@ -777,6 +820,15 @@ def test_async_with_compute_stream_matches_sync(fp8, mode):
             if r is not None:
                 assert torch.equal(r.view(torch.uint8), g.view(torch.uint8))
         assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+        # and every async output against the oracle itself
+        np.testing.assert_array_equal(got[0].cpu().numpy() if fp8 else host_u16(got[0]), ox)
+        np.testing.assert_array_equal(got_c[0].cpu().numpy() if fp8 else host_u16(got_c[0]), ox)
+        if fp8:
+            np.testing.assert_array_equal(got[1].cpu().numpy().view(np.uint32), osc.view(np.uint32))
+            np.testing.assert_array_equal(got_c[1].cpu().numpy().view(np.uint32), osc.view(np.uint32))
+        np.testing.assert_array_equal(got[2].cpu().numpy().view(np.uint32), ow.view(np.uint32))
+        np.testing.assert_array_equal(got[3].cpu().numpy(), om)
+        np.testing.assert_array_equal(host_u16(out), oout)
     assert torch.isfinite(busy).any()
     h.free()
 
