@@ -122,6 +122,7 @@ def lib() -> ctypes.CDLL:
         L.ep_get_layout.argtypes = [ctypes.POINTER(_Config), vp, vp, ctypes.POINTER(vp), ctypes.POINTER(i64)]
         L.ep_relayout.argtypes = [vp, vp, vp, ctypes.POINTER(i64)]
         L.ep_dispatch.argtypes = [vp, u32, vp, vp, vp, vp, vp, vp, vp]
+        L.ep_dispatch_noalloc.argtypes = [vp, u32, vp, vp, vp, vp, vp, vp, vp]
         L.ep_dispatch_cached.argtypes = [vp, u32, vp, vp, vp, vp]
         L.ep_dispatch_prequant.argtypes = [vp, u32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.ep_dispatch_prequant_cached.argtypes = [vp, u32, vp, vp, vp, vp, vp]
@@ -133,7 +134,8 @@ def lib() -> ctypes.CDLL:
         L.ep_handle_counts.argtypes = [vp, vp, vp, vp]
         L.ep_handle_status.argtypes = [vp, ctypes.POINTER(u32), ctypes.POINTER(i64)]
         L.ep_handle_tensor.argtypes = [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(i32)]
-        for fn in ("ep_get_layout", "ep_relayout", "ep_dispatch", "ep_dispatch_cached", "ep_dispatch_prequant",
+        for fn in ("ep_get_layout", "ep_relayout", "ep_dispatch", "ep_dispatch_noalloc", "ep_dispatch_cached",
+                   "ep_dispatch_prequant",
                    "ep_dispatch_prequant_cached", "ep_combine",
                    "ep_handle_config", "ep_handle_check", "ep_handle_counts", "ep_handle_status",
                    "ep_handle_tensor"):

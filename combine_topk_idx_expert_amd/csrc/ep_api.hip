@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "ep_mi355x.h"
@@ -371,10 +372,43 @@ ep_status check_device(const ep_handle* h) {
 
 #include "ep_launch.hpp"
 
+}  // namespace
+
+// Staging memory of ep_dispatch_noalloc: the per-token fp8 scales that the
+// column-major scale pass reads, in a fixed array that every GPU the library
+// runs on holds until the process ends.  Host code never uses this name as an
+// address (on the host it is only a stand-in): the device address comes from
+// hipGetSymbolAddress, once per device, in noalloc_scratch().
+static __device__ __align__(256) float scratch[EP_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, then kept).
+ep_status noalloc_scratch(int device, float** out) {
+  if (device < 0 || device >= kMaxDevices) return fail(EP_ERR_HIP, "device %d beyond the library's table", device);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(EP_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", device, hipGetErrorString(e));
+    g_scratch_dev[device] = (float*)p;
+  }
+  *out = g_scratch_dev[device];
+  return EP_OK;
+}
+
 // x: bf16 [T][H]; or, with prequant, E4M3 codes [T][H] and x_scales [T][H/128].
+// staging: where the column-major fp8 path stages per-token scales (null: the
+// handle's tok_scales, ordered across calls by the handle's event).
 ep_status dispatch_common(const ep_handle* h, uint32_t flags, const void* x, const float* x_scales, bool prequant,
                           const float* w, void* recv_x, float* recv_scales, float* recv_weights,
-                          int32_t* recv_meta, bool meta, hipStream_t s) {
+                          int32_t* recv_meta, bool meta, hipStream_t s, float* staging = nullptr) {
   ep_status st = check_handle(h);
   if (st == EP_OK) st = check_device(h);
   if (st != EP_OK) return st;
@@ -429,6 +463,10 @@ ep_status dispatch_common(const ep_handle* h, uint32_t flags, const void* x, con
     a.x = nullptr;
     a.tok_scales = const_cast<float*>(x_scales);  // read only: the rows' scales come from here
     return meta ? launch_dispatch_mode<true, true, true>(a, s) : launch_dispatch_mode<true, false, true>(a, s);
+  }
+  if (fp8 && a.scales_cm && staging) {
+    a.tok_scales = staging;  // the caller's fixed staging: no handle state, no ordering
+    return meta ? launch_dispatch_mode<true, true, false>(a, s) : launch_dispatch_mode<true, false, false>(a, s);
   }
   if (fp8 && a.scales_cm) {
     // The per-token scales are staged in the handle's tok_scales: order this
@@ -497,6 +535,25 @@ ep_status ep_dispatch(const ep_handle* h, uint32_t flags, const void* x, const f
                       void* stream) {
   return dispatch_common(h, flags, x, nullptr, false, topk_weights, recv_x, recv_scales, recv_weights,
                          recv_src_meta, true, (hipStream_t)stream);
+}
+
+ep_status ep_dispatch_noalloc(const ep_handle* h, uint32_t flags, const void* x, const float* topk_weights,
+                              void* recv_x, float* recv_scales, float* recv_weights, int32_t* recv_src_meta,
+                              void* stream) {
+  ep_status st = check_handle(h);
+  if (st == EP_OK) st = check_device(h);
+  if (st != EP_OK) return st;
+  float* staging = nullptr;
+  if ((flags & EP_DISPATCH_FP8) && (flags & EP_DISPATCH_SCALES_COL_MAJOR) && h->cfg.hidden % 128 == 0) {
+    const int64_t need = h->T * (h->cfg.hidden / 128) * (int64_t)sizeof(float);
+    if (need > (int64_t)EP_NOALLOC_SCRATCH_BYTES)
+      return fail(EP_ERR_OVERFLOW,
+                  "ep_dispatch_noalloc stages T * H/128 fp32 scales (%lld bytes), beyond its fixed %lld-byte array",
+                  (long long)need, (long long)EP_NOALLOC_SCRATCH_BYTES);
+    if (st = noalloc_scratch(h->device, &staging); st != EP_OK) return st;
+  }
+  return dispatch_common(h, flags, x, nullptr, false, topk_weights, recv_x, recv_scales, recv_weights,
+                         recv_src_meta, true, (hipStream_t)stream, staging);
 }
 
 ep_status ep_dispatch_cached(const ep_handle* h, uint32_t flags, const void* x, void* recv_x,

@@ -189,6 +189,24 @@ ep_status ep_dispatch(const ep_handle *h, uint32_t flags, const void *x, const f
                       void *recv_x, float *recv_scales, float *recv_weights,
                       int32_t *recv_src_meta, void *stream);
 
+/* ep_dispatch_noalloc -- ep_dispatch for callers that cannot allocate device
+ * memory: code under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, flags, outputs and errors as ep_dispatch, and
+ * it calls no allocating routine.  The one difference is where the fp8
+ * column-major path (EP_DISPATCH_FP8 | EP_DISPATCH_SCALES_COL_MAJOR) stages
+ * its per-token scales: a fixed array of EP_NOALLOC_SCRATCH_BYTES that the
+ * library keeps on every device it runs on until the process ends, instead
+ * of the handle.  The first call on a device looks up that array's address.
+ * Every call on one GPU shares the array, so two such calls that may overlap
+ * on one GPU (other streams, other handles) race and must be ordered by the
+ * caller; the handle's own ordering of ep_dispatch calls does not cover them.
+ * Extra error: EP_ERR_OVERFLOW when T * (H/128) * 4 bytes exceed the array
+ * (fp8 column-major only; other flags stage nothing). */
+#define EP_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)
+ep_status ep_dispatch_noalloc(const ep_handle *h, uint32_t flags, const void *x, const float *topk_weights,
+                              void *recv_x, float *recv_scales, float *recv_weights,
+                              int32_t *recv_src_meta, void *stream);
+
 /* ep_dispatch_cached -- dispatch with a cached handle: the same routing, new
  * x; only the payload (and fp8 scales) move, padding is re-zeroed when asked
  * ("Ascend DeepEP MoE Dispatch Optimization", section "Entering the real call
