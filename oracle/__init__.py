@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_combine_identity.restype = i32
         L.oracle_quantize_row.argtypes = [P_, i32, P_, P_]
         L.oracle_quantize_row.restype = None
+        L.oracle_quantize_row_ue8m0.argtypes = [P_, i32, P_, P_]
+        L.oracle_quantize_row_ue8m0.restype = None
         L.oracle_quantize_rows.argtypes = [P_, i32, i64, i64, P_, P_]
         L.oracle_quantize_rows.restype = None
         for fn in ("oracle_e4m3_encode_array", "oracle_e4m3_decode_array", "oracle_bf16_round_array"):
@@ -230,11 +232,14 @@ def dispatch_fixed(lay: Layout, H: int, capacity: int, x: np.ndarray | None,
 def dispatch_general(lay: Layout, H: int, *, fp8: bool, zero_padding: bool, topk_weights=None,
                      x: np.ndarray | None = None, x_codes: np.ndarray | None = None,
                      x_scales: np.ndarray | None = None, capacity: int = 0, scales_col_major: bool = False,
-                     row_begin: int = 0, row_end: int | None = None, with_meta: bool = True, fill: int = 0):
+                     scales_ue8m0: bool = False, row_begin: int = 0, row_end: int | None = None,
+                     with_meta: bool = True, fill: int = 0):
     """``oracle_dispatch_general``: exact (capacity 0) or fixed windows, row- or column-major
     scales, fused quantisation of x or pre-quantised (x_codes, x_scales).
     -> (recv_x, recv_scales, recv_weights, recv_src_meta, dropped_rows); recv_scales is
-    [n, H/128], or [H/128, n] when scales_col_major."""
+    [n, H/128] fp32, or [H/128, n] when scales_col_major, or UE8M0 bytes [n, H/32] (uint8)
+    when scales_ue8m0."""
+    assert not (scales_ue8m0 and scales_col_major)
     total = lay.P * capacity if capacity > 0 else lay.total_rows
     if row_end is None:
         row_end = total
@@ -245,7 +250,9 @@ def dispatch_general(lay: Layout, H: int, *, fp8: bool, zero_padding: bool, topk
     xs = None if x_scales is None else np.ascontiguousarray(x_scales, dtype=np.float32).reshape(lay.T, H // 128)
     recv_x = np.full((n, H), fill, np.uint8 if fp8 else np.uint16) if payload else None
     recv_scales = None
-    if fp8 and payload:
+    if fp8 and payload and scales_ue8m0:  # exponent bytes start as `fill`, like the codes
+        recv_scales = np.full((n, H // 32), fill, np.uint8)
+    elif fp8 and payload:
         recv_scales = np.zeros((H // 128, n) if scales_col_major else (n, H // 128), np.float32)
     recv_w = np.zeros(n, np.float32) if with_meta else None
     recv_meta = np.zeros((n, 2), np.int32) if with_meta else None
@@ -253,7 +260,8 @@ def dispatch_general(lay: Layout, H: int, *, fp8: bool, zero_padding: bool, topk
     assert w is not None or not with_meta, "row metadata needs topk_weights"
     dropped = np.zeros(1, np.int64)
     st = lib().oracle_dispatch_general(
-        lay.P, lay.S, lay.E, lay.K, H, lay.A, int(fp8), int(zero_padding), int(scales_col_major), capacity,
+        lay.P, lay.S, lay.E, lay.K, H, lay.A, int(fp8), int(zero_padding),
+        2 if scales_ue8m0 else int(scales_col_major), capacity,
         _p(lay.topk_idx), _p(lay.dst_slot), _p(lay.num_tokens_per_expert_total), _p(lay.expert_offset),
         _p(lay.window_row_base), _p(x), _p(xc), _p(xs), _p(w), row_begin, row_end, _p(recv_x),
         _p(recv_scales), _p(recv_w), _p(recv_meta), _p(dropped))
@@ -337,6 +345,16 @@ def quantize_row(x_row: np.ndarray):
     scales = np.zeros(H // 128, np.float32)
     lib().oracle_quantize_row(_p(x_row), H, _p(codes), _p(scales))
     return codes, scales
+
+
+def quantize_row_ue8m0(x_row: np.ndarray):
+    """``oracle_quantize_row_ue8m0``: -> (codes [H] u8, exponent bytes [H/32] u8)."""
+    x_row = np.ascontiguousarray(x_row, dtype=np.uint16)
+    H = x_row.size
+    codes = np.zeros(H, np.uint8)
+    exps = np.zeros(H // 32, np.uint8)
+    lib().oracle_quantize_row_ue8m0(_p(x_row), H, _p(codes), _p(exps))
+    return codes, exps
 
 
 def quantize_rows(x: np.ndarray, H: int, row_begin: int = 0, row_end: int | None = None):

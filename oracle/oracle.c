@@ -291,6 +291,50 @@ void oracle_quantize_row(const uint16_t *x, int H, uint8_t *codes, float *scales
   }
 }
 
+/* FP8 quantisation with UE8M0 scales.  The tutorial's size-hint passage
+ * ([TUT] 3.2) counts ceil(H/64) int16 scale packs per token, each holding two
+ * UE8M0 values: one unsigned 8-bit exponent per 32 channels.  (Its FP8 section,
+ * [TUT] 3.6, describes the same byte count as fp32 scales per 128 channels;
+ * that is the default format, this is the alternative.)  Reading, per block of
+ * 32 channels:
+ *   amax as in oracle_quantize_row;
+ *   k = the smallest integer in [-127, 127] with 448 * 2^k >= amax (a power of
+ *       two at or above amax / 448, so no |x| / 2^k exceeds 448 and no code
+ *       saturates), found by counting up from -127; amax = 0 gives -127;
+ *   exps[b] = k + 127 (the biased exponent byte), codes = E4M3(x / 2^k) with
+ *       the IEEE fp32 division;
+ *   a non-finite maximum (NaN or Inf in the block) gives exps[b] = 0xFF, the
+ *       UE8M0 NaN, and the codes of oracle_quantize_row's non-finite rule.
+ * codes [H] u8, exps [H/32] u8 (byte b of the row is block b; as int16 packs,
+ * pack i holds block 2i in its low byte and block 2i + 1 in its high byte). */
+void oracle_quantize_row_ue8m0(const uint16_t *x, int H, uint8_t *codes, uint8_t *exps) {
+  for (int b = 0; b < H / 32; b++) {
+    float amax = 0.0f;
+    int has_nan = 0;
+    for (int h = 32 * b; h < 32 * b + 32; h++) {
+      float v = fabsf(oracle_bf16_to_float(x[h]));
+      if (isnan(v))
+        has_nan = 1;
+      else if (v > amax)
+        amax = v;
+    }
+    if (has_nan || isinf(amax)) {
+      exps[b] = 0xFF;
+      for (int h = 32 * b; h < 32 * b + 32; h++) {
+        float xf = oracle_bf16_to_float(x[h]);
+        codes[h] = (has_nan || isinf(xf)) ? 0x7F : (signbit(xf) ? 0x80 : 0x00);
+      }
+      continue;
+    }
+    int k = -127;
+    while (k < 127 && ldexp(448.0, k) < (double)amax) k++;
+    exps[b] = (uint8_t)(k + 127);
+    float scale = ldexpf(1.0f, k);
+    for (int h = 32 * b; h < 32 * b + 32; h++)
+      codes[h] = oracle_e4m3_encode(oracle_bf16_to_float(x[h]) / scale);
+  }
+}
+
 /* oracle_quantize_row applied to rows [row_begin, row_end) of x [T][H]; the
  * outputs hold only those rows. */
 void oracle_quantize_rows(const uint16_t *x, int H, int64_t row_begin, int64_t row_end,
@@ -319,11 +363,14 @@ void oracle_quantize_rows(const uint16_t *x, int H, int64_t row_begin, int64_t r
  *                    oracle_dispatch_fixed): window d starts at d * capacity,
  *                    window-local rows >= capacity are not written, and the rows
  *                    [num_expanded[d], capacity) of a window are its tail.
- *  scales_col_major  recv_scales is laid out [H/128][n] (n = row_end - row_begin:
+ *  scales_col_major  1: recv_scales is laid out [H/128][n] (n = row_end - row_begin:
  *                    one scale position contiguous across rows) instead of
  *                    [n][H/128] ([TUT] 3.6 (3): the column-major scale layout is
  *                    the transpose of the row-major one, with no padding of the
  *                    row dimension).
+ *                    2: UE8M0 scales (oracle_quantize_row_ue8m0): recv_scales
+ *                    holds bytes [n][H/32] (cast to uint8_t *), zero bytes
+ *                    where fp32 scales would be zero.  Not with x_codes.
  *  x_codes, x_scales pre-quantised input ([TUT] 3.6 (2): x may be the pair of
  *                    E4M3 data [T][H] and one fp32 scale per 128 channels
  *                    [T][H/128]); rows then carry these bytes and scales as
@@ -354,16 +401,21 @@ static int dispatch_rows(int P, int S, int E, int K, int H, int A, int fp8, int 
                          int32_t *recv_src_meta) {
   if (P < 1 || E % P != 0 || H < 1 || (fp8 && H % 128 != 0)) return ORACLE_ERR_SHAPE;
   if (x_codes && !fp8) return ORACLE_ERR_SHAPE;
+  const int ue8m0 = scales_col_major == 2;
+  if (ue8m0 && (x_codes || !fp8)) return ORACLE_ERR_SHAPE;
   const int64_t T = (int64_t)P * S;
   const int El = E / P;
   const int nb = H / 128;
+  const int nb32 = H / 32;
   const int64_t n_out = row_end - row_begin;
   uint8_t *codes = NULL;
   float *scales = NULL;
+  uint8_t *exps = NULL;
   if (fp8) {
     codes = (uint8_t *)malloc((size_t)H);
     scales = (float *)malloc(sizeof(float) * (size_t)(nb > 0 ? nb : 1));
-    if (!codes || !scales) return ORACLE_ERR_SHAPE;
+    exps = (uint8_t *)malloc((size_t)(nb32 > 0 ? nb32 : 1));
+    if (!codes || !scales || !exps) return ORACLE_ERR_SHAPE;
   }
   for (int64_t u = 0; u < T; u++) {
     for (int j = 0; j < K; j++) {
@@ -376,6 +428,10 @@ static int dispatch_rows(int P, int S, int E, int K, int H, int A, int fp8, int 
       int64_t rr = r - row_begin;
       if (!recv_x) {
         /* metadata only */
+      } else if (fp8 && ue8m0) {
+        oracle_quantize_row_ue8m0(x + u * H, H, codes, exps);
+        memcpy((uint8_t *)recv_x + rr * H, codes, (size_t)H);
+        memcpy((uint8_t *)recv_scales + rr * nb32, exps, (size_t)nb32);
       } else if (fp8) {
         if (x_codes) {
           memcpy(codes, x_codes + u * H, (size_t)H);
@@ -414,7 +470,10 @@ static int dispatch_rows(int P, int S, int E, int K, int H, int A, int fp8, int 
       if (zero_padding && recv_x) {
         if (fp8) {
           memset((uint8_t *)recv_x + rr * H, 0, (size_t)H);
-          put_scales(recv_scales, scales_col_major, n_out, rr, nb, NULL);
+          if (ue8m0)
+            memset((uint8_t *)recv_scales + rr * nb32, 0, (size_t)nb32);
+          else
+            put_scales(recv_scales, scales_col_major, n_out, rr, nb, NULL);
         } else {
           for (int h = 0; h < H; h++) ((uint16_t *)recv_x)[rr * H + h] = 0;
         }
@@ -438,7 +497,10 @@ static int dispatch_rows(int P, int S, int E, int K, int H, int A, int fp8, int 
         if (recv_x) {
           if (fp8) {
             memset((uint8_t *)recv_x + rr * H, 0, (size_t)H);
-            put_scales(recv_scales, scales_col_major, n_out, rr, nb, NULL);
+            if (ue8m0)
+              memset((uint8_t *)recv_scales + rr * nb32, 0, (size_t)nb32);
+            else
+              put_scales(recv_scales, scales_col_major, n_out, rr, nb, NULL);
           } else {
             for (int h = 0; h < H; h++) ((uint16_t *)recv_x)[rr * H + h] = 0;
           }
@@ -448,6 +510,7 @@ static int dispatch_rows(int P, int S, int E, int K, int H, int A, int fp8, int 
   }
   free(codes);
   free(scales);
+  free(exps);
   return ORACLE_OK;
 }
 

@@ -56,13 +56,42 @@ MUTANTS = [
     ("codes_by_reciprocal",
      [("float q = xf / scale;", "float q = xf * (1.0f / scale);")]),
     ("amax_skips_nan",
-     [("      if (isnan(v))\n        has_nan = 1;\n      else if (v > amax)",
-       "      if (0)\n        has_nan = 1;\n      else if (v > amax)")]),
+     [("    for (int h = 128 * b; h < 128 * b + 128; h++) {\n      float v = fabsf(oracle_bf16_to_float(x[h]));\n"
+       "      if (isnan(v))",
+       "    for (int h = 128 * b; h < 128 * b + 128; h++) {\n      float v = fabsf(oracle_bf16_to_float(x[h]));\n"
+       "      if (0)")]),
+    ("ue8m0_amax_skips_nan",
+     [("    for (int h = 32 * b; h < 32 * b + 32; h++) {\n      float v = fabsf(oracle_bf16_to_float(x[h]));\n"
+       "      if (isnan(v))",
+       "    for (int h = 32 * b; h < 32 * b + 32; h++) {\n      float v = fabsf(oracle_bf16_to_float(x[h]));\n"
+       "      if (0)")]),
     ("nan_codes_keep_sign",
      [("codes[h] = isnan(q) ? 0x7F : oracle_e4m3_encode(q);", "codes[h] = oracle_e4m3_encode(q);")]),
     ("amax_flushes_subnormal_inputs",
-     [("      float v = fabsf(oracle_bf16_to_float(x[h]));",
-       "      float v = fabsf(oracle_bf16_to_float(x[h]));\n      if (v < 1.17549435e-38f) v = 0.0f;")]),
+     [("    for (int h = 128 * b; h < 128 * b + 128; h++) {\n      float v = fabsf(oracle_bf16_to_float(x[h]));",
+       "    for (int h = 128 * b; h < 128 * b + 128; h++) {\n      float v = fabsf(oracle_bf16_to_float(x[h]));\n"
+       "      if (v < 1.17549435e-38f) v = 0.0f;")]),
+    ("ue8m0_exponent_rounds_down",
+     [("while (k < 127 && ldexp(448.0, k) < (double)amax) k++;",
+       "while (k < 127 && ldexp(448.0, k + 1) <= (double)amax) k++;")]),
+    ("ue8m0_exponent_not_minimal",
+     [("while (k < 127 && ldexp(448.0, k) < (double)amax) k++;",
+       "while (k < 127 && ldexp(448.0, k) <= (double)amax) k++;")]),
+    ("ue8m0_amax_skips_last_channel",
+     [("    for (int h = 32 * b; h < 32 * b + 32; h++) {\n      float v = fabsf",
+       "    for (int h = 32 * b; h < 32 * b + 31; h++) {\n      float v = fabsf")]),
+    ("ue8m0_codes_multiply_by_scale",
+     [("codes[h] = oracle_e4m3_encode(oracle_bf16_to_float(x[h]) / scale);",
+       "codes[h] = oracle_e4m3_encode(oracle_bf16_to_float(x[h]) * scale);")]),
+    ("ue8m0_nan_exponent_zero",
+     [("      exps[b] = 0xFF;", "      exps[b] = 0x00;")]),
+    ("ue8m0_padding_exponents_left",
+     [("            memset((uint8_t *)recv_scales + rr * nb32, 0, (size_t)nb32);\n          else\n"
+       "            put_scales(recv_scales, scales_col_major, n_out, rr, nb, NULL);\n        } else {\n"
+       "          for (int h = 0; h < H; h++) ((uint16_t *)recv_x)[rr * H + h] = 0;\n        }\n      }\n    }",
+       "            (void)0;\n          else\n"
+       "            put_scales(recv_scales, scales_col_major, n_out, rr, nb, NULL);\n        } else {\n"
+       "          for (int h = 0; h < H; h++) ((uint16_t *)recv_x)[rr * H + h] = 0;\n        }\n      }\n    }")]),
     ("combine_flushes_subnormal_products",
      [("        float prod = w * oracle_bf16_to_float(y[r * H + h]);\n        acc = acc + prod;",
        "        float prod = w * oracle_bf16_to_float(y[r * H + h]);\n"

@@ -435,6 +435,140 @@ def test_quantize_row_non_finite_blocks():
     np.testing.assert_array_equal(bs2.view(np.uint32), bs[2:5].view(np.uint32))
 
 
+def _ue8m0_rows(rng, H):
+    """bf16 rows whose 32-channel blocks exercise the exponent choice: N(0,1) values, blocks
+    whose maximum is exactly 448 * 2^k (the bound met with equality), a maximum just above
+    1.75 * 2^E (mantissa 0x61: forces the next power of two), maxima of 1.0 * 2^E, all-zero
+    and signed-zero blocks, bf16 subnormals, the smallest normal and the largest finite bf16,
+    values spread over many binades, and NaN / Inf blocks."""
+    rows = []
+    for r in range(12):
+        x = synth.gen_bf16_rows(50 + r, 1, 1, H)[0].copy()
+        for b in range(H // 32):
+            blk = x[32 * b:32 * (b + 1)]
+            kind = (r + b) % 12
+            sign = (rng.integers(0, 2, 32) << 15).astype(np.uint16)
+            if kind == 1:    # maximum exactly 448 * 2^k: 1.75 * 2^(8+k), bf16 0x3F60 + ((8+k) << 7)
+                k = int(rng.integers(-20, 20))
+                blk[:] = sign | rng.integers(0x3000, 0x3F00, 32).astype(np.uint16)
+                blk[rng.integers(0, 32)] = (((127 + 8 + k) << 7) | 0x60) | int(sign[0])
+            elif kind == 2:  # maximum 1.7578125 * 2^E (mantissa 0x61)
+                e = int(rng.integers(100, 140))
+                blk[:] = sign | rng.integers(0x3000, 0x3F00, 32).astype(np.uint16)
+                blk[rng.integers(0, 32)] = (e << 7) | 0x61
+            elif kind == 3:  # maximum 2^E exactly
+                e = int(rng.integers(90, 160))
+                blk[:] = sign | rng.integers(0x2000, 0x2F00, 32).astype(np.uint16)
+                blk[rng.integers(0, 32)] = e << 7
+            elif kind == 4:  # zeros of both signs
+                blk[:] = sign
+            elif kind == 5:  # bf16 subnormals
+                blk[:] = sign | rng.integers(1, 0x80, 32).astype(np.uint16)
+            elif kind == 6:  # smallest normal among subnormals
+                blk[:] = sign | rng.integers(0, 0x80, 32).astype(np.uint16)
+                blk[rng.integers(0, 32)] = 0x0080
+            elif kind == 7:  # the largest finite bf16
+                blk[:] = sign | rng.integers(0x7000, 0x7F00, 32).astype(np.uint16)
+                blk[rng.integers(0, 32)] = 0x7F7F | int(sign[0])
+            elif kind == 8:  # many binades
+                blk[:] = sign | (rng.integers(1, 254, 32) << 7).astype(np.uint16) | rng.integers(0, 0x80, 32).astype(np.uint16)
+            elif kind == 9:  # a NaN
+                blk[rng.integers(0, 32)] = int(rng.choice([0x7FC0, 0xFFC1]))
+            elif kind == 10:  # an infinity
+                blk[rng.integers(0, 32)] = int(rng.choice([0x7F80, 0xFF80]))
+            x[32 * b:32 * (b + 1)] = blk
+        rows.append(x)
+    return np.stack(rows)
+
+
+def test_quantize_row_ue8m0_exponent_codes_and_packs(golden):
+    """UE8M0 quantisation against the stated rule, written here in plain Python.
+    Per 32-channel block, for a finite maximum amax: the exponent byte e gives a scale
+    2^(e-127) with 448 * 2^(e-127) >= amax, and halving it would push amax past 448 (or
+    e = 0); the same byte from frexp; every code is the nearest E4M3 value of x / 2^(e-127)
+    (exact quotient, brute force), never a NaN code.  Non-finite blocks: byte 0xFF and the
+    codes of the non-finite rule.  The bytes, viewed as int16 packs, number ceil(H/64) per
+    token (the page's 112 at hidden 7168), two UE8M0 per pack, block 2i in the low byte."""
+    import math
+
+    rng = np.random.default_rng(21)
+    H = golden["ue8m0_scale_packs"]["hidden"]
+    x = _ue8m0_rows(rng, H)
+    seen_eq = seen_up = False
+    for r in range(x.shape[0]):
+        codes, exps = oracle.quantize_row_ue8m0(x[r])
+        assert exps.shape == (H // 32,)
+        packs = exps.view(np.int16)
+        assert packs.size == -(-H // 64) == golden["ue8m0_scale_packs"]["num_sf_packs_int16"]
+        assert golden["ue8m0_scale_packs"]["ue8m0_per_pack"] == 2
+        lo, hi = (packs.view(np.uint16) & 0xFF).astype(np.uint8), (packs.view(np.uint16) >> 8).astype(np.uint8)
+        np.testing.assert_array_equal(lo, exps[0::2])
+        np.testing.assert_array_equal(hi, exps[1::2])
+        xf = bf16_bits_to_f64(x[r])
+        for b in range(H // 32):
+            blk = xf[32 * b:32 * (b + 1)]
+            cb = codes[32 * b:32 * (b + 1)]
+            e = int(exps[b])
+            if not np.all(np.isfinite(blk)):
+                assert e == 0xFF
+                exp_codes = np.where(np.isnan(blk).any() | np.isinf(blk), 0x7F, np.where(np.signbit(blk), 0x80, 0x00))
+                np.testing.assert_array_equal(cb, exp_codes.astype(np.uint8))
+                continue
+            amax = float(np.abs(blk).max())
+            k = e - 127
+            assert 0 <= e <= 254
+            assert math.ldexp(448.0, k) >= amax, (r, b, e, amax)
+            assert e == 0 or math.ldexp(448.0, k - 1) < amax, (r, b, e, amax)
+            # closed form from frexp: amax = M * 2^E, M in [1, 2); k = E - 8 + (M > 1.75)
+            if amax < 2.0 ** -126:
+                e_cf = 0
+            else:
+                f, ex = math.frexp(amax)
+                e_cf = max(0, (ex - 1) - 8 + (1 if 2 * f > 1.75 else 0) + 127)
+            assert e == e_cf, (r, b, e, e_cf)
+            seen_eq |= amax == math.ldexp(448.0, k) and e > 0
+            seen_up |= e > 0 and 2 * math.frexp(amax)[0] > 1.75  # mantissa above 1.75: next power up
+            q = np.ldexp(blk, -k)  # exact in float64
+            np.testing.assert_array_equal(cb, brute_force_e4m3(q), err_msg=f"row {r} block {b}")
+            assert np.all((cb & 0x7F) <= 0x7E)
+    assert seen_eq and seen_up
+
+
+def test_dispatch_fp8_ue8m0_rows():
+    """Fused UE8M0 dispatch: every valid row carries its token's codes and exponent bytes
+    (oracle_quantize_row_ue8m0), padding rows zero bytes with zero padding, fixed-window
+    tails zero bytes; pre-quantised input and column-major layout are refused."""
+    w = small_workload(H=512)
+    topk = synth.gen_routing(w)
+    x = _ue8m0_rows(np.random.default_rng(22), w.H)
+    x = np.vstack([x] * (-(-w.T // x.shape[0])))[:w.T]
+    wt = synth.gen_weights(w)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    El = w.E // w.P
+    for capacity in (0, int(lay.num_expanded.max()) + 7):
+        rx, sc, rw, rm, _ = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=True, topk_weights=wt, x=x,
+                                                    capacity=capacity, scales_ue8m0=True, fill=0x33)
+        assert sc.dtype == np.uint8 and sc.shape == (rx.shape[0], w.H // 32)
+        covered = np.zeros(rx.shape[0], bool)
+        for u in range(w.T):
+            c, e = oracle.quantize_row_ue8m0(x[u])
+            for j in range(w.K):
+                ex = topk[u, j]
+                if ex < 0:
+                    continue
+                base = (ex // El) * capacity if capacity else lay.window_row_base[ex // El]
+                row = base + lay.dst_slot[u, j]
+                np.testing.assert_array_equal(rx[row], c)
+                np.testing.assert_array_equal(sc[row], e)
+                covered[row] = True
+        assert (rx[~covered] == 0).all() and (sc[~covered] == 0).all()
+        assert (rm[~covered] == -1).all()
+    with pytest.raises(oracle.OracleError):
+        oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=True, topk_weights=wt,
+                                x_codes=np.zeros((w.T, w.H), np.uint8),
+                                x_scales=np.zeros((w.T, w.H // 128), np.float32), scales_ue8m0=True)
+
+
 def test_dispatch_fp8_rows_and_zero_padding():
     w = small_workload(P=4, S=32, E=8, K=2, H=384, A=8, seed=12)
     topk = synth.gen_routing(w)
