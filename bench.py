@@ -540,6 +540,10 @@ def calls_table() -> int:
         bias = torch.empty((T, H), dtype=torch.bfloat16, device=dev).normal_()
         put("combine_bias", lambda: ep.combine(h, y, w_d, bias=bias, out=out), led["combine"] + T * H * 2)
         if fp8:
+            sc8 = torch.empty((R, H // 32), dtype=torch.uint8, device=dev)
+            put("dispatch_ue8m0", lambda: ep.dispatch(h, x_d, w_d, zero_padding=w.zero_padding, scales_ue8m0=True,
+                                                      out=(rx, sc8, rw, rm)), led["dispatch"])
+            del sc8
             codes = torch.randint(0, 256, (T, H), dtype=torch.uint8, device=dev)
             xs = torch.rand((T, nb), dtype=torch.float32, device=dev)
             pre = T * H + T * nb * 4 + 8 * T * K + (led["dispatch"] - led["dispatch_read"])
@@ -707,6 +711,12 @@ def per_config(name: str, reps: int) -> dict:
 
     put("dispatch", _median_us(lambda: ep.dispatch(h, x_d, w_d, fp8, w.zero_padding, out=(rx, sc, rw, rm)), reps),
         led["dispatch"])
+    if fp8:  # UE8M0 scales: H/32 exponent bytes per row, the same bytes as H/128 fp32 scales
+        sc8 = torch.empty((R, H // 32), dtype=torch.uint8, device=dev)
+        put("dispatch_ue8m0", _median_us(lambda: ep.dispatch(h, x_d, w_d, zero_padding=w.zero_padding,
+                                                              scales_ue8m0=True, out=(rx, sc8, rw, rm)), reps),
+            led["dispatch"])
+        del sc8
     if w.cached_iters:
         # new x for every iteration, drawn on the device with a seeded generator
         xs = []

@@ -9,12 +9,13 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libep_mi355x.so"
-EP_ABI_VERSION = 3
+EP_ABI_VERSION = 4
 
 # dispatch flags
 _FP8 = 1
 _ZERO_PADDING = 2
 _SCALES_COL_MAJOR = 4
+_SCALES_UE8M0 = 8
 _SYMMETRIC_WINDOWS = 1
 # ep_handle_status bits
 STATUS_ROUTING = 1
@@ -205,7 +206,7 @@ def _require(t, dtype, shape, name, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _require_recv(h, recv_x, recv_scales, fp8: bool, scales_col_major: bool):
+def _require_recv(h, recv_x, recv_scales, fp8: bool, scales_col_major: bool, scales_ue8m0: bool = False):
     """Caller-provided expanded outputs: [total_rows, H] payload and, for fp8, the scales."""
     import torch
 
@@ -214,8 +215,11 @@ def _require_recv(h, recv_x, recv_scales, fp8: bool, scales_col_major: bool):
     if fp8:
         if recv_scales is None:
             raise ValueError("recv_scales is required for fp8 output")
-        shape = (H // 128, R) if scales_col_major else (R, H // 128)
-        _require(recv_scales, torch.float32, shape, "recv_scales", h.device)
+        if scales_ue8m0:
+            _require(recv_scales, torch.uint8, (R, H // 32), "recv_scales (UE8M0)", h.device)
+        else:
+            shape = (H // 128, R) if scales_col_major else (R, H // 128)
+            _require(recv_scales, torch.float32, shape, "recv_scales", h.device)
 
 
 class Handle:
@@ -392,17 +396,20 @@ def relayout(h: Handle, topk_idx) -> Handle:
     return h
 
 
-def _flags(fp8: bool, zero_padding: bool, scales_col_major: bool = False) -> int:
-    return (_FP8 if fp8 else 0) | (_ZERO_PADDING if zero_padding else 0) | (_SCALES_COL_MAJOR if scales_col_major else 0)
+def _flags(fp8: bool, zero_padding: bool, scales_col_major: bool = False, scales_ue8m0: bool = False) -> int:
+    return ((_FP8 if fp8 else 0) | (_ZERO_PADDING if zero_padding else 0) |
+            (_SCALES_COL_MAJOR if scales_col_major else 0) | (_SCALES_UE8M0 if scales_ue8m0 else 0))
 
 
-def _alloc_recv(h: Handle, fp8: bool, device, scales_col_major: bool = False):
+def _alloc_recv(h: Handle, fp8: bool, device, scales_col_major: bool = False, scales_ue8m0: bool = False):
     import torch
 
     H, R = h.cfg.H, h.total_rows
     recv_x = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=device)
     recv_scales = None
-    if fp8:
+    if fp8 and scales_ue8m0:
+        recv_scales = torch.empty((R, H // 32), dtype=torch.uint8, device=device)
+    elif fp8:
         shape = (H // 128, R) if scales_col_major else (R, H // 128)
         recv_scales = torch.empty(shape, dtype=torch.float32, device=device)
     return recv_x, recv_scales
@@ -424,9 +431,12 @@ def _input(h: Handle, x):
 
 def dispatch(h: Handle, x, topk_weights, fp8: bool = False, zero_padding: bool = False,
              scales_col_major: bool = False, out=None, async_with_compute_stream: bool = False,
-             previous_event=None):
+             previous_event=None, scales_ue8m0: bool = False):
     """ep_dispatch (x bf16) or ep_dispatch_prequant (x = (codes, scales), output fp8)
     -> (recv_x, recv_scales | None, recv_weights, recv_src_meta).
+
+    scales_ue8m0: fp8 output with one UE8M0 exponent byte per 32 channels (recv_scales uint8
+    [total_rows, H/32]); implies fp8.
 
     out: optional preallocated (recv_x, recv_scales, recv_weights, recv_src_meta).
     async_with_compute_stream: run on the library's communication stream after
@@ -436,18 +446,18 @@ def dispatch(h: Handle, x, topk_weights, fp8: bool = False, zero_padding: bool =
 
     cfg = h.cfg
     xin, xs, device = _input(h, x)
-    fp8 = fp8 or xs is not None
+    fp8 = fp8 or xs is not None or scales_ue8m0
     _require(topk_weights, torch.float32, (cfg.T, cfg.K), "topk_weights", h.device)
     if out is None:
-        recv_x, recv_scales = _alloc_recv(h, fp8, device, scales_col_major)
+        recv_x, recv_scales = _alloc_recv(h, fp8, device, scales_col_major, scales_ue8m0)
         recv_w = torch.empty(h.total_rows, dtype=torch.float32, device=device)
         recv_meta = torch.empty((h.total_rows, 2), dtype=torch.int32, device=device)
     else:
         recv_x, recv_scales, recv_w, recv_meta = out
-        _require_recv(h, recv_x, recv_scales, fp8, scales_col_major)
+        _require_recv(h, recv_x, recv_scales, fp8, scales_col_major, scales_ue8m0)
         _require(recv_w, torch.float32, (h.total_rows,), "recv_weights", h.device)
         _require(recv_meta, torch.int32, (h.total_rows, 2), "recv_src_meta", h.device)
-    flags = _flags(fp8, zero_padding, scales_col_major)
+    flags = _flags(fp8, zero_padding, scales_col_major, scales_ue8m0)
 
     def launch():
         with _on(device):
@@ -467,19 +477,21 @@ def dispatch(h: Handle, x, topk_weights, fp8: bool = False, zero_padding: bool =
 
 
 def dispatch_cached(h: Handle, x, fp8: bool = False, zero_padding: bool = False, scales_col_major: bool = False,
-                    out=None, async_with_compute_stream: bool = False, previous_event=None):
+                    out=None, async_with_compute_stream: bool = False, previous_event=None,
+                    scales_ue8m0: bool = False):
     """ep_dispatch_cached / ep_dispatch_prequant_cached -> (recv_x, recv_scales | None);
-    out: optional (recv_x, recv_scales); async_with_compute_stream as in dispatch."""
+    out: optional (recv_x, recv_scales); async_with_compute_stream and scales_ue8m0 as in
+    dispatch."""
     import torch
 
     xin, xs, device = _input(h, x)
-    fp8 = fp8 or xs is not None
+    fp8 = fp8 or xs is not None or scales_ue8m0
     if out is None:
-        recv_x, recv_scales = _alloc_recv(h, fp8, device, scales_col_major)
+        recv_x, recv_scales = _alloc_recv(h, fp8, device, scales_col_major, scales_ue8m0)
     else:
         recv_x, recv_scales = out
-        _require_recv(h, recv_x, recv_scales, fp8, scales_col_major)
-    flags = _flags(fp8, zero_padding, scales_col_major)
+        _require_recv(h, recv_x, recv_scales, fp8, scales_col_major, scales_ue8m0)
+    flags = _flags(fp8, zero_padding, scales_col_major, scales_ue8m0)
 
     def launch():
         with _on(device):

@@ -412,9 +412,14 @@ ep_status dispatch_common(const ep_handle* h, uint32_t flags, const void* x, con
   ep_status st = check_handle(h);
   if (st == EP_OK) st = check_device(h);
   if (st != EP_OK) return st;
-  if (flags & ~(uint32_t)(EP_DISPATCH_FP8 | EP_DISPATCH_ZERO_PADDING | EP_DISPATCH_SCALES_COL_MAJOR))
+  if (flags & ~(uint32_t)(EP_DISPATCH_FP8 | EP_DISPATCH_ZERO_PADDING | EP_DISPATCH_SCALES_COL_MAJOR |
+                          EP_DISPATCH_SCALES_UE8M0))
     return fail(EP_ERR_SHAPE, "unknown dispatch flags 0x%x", flags);
-  const bool fp8 = (flags & EP_DISPATCH_FP8) || prequant;
+  const bool ue8m0 = flags & EP_DISPATCH_SCALES_UE8M0;
+  if (ue8m0 && (prequant || (flags & EP_DISPATCH_SCALES_COL_MAJOR)))
+    return fail(EP_ERR_SHAPE, "UE8M0 scales are row-major and come from the fused quantisation: not with "
+                              "EP_DISPATCH_SCALES_COL_MAJOR or pre-quantised input");
+  const bool fp8 = (flags & EP_DISPATCH_FP8) || prequant || ue8m0;
   const bool zero_pad = flags & EP_DISPATCH_ZERO_PADDING;
   if (fp8 && h->cfg.hidden % 128 != 0)
     return fail(EP_ERR_SHAPE, "fp8 dispatch needs hidden %% 128 == 0 (hidden %d)", h->cfg.hidden);
@@ -464,6 +469,8 @@ ep_status dispatch_common(const ep_handle* h, uint32_t flags, const void* x, con
     a.tok_scales = const_cast<float*>(x_scales);  // read only: the rows' scales come from here
     return meta ? launch_dispatch_mode<true, true, true>(a, s) : launch_dispatch_mode<true, false, true>(a, s);
   }
+  if (ue8m0)
+    return meta ? launch_dispatch_mode<true, true, false, true>(a, s) : launch_dispatch_mode<true, false, false, true>(a, s);
   if (fp8 && a.scales_cm && staging) {
     a.tok_scales = staging;  // the caller's fixed staging: no handle state, no ordering
     return meta ? launch_dispatch_mode<true, true, false>(a, s) : launch_dispatch_mode<true, false, false>(a, s);

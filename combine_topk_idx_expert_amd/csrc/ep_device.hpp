@@ -60,6 +60,14 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   return v;
 }
 
+// Maximum over each group of 4 lanes (DPP quad permutes: swap neighbours,
+// then swap pairs), on non-negative float bit patterns.
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  return v;
+}
+
 // bf16 pair in a 32-bit word -> two floats (bf16 is the upper half of fp32).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

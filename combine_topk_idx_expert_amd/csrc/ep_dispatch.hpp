@@ -94,6 +94,37 @@ __device__ __forceinline__ u32x2 quantize8(u32x4 v, float scale, bool zero_block
   return out;
 }
 
+// UE8M0 exponent byte of a 32-channel block from m, the largest |x| bf16
+// bit pattern of the block: the smallest k in [-127, 127] with
+// 448 * 2^k >= amax, biased by 127.  With amax = M * 2^E (M in [1, 2)) and
+// 448 = 1.75 * 2^8, that is k = E - 8, or E - 7 when M > 1.75 (bf16 mantissa
+// above 0x60); zero and subnormal maxima give k = -127 (byte 0), a
+// non-finite maximum the UE8M0 NaN 0xFF.
+__device__ __forceinline__ uint32_t ue8m0_exponent(uint32_t m) {
+  if (m >= 0x7F80u) return 0xFFu;
+  const int ef = (int)(m >> 7);
+  if (ef == 0) return 0u;
+  const int t = ef - 8 + ((m & 0x7Fu) > 0x60u ? 1 : 0);
+  return t < 0 ? 0u : (uint32_t)t;
+}
+
+// E4M3 codes of 8 bf16 values for a power-of-two scale 2^k, given inv =
+// 2^-k (an exact normal float): x * 2^-k is the correctly rounded x / 2^k.
+__device__ __forceinline__ u32x2 quantize8_pow2(u32x4 v, float inv, bool zero_block) {
+  u32x2 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t p0 = v[2 * h], p1 = v[2 * h + 1];
+    if (!zero_block) {
+      out[h] = e4m3x4_hw(bf16_lo(p0) * inv, bf16_hi(p0) * inv, bf16_lo(p1) * inv, bf16_hi(p1) * inv);
+    } else {
+      out[h] = ((p0 >> 8) & 0x80u) | ((p0 >> 16) & 0x8000u) | (((p1 >> 8) & 0x80u) << 16) |
+               ((p1 & 0x80000000u));
+    }
+  }
+  return out;
+}
+
 // Codes of 8 bf16 values (packed in v) of a block whose maximum is not
 // finite, byte order as in quantize8.  A NaN block (some |x| is NaN) codes
 // every value 0x7F; an Inf block codes its infinities 0x7F (Inf / Inf is NaN)
@@ -168,11 +199,21 @@ __device__ __forceinline__ void store_pacing() {
   }
 }
 
-// scales: fp8 row-major scales to zero with the row (null: none)
-template <int NC, bool FP8>
+// scales: fp8 row-major scales to zero with the row (null: none); with UE8M0
+// they are the row's H/32 exponent bytes, zeroed four per lane (lanes 0..3).
+template <int NC, bool FP8, bool UE8M0 = false>
 __device__ __forceinline__ void zero_row_part(uint8_t* recv, int64_t row, int part, int64_t out_row_bytes,
                                               int nchunk, int lane, float* scales) {
-  if constexpr (FP8) {
+  if constexpr (FP8 && UE8M0) {
+    if (scales) {
+      const int nw = nchunk >> 4;  // 32-bit words of exponent bytes per row
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int wd = ((part * NC * kWave + c * kWave) >> 4) + lane;
+        if (lane < 4 && wd < nw) ((uint32_t*)scales)[row * nw + wd] = 0u;
+      }
+    }
+  } else if constexpr (FP8) {
     if (scales) {
       const int nblk = nchunk >> 4;
 #pragma unroll
@@ -200,9 +241,12 @@ __device__ __forceinline__ void zero_row_part(uint8_t* recv, int64_t row, int pa
 // the bytes unchanged (FP8 only).  FIXED: fixed windows (a.cap > 0); exact
 // windows get kernels without the fixed-window paths (measured: carrying them
 // slowed the exact fp8 dispatch by ~15%).
-template <int NC, bool FP8, bool META, bool PREQ, bool FIXED>
+// UE8M0: fp8 scales as one exponent byte per 32 channels (row-major bytes
+// [rows][H/32]) instead of one fp32 per 128 channels; fused quantisation only.
+template <int NC, bool FP8, bool META, bool PREQ, bool FIXED, bool UE8M0 = false>
 __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
   static_assert(!PREQ || FP8, "pre-quantised input is fp8");
+  static_assert(!UE8M0 || (FP8 && !PREQ), "UE8M0 scales come from the fused quantisation");
   const int gw = wave_index();
   const int lane = lane_id();
   const int nchunk = a.H >> 3;  // 16-byte bf16 chunks per row
@@ -265,10 +309,26 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
       // written afterwards by dispatch_scales_cm_kernel from tok_scales.
       const bool fused_scales = !a.scales_cm;
       float sc[NC];
+      uint32_t ew[NC];  // UE8M0: lanes 0..3 hold four exponent bytes each
 #pragma unroll
       for (int c = 0; c < NC && PREQ; ++c) sc[c] = pq_sc[c];
 #pragma unroll
-      for (int c = 0; c < NC && !PREQ; ++c) {
+      for (int c = 0; c < NC && UE8M0; ++c) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m = max(m, max(v[c][k] & 0x7FFFu, (v[c][k] >> 16) & 0x7FFFu));
+        m = quad_max_u32(m);  // 4 lanes = one 32-channel block
+        const uint32_t eb = ue8m0_exponent(m);
+        const float inv = __uint_as_float((254u - min(eb, 247u)) << 23);  // 2^(127 - eb)
+        codes[c] = quantize8_pow2(v[c], inv, m == 0);
+        if (__builtin_expect(m >= 0x7F80u, 0)) codes[c] = nonfinite_codes8(v[c], m > 0x7F80u);
+        // word w of the part's 16 blocks holds blocks 4w..4w+3, i.e. the bytes of lanes 16w + 4i
+        const int w16 = (lane & 3) * 16;
+        ew[c] = (uint32_t)__shfl((int)eb, w16) | ((uint32_t)__shfl((int)eb, w16 + 4) << 8) |
+                ((uint32_t)__shfl((int)eb, w16 + 8) << 16) | ((uint32_t)__shfl((int)eb, w16 + 12) << 24);
+      }
+#pragma unroll
+      for (int c = 0; c < NC && !PREQ && !UE8M0; ++c) {
         uint32_t m = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) m = max(m, max(v[c][k] & 0x7FFFu, (v[c][k] >> 16) & 0x7FFFu));
@@ -293,8 +353,13 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
         for (int c = 0; c < NC; ++c) {
           const int q = tile + c * kWave + lane;
           if (q < nchunk) stream_store(dst + q, codes[c]);
-          const int blk = (tile + c * kWave) / 16 + lane;
-          if (fused_scales && lane < 4 && blk < nblk) a.recv_scales[(int64_t)row * nblk + blk] = sc[c];
+          if constexpr (UE8M0) {
+            const int wd = ((tile + c * kWave) >> 4) + lane;  // 32-bit word of exponent bytes
+            if (lane < 4 && wd < (nchunk >> 4)) ((uint32_t*)a.recv_scales)[(int64_t)row * (nchunk >> 4) + wd] = ew[c];
+          } else {
+            const int blk = (tile + c * kWave) / 16 + lane;
+            if (fused_scales && lane < 4 && blk < nblk) a.recv_scales[(int64_t)row * nblk + blk] = sc[c];
+          }
         }
         store_pacing<NC>();
       }
@@ -304,7 +369,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
     if constexpr (!FIXED) {
       const int p = (gw - token_items) / a.split;
       const int part = (gw - token_items) - p * a.split;
-      zero_row_part<NC, FP8>(recv, a.pad_rows[p], part, out_row_bytes, nchunk, lane, zero_scales);
+      zero_row_part<NC, FP8, UE8M0>(recv, a.pad_rows[p], part, out_row_bytes, nchunk, lane, zero_scales);
     } else {
       // Fixed windows: padding rows (if asked) then tail rows (always),
       // counted on the device.  Wave w zeroes whole rows z = z0 + w, z0 + w +
@@ -327,7 +392,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
           row = (int64_t)win * a.cap + a.cap - (a.tail_base[win + 1] - a.tail_base[win]) + (k - a.tail_base[win]);
         }
         for (int part = 0; part < a.split; ++part)
-          zero_row_part<NC, FP8>(recv, row, part, out_row_bytes, nchunk, lane, zero_scales);
+          zero_row_part<NC, FP8, UE8M0>(recv, row, part, out_row_bytes, nchunk, lane, zero_scales);
       }
     }
   } else if (META) {

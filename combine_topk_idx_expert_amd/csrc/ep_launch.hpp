@@ -51,7 +51,7 @@ int parts_per_row(int H, int nc) { return ((H >> 3) + nc * kWave - 1) / (nc * kW
 // whose number only the device knows (at most P * cap rows).
 constexpr int64_t kZeroWaves = 16384;
 
-template <bool FP8, bool META, bool PREQ, bool FIXED>
+template <bool FP8, bool META, bool PREQ, bool FIXED, bool UE8M0 = false>
 ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
   constexpr int nc = FP8 ? kNcFp8 : kNcBf16;
   a.split = parts_per_row(a.H, nc);
@@ -65,7 +65,7 @@ ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
     const int threads = EP_ROW_BLOCK_WAVES * kWave;
     const int blocks = (int)((waves + EP_ROW_BLOCK_WAVES - 1) / EP_ROW_BLOCK_WAVES);
     const size_t lds = EP_DISPATCH_LDS_BYTES;  // > 0 caps workgroups per CU (occupancy)
-    dispatch_kernel<nc, FP8, META, PREQ, FIXED><<<blocks, threads, lds, s>>>(a);
+    dispatch_kernel<nc, FP8, META, PREQ, FIXED, UE8M0><<<blocks, threads, lds, s>>>(a);
     EP_LAUNCHED("dispatch_kernel");
   }
   // row-major scales are written by the dispatch waves themselves
@@ -77,9 +77,10 @@ ep_status launch_dispatch(DispatchArgs a, hipStream_t s) {
   return EP_OK;
 }
 
-template <bool FP8, bool META, bool PREQ>
+template <bool FP8, bool META, bool PREQ, bool UE8M0 = false>
 ep_status launch_dispatch_mode(const DispatchArgs& a, hipStream_t s) {
-  return a.cap > 0 ? launch_dispatch<FP8, META, PREQ, true>(a, s) : launch_dispatch<FP8, META, PREQ, false>(a, s);
+  return a.cap > 0 ? launch_dispatch<FP8, META, PREQ, true, UE8M0>(a, s)
+                   : launch_dispatch<FP8, META, PREQ, false, UE8M0>(a, s);
 }
 
 // Combine: whole rows of up to 8 KiB (K <= 8, so <= 64 KiB of LDS per token

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 3
+#define EP_ABI_VERSION 4
 
 /* Limits of the library. */
 #define EP_MAX_RANKS 1024
@@ -88,6 +88,8 @@ typedef enum {
 #define EP_DISPATCH_FP8 1u          /* emit E4M3 codes + fp32 scales per 128 channels  */
 #define EP_DISPATCH_ZERO_PADDING 2u /* zero the alignment padding rows' payload         */
 #define EP_DISPATCH_SCALES_COL_MAJOR 4u /* fp8: recv_scales as [H/128, total_rows]       */
+#define EP_DISPATCH_SCALES_UE8M0 8u /* fp8 with one UE8M0 exponent byte per 32 channels  */
+                                    /* (implies EP_DISPATCH_FP8; see ep_dispatch)        */
 
 /* Shape of one dispatch/combine problem.  The tutorial's EPBuffer is built for
  * a token capacity, hidden size and top-k, and dispatch takes num_experts and
@@ -165,6 +167,10 @@ ep_status ep_relayout(ep_handle *h, const int64_t *topk_idx, void *stream, int64
  *                 total_rows] with EP_DISPATCH_SCALES_COL_MAJOR (scale b of row
  *                 r at b * total_rows + r: one scale position contiguous across
  *                 rows, no row padding; TileLang tutorial ch. 38, section 3.6);
+ *                 with EP_DISPATCH_SCALES_UE8M0 it holds bytes, uint8
+ *                 [total_rows, H/32]: one UE8M0 exponent per 32 channels, so
+ *                 that viewed as int16 it is the ceil(H/64) packs of two UE8M0
+ *                 per token of the tutorial's size-hint passage (section 3.2);
  *                 required with EP_DISPATCH_FP8 (H % 128 == 0), ignored
  *                 otherwise.
  *   recv_weights  device, fp32 [total_rows].
@@ -173,7 +179,14 @@ ep_status ep_relayout(ep_handle *h, const int64_t *topk_idx, void *stream, int64
  * Row r = window_row_base[rank(e)] + dst_slot[u][j] of every valid slot gets
  * x[u] (bf16 copy, or its E4M3 codes: scale = amax/448 per 128-channel block
  * in fp32, code = E4M3FN round-to-nearest-even of x/scale; a block with amax 0
- * has scale 0 and signed-zero codes), recv_weights = topk_weights[u][j] and
+ * has scale 0 and signed-zero codes; a block holding NaN gets scale 0x7FC00000
+ * and codes 0x7F, one holding +-Inf (no NaN) scale +Inf, codes 0x7F for the
+ * infinities and signed zeros for finite values; with EP_DISPATCH_SCALES_UE8M0
+ * the scale of each 32-channel block is 2^k for the smallest k in [-127, 127]
+ * with 448 * 2^k >= amax, stored as the byte k + 127, code = E4M3FN of
+ * x / 2^k, and a non-finite block gets the byte 0xFF and the codes above;
+ * UE8M0 is row-major, for this call and ep_dispatch_cached only, and not with
+ * EP_DISPATCH_SCALES_COL_MAJOR), recv_weights = topk_weights[u][j] and
  * recv_src_meta = (u, j).  Padding rows get weight 0, meta (-1, -1) and, with
  * EP_DISPATCH_ZERO_PADDING, a zero payload (and zero scales); otherwise their
  * payload is left as it was ("Ascend DeepEP MoE Dispatch Optimization",

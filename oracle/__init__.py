@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_quantize_row_ue8m0.argtypes = [P_, i32, P_, P_]
         L.oracle_quantize_row_ue8m0.restype = None
         L.oracle_quantize_rows.argtypes = [P_, i32, i64, i64, P_, P_]
+        L.oracle_quantize_rows_ue8m0.argtypes = [P_, i32, i64, i64, P_, P_]
+        L.oracle_quantize_rows_ue8m0.restype = None
         L.oracle_quantize_rows.restype = None
         for fn in ("oracle_e4m3_encode_array", "oracle_e4m3_decode_array", "oracle_bf16_round_array"):
             getattr(L, fn).argtypes = [P_, i64, P_]
@@ -367,6 +369,18 @@ def quantize_rows(x: np.ndarray, H: int, row_begin: int = 0, row_end: int | None
     scales = np.zeros((n, H // 128), np.float32)
     lib().oracle_quantize_rows(_p(x), H, row_begin, row_end, _p(codes), _p(scales))
     return codes, scales
+
+
+def quantize_rows_ue8m0(x: np.ndarray, H: int, row_begin: int = 0, row_end: int | None = None):
+    """``oracle_quantize_row_ue8m0`` on rows [row_begin, row_end) of x -> (codes, exponent bytes)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16).reshape(-1, H)
+    if row_end is None:
+        row_end = x.shape[0]
+    n = row_end - row_begin
+    codes = np.zeros((n, H), np.uint8)
+    exps = np.zeros((n, H // 32), np.uint8)
+    lib().oracle_quantize_rows_ue8m0(_p(x), H, row_begin, row_end, _p(codes), _p(exps))
+    return codes, exps
 
 
 def e4m3_encode(q: np.ndarray) -> np.ndarray:

@@ -335,6 +335,15 @@ void oracle_quantize_row_ue8m0(const uint16_t *x, int H, uint8_t *codes, uint8_t
   }
 }
 
+/* oracle_quantize_row_ue8m0 applied to rows [row_begin, row_end) of x [T][H];
+ * the outputs hold only those rows. */
+void oracle_quantize_rows_ue8m0(const uint16_t *x, int H, int64_t row_begin, int64_t row_end,
+                                uint8_t *codes, uint8_t *exps) {
+  for (int64_t u = row_begin; u < row_end; u++)
+    oracle_quantize_row_ue8m0(x + u * H, H, codes + (u - row_begin) * H,
+                              exps + (u - row_begin) * (H / 32));
+}
+
 /* oracle_quantize_row applied to rows [row_begin, row_end) of x [T][H]; the
  * outputs hold only those rows. */
 void oracle_quantize_rows(const uint16_t *x, int H, int64_t row_begin, int64_t row_end,

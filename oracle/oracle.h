@@ -30,6 +30,8 @@ int oracle_layout(int P, int S, int E, int K, int A, int symmetric, const int64_
                   int64_t *recv_src_base);
 void oracle_quantize_row(const uint16_t *x, int H, uint8_t *codes, float *scales);
 void oracle_quantize_row_ue8m0(const uint16_t *x, int H, uint8_t *codes, uint8_t *exps);
+void oracle_quantize_rows_ue8m0(const uint16_t *x, int H, int64_t row_begin, int64_t row_end,
+                                uint8_t *codes, uint8_t *exps);
 void oracle_quantize_rows(const uint16_t *x, int H, int64_t row_begin, int64_t row_end,
                           uint8_t *codes, float *scales);
 int oracle_dispatch(int P, int S, int E, int K, int H, int A, int fp8, int zero_padding,

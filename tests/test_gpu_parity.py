@@ -1637,3 +1637,151 @@ def test_column_major_fp8_calls_through_the_c_abi_on_two_streams():
         np.testing.assert_array_equal(outs[i][1].cpu().numpy().view(np.uint32), osc.view(np.uint32))
     del busy
     h.free()
+
+
+# --------------------------------------------------------------------------
+# UE8M0 scales: one power-of-two exponent byte per 32 channels
+# --------------------------------------------------------------------------
+
+UE8M0_CASES = [D["tiny-p4-s64-e16-k2-h512"],
+               synth.scaled(D["dsv3-bf16-p8-s4096-e256-k8-h7168"], S=300),
+               synth.scaled(D["ep128-zipf-p128-s1024-e256-k6-h7168"], S=70, H=1024),
+               wl.Workload("ue8m0-p4-s65-e32-k3-h8320", 4, 65, 32, 3, 8320, 8, True, "uniform", seed=81)]
+
+
+def _ue8m0_edge_rows(T, H, seed):
+    """bf16 rows whose 32-channel blocks exercise the exponent choice: the maximum exactly
+    448 * 2^k, a mantissa just above 1.75, exact powers of two, zeros, subnormals, the
+    smallest normal, the largest finite bf16, NaN and Inf; the rest N(0,1)."""
+    rng = np.random.default_rng(seed)
+    x = synth.gen_bf16_rows(seed, wl.STREAM_X, T, H).copy()
+    for u in range(T):
+        for b in range(H // 32):
+            blk = x[u, 32 * b:32 * (b + 1)]
+            kind = (u + b) % 10
+            at = int(rng.integers(0, 32))
+            if kind == 1:
+                blk[at] = (((127 + 8 + int(rng.integers(-30, 30))) << 7) | 0x60)
+            elif kind == 2:
+                blk[at] = (int(rng.integers(100, 150)) << 7) | 0x61
+            elif kind == 3:
+                blk[:] = 0x8000 * rng.integers(0, 2, 32).astype(np.uint16)
+            elif kind == 4:
+                blk[:] = rng.integers(1, 0x80, 32).astype(np.uint16)
+                blk[at] = 0x0080
+            elif kind == 5:
+                blk[at] = 0x7F7F
+            elif kind == 6:
+                blk[at] = int(rng.choice([0x7FC0, 0xFF81]))
+            elif kind == 7:
+                blk[at] = int(rng.choice([0x7F80, 0xFF80]))
+            x[u, 32 * b:32 * (b + 1)] = blk
+    return x
+
+
+@pytest.mark.parametrize("w", UE8M0_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("mode", ["exact", "fixed"])
+@pytest.mark.parametrize("zp", [True, False], ids=["zero-pad", "no-pad"])
+def test_ue8m0_dispatch_small(w, mode, zp):
+    """Fresh and cached fp8 dispatch with UE8M0 scales, codes and exponent bytes bit for bit
+    against the oracle (edge-value rows: NaN, Inf, exact 448 * 2^k maxima, subnormals),
+    exact and fixed windows, with and without zero padding."""
+    topk = routing_with_holes(w, 23)
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk)
+    W = int(lay.num_expanded.max()) + 5 if mode == "fixed" else 0
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A, num_worst_rows=W), torch.from_numpy(topk).to(DEV))
+    x = _ue8m0_edge_rows(w.T, w.H, 24)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    R = h.total_rows
+    rx = torch.full((R, w.H), 0x33, dtype=torch.uint8, device=DEV)
+    sc = torch.full((R, w.H // 32), 0x33, dtype=torch.uint8, device=DEV)
+    rw = torch.empty(R, dtype=torch.float32, device=DEV)
+    rm = torch.empty((R, 2), dtype=torch.int32, device=DEV)
+    say("ue8m0", w.name, mode, zp)
+    ep.dispatch(h, xd, wd, zero_padding=zp, scales_ue8m0=True, out=(rx, sc, rw, rm))
+    torch.cuda.synchronize()
+    ox, osc, ow, om, _ = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=zp, topk_weights=wt, x=x,
+                                                 capacity=W, scales_ue8m0=True, fill=0x33)
+    np.testing.assert_array_equal(rx.cpu().numpy(), ox)
+    np.testing.assert_array_equal(sc.cpu().numpy(), osc)
+    np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+    np.testing.assert_array_equal(rm.cpu().numpy(), om)
+    assert (osc == 0xFF).any() and (osc == 0).any()
+    # cached dispatch of other x into the same buffers
+    x2 = synth.gen_bf16_rows(w.seed + 5, wl.STREAM_X, w.T, w.H)
+    ep.dispatch_cached(h, dev_bf16(x2), zero_padding=zp, scales_ue8m0=True, out=(rx, sc))
+    torch.cuda.synchronize()
+    ox2, osc2, _, _, _ = oracle.dispatch_general(lay, w.H, fp8=True, zero_padding=zp, x=x2, capacity=W,
+                                                 scales_ue8m0=True, with_meta=False, fill=0x33)
+    # rows the cached call leaves alone still hold the first fill, as the oracle's do
+    np.testing.assert_array_equal(rx.cpu().numpy(), ox2)
+    np.testing.assert_array_equal(sc.cpu().numpy(), osc2)
+    h.free()
+
+
+def test_ue8m0_full_size():
+    """The DSv3 fp8 workload with UE8M0 scales: every valid row's codes and exponent bytes
+    against the oracle's per-token encoding, zero padding, and one cached iteration."""
+    w = D["dsv3-fp8-p8-s4096-e256-k8-h7168"]
+    topk = synth.gen_routing(w)
+    lay, h = layout_both(w, topk)
+    x = synth.gen_x(w)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    rx, sc, rw, rm = ep.dispatch(h, xd, wd, zero_padding=True, scales_ue8m0=True)
+    torch.cuda.synchronize()
+    assert sc.dtype == torch.uint8 and tuple(sc.shape) == (h.total_rows, w.H // 32)
+    for it in (0, 1):
+        if it:
+            x = synth.workloads.gen_cached_x(w, 1)
+            xd = dev_bf16(x)
+            rx.fill_(0x33)
+            sc.fill_(0x33)
+            ep.dispatch_cached(h, xd, zero_padding=True, scales_ue8m0=True, out=(rx, sc))
+            torch.cuda.synchronize()
+        say("ue8m0 full size, iteration", it)
+        codes = np.empty((w.T, w.H), np.uint8)
+        exps = np.empty((w.T, w.H // 32), np.uint8)
+        oracle_over_ranges(lambda a, b: oracle.quantize_rows_ue8m0(x, w.H, a, b)[0], w.T, codes)
+        oracle_over_ranges(lambda a, b: oracle.quantize_rows_ue8m0(x, w.H, a, b)[1], w.T, exps)
+        codes_d, exps_d = torch.from_numpy(codes).to(DEV), torch.from_numpy(exps).to(DEV)
+        El = w.E // w.P
+        for j in range(w.K):
+            m = topk[:, j] >= 0
+            us = np.flatnonzero(m)
+            rows = lay.window_row_base[topk[m, j] // El] + lay.dst_slot[m, j]
+            assert torch.equal(gather_rows(rx, rows), gather_rows(codes_d, us)), j
+            assert torch.equal(gather_rows(sc, rows), gather_rows(exps_d, us)), j
+        pad = np.flatnonzero(rm.cpu().numpy()[:, 0] < 0)
+        assert int(gather_rows(rx, pad).max()) == 0 and int(gather_rows(sc, pad).max()) == 0
+    h.free()
+
+
+def test_ue8m0_refusals():
+    """UE8M0 scales are row-major and come from the fused quantisation: with column-major
+    scales or pre-quantised input the call fails before anything is enqueued."""
+    w = SMALL[0]
+    topk = synth.gen_routing(w)
+    h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A), torch.from_numpy(topk).to(DEV))
+    R = h.total_rows
+    xd = dev_bf16(synth.gen_x(w))
+    wd = torch.from_numpy(synth.gen_weights(w)).to(DEV)
+    L = ep.lib()
+    import ctypes
+    vp = ctypes.c_void_p
+    rx = torch.full((R, w.H), 0x33, dtype=torch.uint8, device=DEV)
+    sc = torch.full((R, w.H // 32), 0x33, dtype=torch.uint8, device=DEV)
+    rw = torch.empty(R, dtype=torch.float32, device=DEV)
+    rm = torch.empty((R, 2), dtype=torch.int32, device=DEV)
+    st = L.ep_dispatch(vp(h.ptr), 1 | 4 | 8, vp(xd.data_ptr()), vp(wd.data_ptr()), vp(rx.data_ptr()),
+                       vp(sc.data_ptr()), vp(rw.data_ptr()), vp(rm.data_ptr()), vp(0))
+    assert st == ep.Status.ERR_SHAPE and b"UE8M0" in L.ep_last_error()
+    codes = torch.zeros((w.T, w.H), dtype=torch.uint8, device=DEV)
+    xs = torch.zeros((w.T, w.H // 128), dtype=torch.float32, device=DEV)
+    st = L.ep_dispatch_prequant(vp(h.ptr), 8, vp(codes.data_ptr()), vp(xs.data_ptr()), vp(wd.data_ptr()),
+                                vp(rx.data_ptr()), vp(sc.data_ptr()), vp(rw.data_ptr()), vp(rm.data_ptr()), vp(0))
+    assert st == ep.Status.ERR_SHAPE
+    torch.cuda.synchronize()
+    assert bool((rx == 0x33).all()) and bool((sc == 0x33).all())
+    h.free()

@@ -532,6 +532,11 @@ def test_quantize_row_ue8m0_exponent_codes_and_packs(golden):
             np.testing.assert_array_equal(cb, brute_force_e4m3(q), err_msg=f"row {r} block {b}")
             assert np.all((cb & 0x7F) <= 0x7E)
     assert seen_eq and seen_up
+    bc, be = oracle.quantize_rows_ue8m0(x, H, 3, 9)  # the batched form is the per-row form
+    for r in range(3, 9):
+        c1, e1 = oracle.quantize_row_ue8m0(x[r])
+        np.testing.assert_array_equal(bc[r - 3], c1)
+        np.testing.assert_array_equal(be[r - 3], e1)
 
 
 def test_dispatch_fp8_ue8m0_rows():
