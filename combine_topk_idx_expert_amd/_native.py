@@ -143,6 +143,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, fn).restype = i32
         L.ep_debug_e4m3_encode.argtypes = [vp, vp, i64, vp]
         L.ep_debug_e4m3_encode.restype = i32
+        L.ep_debug_timing.argtypes = [vp, i64]
+        L.ep_debug_timing.restype = i32
         L.ep_debug_copy.argtypes = [vp, vp, i64, vp]
         L.ep_debug_copy.restype = i32
         L.ep_last_error.argtypes = []

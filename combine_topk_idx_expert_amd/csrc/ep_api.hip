@@ -86,7 +86,8 @@ struct ep_handle {
   hipEvent_t summary_ready = nullptr;  // the last layout's host summary has landed
   hipEvent_t cm_done = nullptr;     // end of the last column-major fp8 dispatch (tok_scales free again)
   bool cm_recorded = false;
-  size_t lds_count, lds_scan, lds_finalize, lds_rank;
+  size_t lds_count, lds_scan, lds_finalize, lds_rank, lds_small;
+  bool small_layout = false;  // the whole layout in one workgroup (layout_small_kernel)
 };
 
 namespace {
@@ -196,10 +197,11 @@ ep_status allocate(ep_handle* h) {
   e = hipEventCreateWithFlags(&h->cm_done, hipEventDisableTiming);
   if (e != hipSuccess) return fail(EP_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
 
-  h->lds_count = (size_t)(d.ncols + kChunk * ((d.P + 31) / 32) + kChunk * d.K) * 4;
+  h->lds_count = (size_t)(kLayoutWaves * d.ncols + kChunk * ((d.P + 31) / 32) + kChunk * d.K) * 4;
   h->lds_scan = (size_t)(((d.P + 2) & ~1) * 4 + (kScanThreads / 64) * 8);
-  h->lds_finalize = (size_t)((d.E + 1) + ((d.E + 2) / 2) + 1 + kFinalizeThreads / 64) * 8 + (size_t)d.ncols * 4;
-  h->lds_rank = (size_t)(kLayoutWaves * ((d.E + 1) + (d.P + 1)) + 2 * kChunk * d.K) * 4;
+  h->lds_finalize = (size_t)finalize_lds_words(d, kFinalizeThreads) * 8 + (size_t)d.ncols * 4;
+  h->lds_rank = (size_t)(kLayoutWaves * d.ncols + 2 * kChunk * d.K) * 4;
+  h->lds_small = small_lds_bytes(d);
   int lds_max = 0;
   if (hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, h->device) != hipSuccess)
     return fail(EP_ERR_HIP, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock) failed");
@@ -207,6 +209,8 @@ ep_status allocate(ep_handle* h) {
   if (lds_need > (size_t)lds_max)
     return fail(EP_ERR_SHAPE, "layout needs %zu bytes of LDS per workgroup, the device has %d (E=%d P=%d K=%d)",
                 lds_need, lds_max, d.E, d.P, d.K);
+  // small batches: one launch for the whole layout when it fits one workgroup
+  h->small_layout = d.num_chunks <= kSmallChunks && h->lds_small <= kSmallLdsMax && h->lds_small <= (size_t)lds_max;
   return EP_OK;
 }
 
@@ -270,26 +274,32 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
   if (capturing && !h->fixed)
     return fail(EP_ERR_HIP, "exact windows read the row counts back to the host and cannot be captured in a "
                             "graph; use fixed windows (num_worst_rows > 0)");
-  if (d.num_chunks > 0) {
-    layout_count_kernel<<<d.num_chunks, kLayoutThreads, h->lds_count, s>>>(d, topk_idx, h->is_token_in_rank,
-                                                                   h->chunk_hist);
-    EP_LAUNCHED("layout_count_kernel");
-  }
-  layout_scan_kernel<<<d.ncols, kScanThreads, h->lds_scan, s>>>(
-      d, h->chunk_hist, h->chunk_excl_t, h->col_total, h->num_tokens_per_expert, h->num_tokens_per_rank,
-      h->rank_prefix_matrix);
-  EP_LAUNCHED("layout_scan_kernel");
   FinalizeOut fo{h->n_e, h->expert_offset, h->num_expanded, h->window_row_base, h->num_recv,
                  h->recv_src_base, h->pad_base, h->pad_rows, h->packed_base, h->row_slot, h->tail_base,
                  h->summary_dev, h->summary_host_dev, ++h->layout_seq};
-  layout_finalize_kernel<<<1, kFinalizeThreads, h->lds_finalize, s>>>(d, h->col_total, fo);
-  EP_LAUNCHED("layout_finalize_kernel");
-  if (!capturing) EP_HIP(hipEventRecord(h->summary_ready, s));  // the finalize kernel wrote the host summary
-  {
-    // at least one workgroup per expert, so that the padding rows are written even when T = 0
-    RankOut ro{h->dst_slot, h->dst_row, h->row_slot, h->send_head, h->recv_src_idx, h->pad_rows};
-    RankIn ri{h->chunk_excl_t, h->n_e, h->pad_base, h->expert_offset, h->window_row_base, h->packed_base,
-              h->recv_src_base};
+  RankOut ro{h->dst_slot, h->dst_row, h->row_slot, h->send_head, h->recv_src_idx, h->pad_rows};
+  RankIn ri{h->chunk_excl_t, h->n_e, h->pad_base, h->expert_offset, h->window_row_base, h->packed_base,
+            h->recv_src_base};
+  if (h->small_layout) {
+    layout_small_kernel<<<1, kSmallThreads, h->lds_small, s>>>(d, topk_idx, h->is_token_in_rank,
+                                                               h->num_tokens_per_expert, h->num_tokens_per_rank,
+                                                               h->rank_prefix_matrix, fo, ri, ro);
+    EP_LAUNCHED("layout_small_kernel");
+    if (!capturing) EP_HIP(hipEventRecord(h->summary_ready, s));
+  } else {
+    if (d.num_chunks > 0) {
+      layout_count_kernel<<<d.num_chunks, kLayoutThreads, h->lds_count, s>>>(d, topk_idx, h->is_token_in_rank,
+                                                                     h->chunk_hist);
+      EP_LAUNCHED("layout_count_kernel");
+    }
+    layout_scan_kernel<<<d.ncols, kScanThreads, h->lds_scan, s>>>(
+        d, h->chunk_hist, h->chunk_excl_t, h->col_total, h->num_tokens_per_expert, h->num_tokens_per_rank,
+        h->rank_prefix_matrix);
+    EP_LAUNCHED("layout_scan_kernel");
+    layout_finalize_kernel<<<1, kFinalizeThreads, h->lds_finalize, s>>>(d, h->col_total, fo);
+    EP_LAUNCHED("layout_finalize_kernel");
+    if (!capturing) EP_HIP(hipEventRecord(h->summary_ready, s));  // the finalize kernel wrote the host summary
+    // at least one workgroup, so that the padding rows are written even when T = 0
     layout_rank_kernel<<<std::max(d.num_chunks, 1), kLayoutThreads, h->lds_rank, s>>>(d, topk_idx, ri, ro);
     EP_LAUNCHED("layout_rank_kernel");
   }
@@ -703,6 +713,21 @@ ep_status ep_debug_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* s
   e4m3_encode_kernel<<<(int)((threads + 255) / 256), 256, 0, (hipStream_t)stream>>>(in, out, n);
   EP_LAUNCHED("e4m3_encode_kernel");
   return EP_OK;
+}
+
+ep_status ep_debug_timing(uint64_t* slots, int64_t n) {
+#if EP_DEVICE_TIMING
+  if (!slots) return fail(EP_ERR_NULL, "slots is NULL");
+  const int64_t all = (int64_t)kEpTimingKernels * kEpTimingPhases * kEpTimingGroups;
+  if (n < 0 || n > all) return fail(EP_ERR_SHAPE, "n must be in [0, %lld]", (long long)all);
+  EP_HIP(hipMemcpyFromSymbol(slots, HIP_SYMBOL(ep_timing_slots), (size_t)n * sizeof(uint64_t), 0,
+                             hipMemcpyDeviceToHost));
+  return EP_OK;
+#else
+  (void)slots;
+  (void)n;
+  return fail(EP_ERR_SHAPE, "the library was built without EP_DEVICE_TIMING");
+#endif
 }
 
 const char* ep_last_error(void) { return g_last_error.c_str(); }

@@ -5,6 +5,33 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Device-side timing slots (compile-time switch, off by default): with
+// EP_DEVICE_TIMING=1 every kernel stamps the device's constant-rate clock
+// (wall_clock64, 100 MHz on MI355X) at its phase boundaries, one slot per
+// (kernel, phase, workgroup) for the first kEpTimingGroups workgroups, so a
+// profile can split a kernel's time into its steps without a profiler.  Off,
+// the marks compile to nothing.
+#ifndef EP_DEVICE_TIMING
+#define EP_DEVICE_TIMING 0
+#endif
+constexpr int kEpTimingKernels = 8;   // kernel ids, see EP_TK_*
+constexpr int kEpTimingPhases = 8;
+constexpr int kEpTimingGroups = 1024;
+enum { EP_TK_COUNT = 0, EP_TK_SCAN, EP_TK_FINALIZE, EP_TK_RANK, EP_TK_SMALL, EP_TK_DISPATCH, EP_TK_COMBINE };
+#if EP_DEVICE_TIMING
+__device__ uint64_t ep_timing_slots[kEpTimingKernels * kEpTimingPhases * kEpTimingGroups];
+#define EP_TIMING_MARK(kernel, phase)                                                                    \
+  do {                                                                                                   \
+    if (threadIdx.x == 0 && blockIdx.x < (unsigned)kEpTimingGroups)                                      \
+      ::ep_timing_slots[((kernel) * kEpTimingPhases + (phase)) * kEpTimingGroups + blockIdx.x] =        \
+          (uint64_t)wall_clock64();                                                                      \
+  } while (0)
+#else
+#define EP_TIMING_MARK(kernel, phase) \
+  do {                                \
+  } while (0)
+#endif
+
 namespace ep {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

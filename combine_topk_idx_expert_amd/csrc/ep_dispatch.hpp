@@ -254,6 +254,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
   uint8_t* recv = (uint8_t*)a.recv_x;
   const int token_items = a.T * a.split;
   const int pad_items = FIXED ? a.zero_waves : a.zero_pad ? a.total_pad * a.split : 0;
+  EP_TIMING_MARK(EP_TK_DISPATCH, 0);
 
   if (gw < token_items) {
     const int u = gw / a.split;
@@ -514,6 +515,7 @@ template <int NCT, int G>
 __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
 #pragma clang fp contract(off)
   const int gw = wave_index();
+  EP_TIMING_MARK(EP_TK_COMBINE, 0);
   if (gw >= a.T * a.split) return;
   const int u = gw / a.split;  // ascending tokens: measured faster than descending
   const int part = gw % a.split;

@@ -346,6 +346,19 @@ ep_status ep_debug_e4m3_encode(const float *in, uint8_t *out, int64_t n, void *s
  * is compared with.  Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_OVERFLOW, EP_ERR_HIP. */
 ep_status ep_debug_copy(void *dst, const void *src, int64_t nbytes, void *stream);
 
+/* Profiling hook, not part of the method: the device-side timing slots of a
+ * library built with EP_DEVICE_TIMING=1 ("Ascend DeepEP MoE Dispatch
+ * Optimization", section "Measure time and bytes correctly first", device-side
+ * timing).  Every kernel then stamps the device's constant-rate clock
+ * (100 MHz) at its phase boundaries: slot ((kernel * 8 + phase) * 1024 +
+ * workgroup) for the first 1024 workgroups, kernel 0 count, 1 scan,
+ * 2 finalize, 3 rank, 4 the one-workgroup layout, 5 dispatch, 6 combine.
+ * Copies the first n slots (synchronously) into host memory `slots`.  A slot
+ * keeps the last stamp written to it.  Built without the switch (the
+ * default), the kernels stamp nothing and this returns EP_ERR_SHAPE.
+ * Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_HIP. */
+ep_status ep_debug_timing(uint64_t *slots, int64_t n);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char *ep_last_error(void);
 

@@ -118,6 +118,88 @@ def test_layout_small(w, holes):
     h.free()
 
 
+# Shapes of at most 16 chunks of 64 tokens, whose layout runs as one workgroup, and one of
+# 17 chunks just past that limit (four kernels).
+SMALL_BATCH = [
+    wl.Workload("sb-p4-s64-e16-k2", 4, 64, 16, 2, 512, 16, True, "uniform", seed=31),       # 4 chunks
+    wl.Workload("sb-p16-s64-e64-k6", 16, 64, 64, 6, 256, 8, True, "uniform", seed=32),      # 16 chunks
+    wl.Workload("sb-p8-s100-e256-k8", 8, 100, 256, 8, 1024, 128, True, "uniform", seed=33),  # 16 ragged chunks
+    wl.Workload("sb-p1-s1-e8-k3", 1, 1, 8, 3, 128, 4, True, "uniform", seed=34),            # 1 token
+    wl.Workload("sb-p2-s7-e512-k4", 2, 7, 512, 4, 256, 3, True, "uniform", seed=35),         # many experts
+    wl.Workload("sb-p17-s64-e34-k3", 17, 64, 34, 3, 256, 2, True, "uniform", seed=36),      # 17 chunks
+]
+
+
+@pytest.mark.parametrize("w", SMALL_BATCH, ids=lambda w: w.name)
+@pytest.mark.parametrize("mode", ["exact", "fixed", "symmetric"])
+def test_small_batch_layout(w, mode):
+    """Decode-sized batches: every handle array against the oracle with holes, duplicate
+    experts and tokens routed nowhere (fixed windows: also an out-of-range id, reported as a
+    status, and a window that truncates), then dispatch and combine against the oracle."""
+    topk = routing_with_holes(w, 41)
+    if mode == "fixed":
+        topk = topk.copy()
+        topk[0, 0] = w.E + 3  # out of range: counted as unused, reported as a status
+    lay = oracle.layout(w.P, w.S, w.E, w.K, w.A, np.where(topk >= w.E, -1, topk), mode == "symmetric")
+    x = synth.gen_bf16_rows(w.seed, wl.STREAM_X, w.T, w.H)
+    wt = synth.gen_weights(w)
+    xd, wd = dev_bf16(x), torch.from_numpy(wt).to(DEV)
+    if mode == "fixed":
+        W = max(1, int(np.median(lay.num_expanded)))  # some windows truncate
+        h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A, num_worst_rows=W), torch.from_numpy(topk).to(DEV))
+        torch.cuda.synchronize()
+        check_fixed_layout(lay, h, W)
+        flags, dropped = h.status()
+        exp_drop = int(np.maximum(lay.num_expanded - W, 0).sum())
+        assert flags & ep.STATUS_ROUTING and dropped == exp_drop
+        assert bool(flags & ep.STATUS_TRUNCATED) == (exp_drop > 0)
+        rx, _, rw, rm = ep.dispatch(h, xd, wd, zero_padding=True)
+        torch.cuda.synchronize()
+        ox, _, ow, om, _ = oracle.dispatch_general(lay, w.H, fp8=False, zero_padding=True, topk_weights=wt, x=x,
+                                                   capacity=W)
+        np.testing.assert_array_equal(host_u16(rx), ox)
+        np.testing.assert_array_equal(rm.cpu().numpy(), om)
+        out = ep.combine(h, rx, wd)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_u16(out), oracle.combine_general(lay, w.H, ox, wt, capacity=W))
+    else:
+        h = ep.get_layout(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A, mode == "symmetric"), torch.from_numpy(topk).to(DEV))
+        torch.cuda.synchronize()
+        check_layout(lay, h)
+        rx, _, rw, rm = ep.dispatch(h, xd, wd, zero_padding=True)
+        torch.cuda.synchronize()
+        ox, _, ow, om = oracle.dispatch(lay, w.H, x, wt, False, True)
+        got = host_u16(rx)
+        in_win = np.zeros(len(om), bool)  # symmetric windows leave the rows past num_expanded alone
+        for d_ in range(w.P):
+            in_win[lay.window_row_base[d_]:lay.window_row_base[d_] + lay.num_expanded[d_]] = True
+        np.testing.assert_array_equal(got[in_win], ox[in_win])
+        np.testing.assert_array_equal(rm.cpu().numpy()[in_win], om[in_win])
+        np.testing.assert_array_equal(rw.cpu().numpy()[in_win].view(np.uint32), ow[in_win].view(np.uint32))
+        out = ep.combine(h, rx, wd)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_u16(out), oracle.combine(lay, w.H, got, wt))
+    # relayout of the same handle with another routing
+    topk2 = routing_with_holes(w, 42)
+    lay2 = oracle.layout(w.P, w.S, w.E, w.K, w.A, topk2, mode == "symmetric")
+    ep.relayout(h, torch.from_numpy(topk2).to(DEV))
+    torch.cuda.synchronize()
+    if mode == "fixed":
+        check_fixed_layout(lay2, h, W)
+    else:
+        check_layout(lay2, h)
+    h.free()
+
+
+def test_small_batch_empty():
+    """No tokens at all (S = 0) through the one-workgroup layout: zero counts, no rows."""
+    w = wl.Workload("sb-empty", 4, 0, 16, 2, 128, 4, True, "uniform")
+    lay, h = layout_both(w, np.zeros((0, 2), np.int64))
+    check_layout(lay, h)
+    assert h.total_rows == 0
+    h.free()
+
+
 def test_layout_symmetric_windows():
     w = SMALL[2]
     topk = synth.gen_routing(w)
