@@ -28,6 +28,7 @@ from ._native import (  # noqa: F401
     STATUS_TRUNCATED,
     Status,
     TENSORS,
+    buffer_size_hint,
     combine,
     comm_stream,
     debug_copy,

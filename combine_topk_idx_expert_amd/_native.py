@@ -79,6 +79,12 @@ class _Config(ctypes.Structure):
     ]
 
 
+class _SizeHint(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in (
+        "handle_bytes", "max_rows", "recv_x_bytes", "recv_scales_bytes", "recv_weights_bytes",
+        "recv_src_meta_bytes", "combine_out_bytes", "total_bytes")]
+
+
 @dataclasses.dataclass(frozen=True)
 class Config:
     """P virtual ranks x S tokens, hidden H, top-K of E experts, expert_alignment A.
@@ -122,6 +128,8 @@ def lib() -> ctypes.CDLL:
         vp, i32, u32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64
         L.ep_get_layout.argtypes = [ctypes.POINTER(_Config), vp, vp, ctypes.POINTER(vp), ctypes.POINTER(i64)]
         L.ep_relayout.argtypes = [vp, vp, vp, ctypes.POINTER(i64)]
+        L.ep_buffer_size_hint.argtypes = [ctypes.POINTER(_Config), u32, ctypes.POINTER(_SizeHint)]
+        L.ep_buffer_size_hint.restype = i32
         L.ep_dispatch.argtypes = [vp, u32, vp, vp, vp, vp, vp, vp, vp]
         L.ep_dispatch_noalloc.argtypes = [vp, u32, vp, vp, vp, vp, vp, vp, vp]
         L.ep_dispatch_cached.argtypes = [vp, u32, vp, vp, vp, vp]
@@ -362,6 +370,16 @@ def _overlapped(h, device, tensors, launch, previous_event):
     h._pending = [e for e in h._pending if not e.query()]
     h._pending.append(done)  # h.free() waits for it
     return EventOverlap(done, result)
+
+
+def buffer_size_hint(cfg: Config, fp8: bool = False, scales_ue8m0: bool = False) -> dict:
+    """ep_buffer_size_hint: device bytes the config needs (handle arena, expanded tensors at
+    their largest row count, combine output, total rounded up to 2 MiB), computed on the host;
+    nothing is allocated."""
+    out = _SizeHint()
+    _check(lib().ep_buffer_size_hint(ctypes.byref(cfg._c()), _flags(fp8, False, False, scales_ue8m0),
+                                     ctypes.byref(out)))
+    return {name: getattr(out, name) for name, _ in _SizeHint._fields_}
 
 
 def get_layout(cfg: Config, topk_idx) -> Handle:

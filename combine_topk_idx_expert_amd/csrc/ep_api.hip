@@ -140,7 +140,10 @@ LayoutDims make_dims(const ep_config& c) {
   return d;
 }
 
-ep_status allocate(ep_handle* h) {
+// The handle's device arrays, laid end to end in one arena (each aligned to
+// 256 bytes): returns the arena's size; with base != nullptr, also points the
+// handle's members into it.  Uses only h->cfg, h->dims and h->T.
+size_t arena_layout(ep_handle* h, uint8_t* base) {
   const LayoutDims& d = h->dims;
   const int64_t T = h->T, P = d.P, E = d.E, K = d.K;
   struct Item {
@@ -174,16 +177,22 @@ ep_status allocate(ep_handle* h) {
       {(void**)&h->tail_base, (size_t)((P + 1) * 8)},
       {(void**)&h->tok_scales, (size_t)(h->cfg.hidden % 128 == 0 ? T * (h->cfg.hidden / 128) * 4 : 0)},
   };
-  size_t total = 0;
-  for (const Item& it : items) total += align_up(std::max<size_t>(it.bytes, 1));
+  size_t off = 0;
+  for (const Item& it : items) {
+    if (base) *it.ptr = base + off;
+    off += align_up(std::max<size_t>(it.bytes, 1));
+  }
+  return off;
+}
+
+ep_status allocate(ep_handle* h) {
+  const LayoutDims& d = h->dims;
+  const int64_t P = d.P;
+  const size_t total = arena_layout(h, nullptr);
   hipError_t e = hipMalloc(&h->arena, total);
   if (e != hipSuccess) return fail(EP_ERR_NOMEM, "hipMalloc(%zu): %s", total, hipGetErrorString(e));
   h->arena_bytes = total;
-  size_t off = 0;
-  for (const Item& it : items) {
-    *it.ptr = (uint8_t*)h->arena + off;
-    off += align_up(std::max<size_t>(it.bytes, 1));
-  }
+  arena_layout(h, (uint8_t*)h->arena);
   e = hipHostMalloc((void**)&h->summary_host, (size_t)((kSummaryHeader + 3 * P + 2) * 8),
                     hipHostMallocMapped | hipHostMallocCoherent);
   if (e != hipSuccess) return fail(EP_ERR_NOMEM, "hipHostMalloc: %s", hipGetErrorString(e));
@@ -535,6 +544,45 @@ ep_status ep_get_layout(const ep_config* cfg, const int64_t* topk_idx, void* str
     return st;
   }
   *out = h;
+  return EP_OK;
+}
+
+ep_status ep_buffer_size_hint(const ep_config* cfg, uint32_t dispatch_flags, ep_size_hint* out) {
+  if (!out) return fail(EP_ERR_NULL, "out is NULL");
+  ep_status st = validate_config(cfg);
+  if (st != EP_OK) return st;
+  if (dispatch_flags & ~(uint32_t)(EP_DISPATCH_FP8 | EP_DISPATCH_ZERO_PADDING | EP_DISPATCH_SCALES_COL_MAJOR |
+                                   EP_DISPATCH_SCALES_UE8M0))
+    return fail(EP_ERR_SHAPE, "unknown dispatch flags 0x%x", dispatch_flags);
+  const bool fp8 = dispatch_flags & (EP_DISPATCH_FP8 | EP_DISPATCH_SCALES_UE8M0);
+  if (fp8 && cfg->hidden % 128 != 0)
+    return fail(EP_ERR_SHAPE, "fp8 dispatch needs hidden %% 128 == 0 (hidden %d)", cfg->hidden);
+  ep_handle probe;  // sizes only: nothing is allocated
+  probe.cfg = *cfg;
+  probe.dims = make_dims(*cfg);
+  probe.T = (int64_t)cfg->num_ranks * cfg->num_tokens;
+  const LayoutDims& d = probe.dims;
+  const int64_t T = probe.T, H = cfg->hidden;
+  // every slot valid and every expert one row short of a multiple of A: the
+  // largest total_rows a layout can give (symmetric windows: P times the
+  // largest window, itself at most all slots plus one rank's padding)
+  const int64_t packed = T * d.K + (int64_t)d.E * (d.A - 1);
+  int64_t rows = packed;
+  if (cfg->num_worst_rows > 0)
+    rows = (int64_t)d.P * cfg->num_worst_rows;
+  else if (d.symmetric)
+    rows = (int64_t)d.P * (T * d.K + (int64_t)d.El * (d.A - 1));
+  out->handle_bytes = (int64_t)arena_layout(&probe, nullptr);
+  out->max_rows = rows;
+  out->recv_x_bytes = rows * H * (fp8 ? 1 : 2);
+  out->recv_scales_bytes = fp8 ? rows * (H / 32) : 0;  // fp32 per 128 or UE8M0 per 32: H/32 bytes a row
+  out->recv_weights_bytes = rows * 4;
+  out->recv_src_meta_bytes = rows * 8;
+  out->combine_out_bytes = T * H * 2;
+  const int64_t sum = out->handle_bytes + out->recv_x_bytes + out->recv_scales_bytes + out->recv_weights_bytes +
+                      out->recv_src_meta_bytes + out->combine_out_bytes;
+  const int64_t mib2 = (int64_t)2 << 20;
+  out->total_bytes = (sum + mib2 - 1) / mib2 * mib2;
   return EP_OK;
 }
 

@@ -145,6 +145,38 @@ typedef struct ep_handle ep_handle; /* opaque; owns its device arrays */
 ep_status ep_get_layout(const ep_config *cfg, const int64_t *topk_idx, void *stream,
                         ep_handle **out, int64_t *total_rows);
 
+/* --------------------------------------------------------------------------
+ * ep_buffer_size_hint -- device memory a config needs, computed on the host
+ * without allocating or launching anything (TileLang tutorial ch. 38, section
+ * 3.2: the size hint that lays the buffers out once and returns the byte
+ * count, rounded to 2 MB).
+ *   cfg             as for ep_get_layout (validated the same way).
+ *   dispatch_flags  EP_DISPATCH_* bits of the dispatches that will run (fp8
+ *                   output halves recv_x and adds scales).
+ *   out             host, receives:
+ *     handle_bytes        the device arena ep_get_layout allocates for the handle;
+ *     max_rows            the expanded tensors' row count: P * num_worst_rows in
+ *                         fixed mode, else the largest total_rows any routing can
+ *                         give, T*K + E*(A-1) (packed windows) or
+ *                         P * (T*K + E_l*(A-1)) (symmetric windows);
+ *     recv_x_bytes, recv_scales_bytes, recv_weights_bytes, recv_src_meta_bytes
+ *                         of max_rows rows (fp8 scales: H/32 bytes a row, fp32
+ *                         per 128 channels or UE8M0 per 32);
+ *     combine_out_bytes   T * H * 2;
+ *     total_bytes         the sum, rounded up to a multiple of 2 MiB.
+ * Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_OVERFLOW (as ep_get_layout). */
+typedef struct {
+  int64_t handle_bytes;
+  int64_t max_rows;
+  int64_t recv_x_bytes;
+  int64_t recv_scales_bytes;
+  int64_t recv_weights_bytes;
+  int64_t recv_src_meta_bytes;
+  int64_t combine_out_bytes;
+  int64_t total_bytes;
+} ep_size_hint;
+ep_status ep_buffer_size_hint(const ep_config *cfg, uint32_t dispatch_flags, ep_size_hint *out);
+
 /* ep_relayout -- ep_get_layout into an existing handle for a new topk_idx of
  * the same config, without allocating (one long-lived buffer reused across
  * layers, TileLang tutorial ch. 38, section 2.6).  No call using `h` may be

@@ -134,3 +134,31 @@ def test_c_program_links_against_the_library():
     for lib in ("libep_mi355x.so", "liboracle.so"):
         line = next(ln for ln in out.splitlines() if lib in ln)
         assert "not found" not in line, line
+
+
+def test_buffer_size_hint_needs_no_gpu(L):
+    """ep_buffer_size_hint on the host: row bounds from the closed forms, bytes per tensor,
+    the total a multiple of 2 MiB; validation as for ep_get_layout."""
+    P, S, H, K, E, A = 8, 4096, 7168, 8, 256, 128
+    T = P * S
+    hb = ep.buffer_size_hint(ep.Config(P, S, H, K, E, A))
+    assert hb["max_rows"] == T * K + E * (A - 1)
+    assert hb["recv_x_bytes"] == hb["max_rows"] * H * 2 and hb["recv_scales_bytes"] == 0
+    assert hb["recv_weights_bytes"] == hb["max_rows"] * 4 and hb["recv_src_meta_bytes"] == hb["max_rows"] * 8
+    assert hb["combine_out_bytes"] == T * H * 2
+    # the handle holds at least its [T, P] send_head, [T, K] dst_slot / dst_row and [T, P] is_token_in_rank
+    assert hb["handle_bytes"] >= T * P * 4 + 2 * T * K * 4 + T * P
+    parts = sum(v for k, v in hb.items() if k.endswith("_bytes") and k != "total_bytes")
+    assert hb["total_bytes"] % (2 << 20) == 0 and parts <= hb["total_bytes"] < parts + (2 << 20)
+    h8 = ep.buffer_size_hint(ep.Config(P, S, H, K, E, A), fp8=True)
+    assert h8["recv_x_bytes"] == hb["max_rows"] * H and h8["recv_scales_bytes"] == hb["max_rows"] * (H // 32)
+    assert ep.buffer_size_hint(ep.Config(P, S, H, K, E, A), scales_ue8m0=True)["recv_scales_bytes"] == \
+        h8["recv_scales_bytes"]
+    hf = ep.buffer_size_hint(ep.Config(P, S, H, K, E, A, num_worst_rows=35840))
+    assert hf["max_rows"] == P * 35840
+    hs = ep.buffer_size_hint(ep.Config(P, S, H, K, E, A, symmetric_windows=True))
+    assert hs["max_rows"] == P * (T * K + (E // P) * (A - 1))
+    with pytest.raises(ep.EpError):
+        ep.buffer_size_hint(ep.Config(P, S, H, K, E + 1, A))
+    with pytest.raises(ep.EpError):
+        ep.buffer_size_hint(ep.Config(P, S, 136, K, E, A), fp8=True)

@@ -483,8 +483,13 @@ FULL = [D[n] for n in wl.CONFIG_ORDER]
 @pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
 def test_full_size(w):
     topk = synth.gen_routing(w)
+    free0 = torch.cuda.mem_get_info()[0]
     lay, h = layout_both(w, topk)
     check_layout(lay, h)
+    hint = ep.buffer_size_hint(ep.Config(w.P, w.S, w.H, w.K, w.E, w.A), fp8=w.fp8)
+    assert h.total_rows <= hint["max_rows"]
+    # the handle's device arena, as the hint counts it (allocation granularity aside)
+    assert free0 - torch.cuda.mem_get_info()[0] <= hint["handle_bytes"] + (8 << 20)
     R = lay.total_rows
     say("generate x", w.name)
     x = synth.gen_x(w)
