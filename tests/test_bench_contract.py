@@ -8,7 +8,7 @@ import subprocess
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-LINE = os.path.join(ROOT, "profiles", "bench_line_dsv3-bf16-p8-s4096-e256-k8-h7168.json")
+LINE = os.path.join(ROOT, "profiles", "bench_line_ep32-group-fwdbwd-p32-s8192-e256-k8-h4096.json")
 
 
 def test_more_than_one_gpu_is_refused_with_a_message():
@@ -26,11 +26,17 @@ def test_committed_bench_line_has_every_field():
               "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
         assert k in d, k
     assert d["n_gpus"] == 1 and d["higher_is_better"] is True and d["data"] == "synthetic"
-    assert d["config"]["workload"] == "dsv3-bf16-p8-s4096-e256-k8-h7168"
+    assert d["config"]["workload"] == "ep32-group-fwdbwd-p32-s8192-e256-k8-h4096"
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-9
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0 and c["sample"]
+    assert c["single_thread"]["threads"] == 1 and c["single_thread"]["value"] > 0
+    # the committed line is the default command's: its workload is bench.py's default one
+    sys.path.insert(0, ROOT)
+    import bench
+
+    assert d["config"]["workload"] == bench.DEFAULT_WORKLOAD
     # tokens per second of the whole step: T / ms_per_step
     assert abs(d["value"] - d["config"]["T"] / (d["ms_per_step"] * 1e-3)) / d["value"] < 1e-6
