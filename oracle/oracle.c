@@ -424,7 +424,12 @@ static int dispatch_rows(int P, int S, int E, int K, int H, int A, int fp8, int 
     codes = (uint8_t *)malloc((size_t)H);
     scales = (float *)malloc(sizeof(float) * (size_t)(nb > 0 ? nb : 1));
     exps = (uint8_t *)malloc((size_t)(nb32 > 0 ? nb32 : 1));
-    if (!codes || !scales || !exps) return ORACLE_ERR_SHAPE;
+    if (!codes || !scales || !exps) {
+      free(codes);
+      free(scales);
+      free(exps);
+      return ORACLE_ERR_SHAPE;
+    }
   }
   for (int64_t u = 0; u < T; u++) {
     for (int j = 0; j < K; j++) {
@@ -682,7 +687,12 @@ static int combine_identity_rows(int K, int H, int fp8, const int64_t *topk_idx,
   uint16_t *row = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)H);
   uint8_t *codes = (uint8_t *)malloc((size_t)H);
   float *scales = (float *)malloc(sizeof(float) * (size_t)(H / 128 + 1));
-  if (!row || !codes || !scales) return ORACLE_ERR_SHAPE;
+  if (!row || !codes || !scales) {
+    free(row);
+    free(codes);
+    free(scales);
+    return ORACLE_ERR_SHAPE;
+  }
   for (int64_t u = tok_begin; u < tok_end; u++) {
     if (fp8) {
       oracle_quantize_row(x + u * H, H, codes, scales);

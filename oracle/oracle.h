@@ -40,9 +40,22 @@ int oracle_dispatch(int P, int S, int E, int K, int H, int A, int fp8, int zero_
                     const int64_t *window_row_base, const uint16_t *x, const float *topk_weights,
                     int64_t row_begin, int64_t row_end, void *recv_x, float *recv_scales,
                     float *recv_weights, int32_t *recv_src_meta);
+int oracle_dispatch_general(int P, int S, int E, int K, int H, int A, int fp8, int zero_padding,
+                            int scales_col_major, int64_t capacity, const int64_t *topk_idx,
+                            const int32_t *dst_slot, const int32_t *num_tokens_per_expert_total,
+                            const int64_t *expert_offset, const int64_t *window_row_base,
+                            const uint16_t *x, const uint8_t *x_codes, const float *x_scales,
+                            const float *topk_weights, int64_t row_begin, int64_t row_end,
+                            void *recv_x, float *recv_scales, float *recv_weights,
+                            int32_t *recv_src_meta, int64_t *dropped);
 int oracle_combine(int P, int S, int E, int K, int H, const int64_t *topk_idx,
                    const int32_t *dst_slot, const int64_t *window_row_base, const uint16_t *y,
                    const float *topk_weights, int64_t tok_begin, int64_t tok_end, uint16_t *out);
+int oracle_combine_general(int P, int S, int E, int K, int H, int64_t capacity,
+                           const int64_t *topk_idx, const int32_t *dst_slot,
+                           const int64_t *window_row_base, const uint16_t *y,
+                           const float *topk_weights, const uint16_t *bias, int64_t tok_begin,
+                           int64_t tok_end, uint16_t *out);
 
 #ifdef __cplusplus
 }

@@ -1,12 +1,16 @@
 // roundtrip.cpp -- the C ABI used from C++ alone (no Python): layout, bf16
-// and fp8 dispatch, cached dispatch and combine on a small problem, compared
-// byte for byte with the CPU oracle (linked from oracle/liboracle.so; test
-// code only).  Exit status 0 and one "ok" line when everything matches.
+// and fp8 dispatch, cached dispatch and combine on a small problem; then
+// output buffers sized by ep_buffer_size_hint, fp8 dispatch with UE8M0 scales,
+// ep_dispatch_noalloc with column-major scales, and fixed-length windows
+// (dispatch, status, combine).  Everything is compared byte for byte with the
+// CPU oracle (linked from oracle/liboracle.so; test code only).  Exit status 0
+// and one "ok" line when everything matches.
 //
 // Inputs come from a fixed splitmix64 stream: top-k of distinct experts with
 // some unused (-1) slots, bf16 rows of moderate magnitude, positive weights.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -176,7 +180,119 @@ int main() {
     HIP_OK(hipFree(d_rw));
     HIP_OK(hipFree(d_meta));
   }
+
+  // Output buffers sized by the host-only hint, as a caller allocating the
+  // long-lived buffer once would: bf16 rows need max_rows * 2H bytes, fp8
+  // rows max_rows * H plus H/32 scale bytes a row (fp32 per 128 channels or
+  // UE8M0 per 32).
+  ep_size_hint hb{}, h8{};
+  EP_OK_(ep_buffer_size_hint(&cfg, EP_DISPATCH_ZERO_PADDING, &hb));
+  EP_OK_(ep_buffer_size_hint(&cfg, EP_DISPATCH_FP8 | EP_DISPATCH_ZERO_PADDING, &h8));
+  expect(hb.max_rows >= R && h8.max_rows == hb.max_rows, "size hint: max_rows bounds the layout");
+  expect(hb.recv_x_bytes == hb.max_rows * 2 * H && h8.recv_x_bytes == h8.max_rows * H, "size hint: payload bytes");
+  expect(h8.recv_scales_bytes == h8.max_rows * (H / 32) && hb.recv_scales_bytes == 0, "size hint: scale bytes");
+  expect(hb.combine_out_bytes == T * H * 2 && hb.total_bytes % (2 << 20) == 0, "size hint: combine and total");
+  void *d_hx = nullptr, *d_hsc = nullptr, *d_hrw = nullptr, *d_hmeta = nullptr;
+  HIP_OK(hipMalloc(&d_hx, hb.recv_x_bytes));
+  HIP_OK(hipMalloc(&d_hsc, h8.recv_scales_bytes));
+  HIP_OK(hipMalloc(&d_hrw, hb.recv_weights_bytes));
+  HIP_OK(hipMalloc(&d_hmeta, hb.recv_src_meta_bytes));
+  {
+    // fp8 with UE8M0 scales: one exponent byte per 32 channels, row-major
+    std::vector<uint8_t> rx(R * H), orx(R * H), sc(R * (H / 32)), osc(R * (H / 32));
+    HIP_OK(hipMemset(d_hsc, 0x33, h8.recv_scales_bytes));
+    EP_OK_(ep_dispatch(h, EP_DISPATCH_SCALES_UE8M0 | EP_DISPATCH_ZERO_PADDING, d_x, d_w, d_hx, (float*)d_hsc,
+                       (float*)d_hrw, (int32_t*)d_hmeta, nullptr));
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(rx.data(), d_hx, rx.size(), hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(sc.data(), d_hsc, sc.size(), hipMemcpyDeviceToHost));
+    if (oracle_dispatch_general(P, S, E, K, H, A, 1, 1, 2, 0, topk.data(), dst_slot.data(), ne_tot.data(),
+                                eoff.data(), wbase.data(), x.data(), nullptr, nullptr, w.data(), 0, R, orx.data(),
+                                (float*)osc.data(), nullptr, nullptr, nullptr) != ORACLE_OK)
+      return 5;
+    expect(rx == orx, "UE8M0 codes");
+    expect(sc == osc, "UE8M0 exponent bytes");
+  }
+  {
+    // the scratch-free dispatch, fp8 with column-major scales [H/128][R]
+    const int nb = H / 128;
+    std::vector<uint8_t> rx(R * H), orx(R * H);
+    std::vector<float> sc(nb * R), osc(nb * R), rw(R), orw(R);
+    std::vector<int32_t> meta(R * 2), ometa(R * 2);
+    const uint32_t fl = EP_DISPATCH_FP8 | EP_DISPATCH_SCALES_COL_MAJOR | EP_DISPATCH_ZERO_PADDING;
+    EP_OK_(ep_dispatch_noalloc(h, fl, d_x, d_w, d_hx, (float*)d_hsc, (float*)d_hrw, (int32_t*)d_hmeta, nullptr));
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(rx.data(), d_hx, rx.size(), hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(sc.data(), d_hsc, sc.size() * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(rw.data(), d_hrw, R * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(meta.data(), d_hmeta, R * 8, hipMemcpyDeviceToHost));
+    if (oracle_dispatch_general(P, S, E, K, H, A, 1, 1, 1, 0, topk.data(), dst_slot.data(), ne_tot.data(),
+                                eoff.data(), wbase.data(), x.data(), nullptr, nullptr, w.data(), 0, R, orx.data(),
+                                osc.data(), orw.data(), ometa.data(), nullptr) != ORACLE_OK)
+      return 5;
+    expect(rx == orx, "no-alloc fp8 codes");
+    expect(std::memcmp(sc.data(), osc.data(), sc.size() * 4) == 0, "no-alloc column-major scales");
+    expect(std::memcmp(rw.data(), orw.data(), R * 4) == 0 && meta == ometa, "no-alloc weights and meta");
+  }
   ep_handle_free(h);
+  HIP_OK(hipFree(d_hx));
+  HIP_OK(hipFree(d_hsc));
+  HIP_OK(hipFree(d_hrw));
+  HIP_OK(hipFree(d_hmeta));
+
+  {
+    // fixed-length windows: W rows per window, no read-back, zero tails
+    int64_t W = 0;
+    for (int r = 0; r < P; ++r) W = std::max<int64_t>(W, nexp[r]);
+    W += 3;
+    ep_config cf = cfg;
+    cf.num_worst_rows = (int32_t)W;
+    ep_size_hint hf{};
+    EP_OK_(ep_buffer_size_hint(&cf, EP_DISPATCH_ZERO_PADDING, &hf));
+    ep_handle* hx = nullptr;
+    int64_t rows_f = -1;
+    EP_OK_(ep_get_layout(&cf, d_topk, nullptr, &hx, &rows_f));
+    expect(rows_f == P * W && hf.max_rows == P * W, "fixed windows: P * W rows");
+    void *d_fx, *d_frw, *d_fmeta;
+    uint16_t* d_fout;
+    HIP_OK(hipMalloc(&d_fx, hf.recv_x_bytes));
+    HIP_OK(hipMalloc(&d_frw, hf.recv_weights_bytes));
+    HIP_OK(hipMalloc(&d_fmeta, hf.recv_src_meta_bytes));
+    HIP_OK(hipMalloc((void**)&d_fout, hf.combine_out_bytes));
+    HIP_OK(hipMemset(d_fx, 0x5A, hf.recv_x_bytes));
+    EP_OK_(ep_dispatch(hx, EP_DISPATCH_ZERO_PADDING, d_x, d_w, d_fx, nullptr, (float*)d_frw, (int32_t*)d_fmeta,
+                       nullptr));
+    EP_OK_(ep_combine(hx, d_fx, d_w, nullptr, d_fout, nullptr));
+    HIP_OK(hipDeviceSynchronize());
+    uint32_t st_flags = 99;
+    int64_t dropped = -1;
+    EP_OK_(ep_handle_status(hx, &st_flags, &dropped));
+    expect(st_flags == 0 && dropped == 0, "fixed windows: status");
+    const int64_t RF = P * W;
+    std::vector<uint16_t> fx(RF * H), ofx(RF * H), fout(T * H), ofout(T * H);
+    std::vector<float> frw(RF), ofrw(RF);
+    std::vector<int32_t> fmeta(RF * 2), ofmeta(RF * 2);
+    HIP_OK(hipMemcpy(fx.data(), d_fx, RF * H * 2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(frw.data(), d_frw, RF * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(fmeta.data(), d_fmeta, RF * 8, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(fout.data(), d_fout, T * H * 2, hipMemcpyDeviceToHost));
+    int64_t odropped = -1;
+    if (oracle_dispatch_general(P, S, E, K, H, A, 0, 1, 0, W, topk.data(), dst_slot.data(), ne_tot.data(),
+                                eoff.data(), nullptr, x.data(), nullptr, nullptr, w.data(), 0, RF, ofx.data(),
+                                nullptr, ofrw.data(), ofmeta.data(), &odropped) != ORACLE_OK ||
+        oracle_combine_general(P, S, E, K, H, W, topk.data(), dst_slot.data(), nullptr, ofx.data(), w.data(),
+                               nullptr, 0, T, ofout.data()) != ORACLE_OK)
+      return 5;
+    expect(odropped == 0, "fixed windows: the oracle drops nothing");
+    expect(fx == ofx, "fixed windows: payload and zero tails");
+    expect(std::memcmp(frw.data(), ofrw.data(), RF * 4) == 0 && fmeta == ofmeta, "fixed windows: weights and meta");
+    expect(fout == ofout, "fixed windows: combine");
+    ep_handle_free(hx);
+    HIP_OK(hipFree(d_fx));
+    HIP_OK(hipFree(d_frw));
+    HIP_OK(hipFree(d_fmeta));
+    HIP_OK(hipFree(d_fout));
+  }
   HIP_OK(hipFree(d_topk));
   HIP_OK(hipFree(d_x));
   HIP_OK(hipFree(d_w));

@@ -1241,8 +1241,10 @@ def test_debug_copy_is_a_copy():
 
 
 def test_c_abi_program_roundtrip():
-    """The C ABI from C++ alone (tests/c_abi/roundtrip.cpp): layout, bf16 / fp8 / cached
-    dispatch and combine against the oracle, run as a child process."""
+    """The C ABI from C++ alone (tests/c_abi/roundtrip.cpp), run as a child process, against
+    the oracle: layout, bf16 / fp8 / cached dispatch and combine; output buffers sized by
+    ep_buffer_size_hint; fp8 with UE8M0 scales; ep_dispatch_noalloc with column-major
+    scales; fixed-length windows (dispatch with zero tails, status, combine)."""
     import os
     import subprocess
 
