@@ -14,7 +14,9 @@ every step, as the pages recommend for the EP buffer.
 
 Beside the headline step the JSON line carries:
   "configs"        every other full-size workload timed per call (HIP events,
-                   median of 20): fresh dispatch, cached dispatch (for the fp8
+                   median of 20, each call behind a head start so that the
+                   host's launch time stays outside the events): fresh
+                   dispatch, cached dispatch (for the fp8
                    workload: 20 iterations, each with new x), combine, each
                    with its ledger bytes and fraction of the HBM peak;
   "fixed_windows"  the headline forward step with fixed-length windows
@@ -34,8 +36,9 @@ Prints ONE JSON line.  Usage:
 
 `python bench.py --calls` instead times every call of the library on every
 workload (HIP events; median and minimum of 20 calls, each timed alone after
-3 untimed ones, once right after the previous call and once with the L2s and
-the memory-side cache flushed by a 1 GiB scratch buffer) and prints one
+3 untimed ones and behind a head start, once right after the previous call and
+once with the L2s and the memory-side cache flushed by a 1 GiB scratch buffer;
+layout rows are host wall-clock times) and prints one
 JSON line per workload: layout, dispatch, cached dispatch, combine, combine
 with a bias, fixed-window dispatch, and for fp8 workloads the pre-quantised
 and column-major-scale dispatches, each with its ledger bytes and % of HBM.
@@ -420,12 +423,25 @@ def device_ceilings(dev) -> dict:
 
 _last_min_us = [0.0]
 
+# A spin kernel of this many shader cycles (~0.1 ms) runs before every timed call, outside
+# its events: the GPU is then still busy while the host checks the call's arguments and
+# launches it, so the events bracket the call alone and not the host's launch time (after a
+# synchronisation the GPU would otherwise sit idle inside the first event).  It touches no
+# memory, so the caches stay as the previous call left them.
+HEAD_START_CYCLES = 250_000
+
+
+def _head_start() -> None:
+    import torch
+
+    torch.cuda._sleep(HEAD_START_CYCLES)
+
 
 def _median_us(fn, reps: int = 20, warmup: int = 3, flush=None) -> float:
     """Median of `reps` timed calls (HIP events), each timed alone between two
-    synchronisations, after `warmup` untimed ones; the minimum is kept in
-    _last_min_us.  `flush`, if given, runs before every timed call, outside the
-    events."""
+    synchronisations, after `warmup` untimed ones and behind a head start (see
+    HEAD_START_CYCLES); the minimum is kept in _last_min_us.  `flush`, if given,
+    runs before every timed call, outside the events."""
     import statistics
 
     import torch
@@ -437,6 +453,7 @@ def _median_us(fn, reps: int = 20, warmup: int = 3, flush=None) -> float:
     for _ in range(reps):
         if flush is not None:
             flush()
+        _head_start()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         fn()
@@ -666,7 +683,8 @@ def overlap_table(workload: str, steps: int) -> int:
 
 def per_config(name: str, reps: int) -> dict:
     """One full-size workload timed per call (HIP events on the launch stream, each call
-    alone between two synchronisations after 3 untimed ones, median of `reps`): fresh
+    alone between two synchronisations after 3 untimed ones and behind a head start, median
+    of `reps`): fresh
     dispatch (the workload's dtype), cached dispatch, combine.  A workload with cached
     iterations times each of them with its own new x (drawn on the device, resident before
     timing).  Fractions use the same ledger as the headline."""
@@ -728,6 +746,7 @@ def per_config(name: str, reps: int) -> dict:
         torch.cuda.synchronize()
         ts = []
         for xi in xs:
+            _head_start()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             ep.dispatch_cached(h, xi, fp8, w.zero_padding, out=(rx, sc))
