@@ -81,9 +81,10 @@ struct ep_handle {
   int64_t* summary_host = nullptr;      // pinned; the finalize kernel writes it directly
   int64_t* summary_host_dev = nullptr;  // its device address
   int64_t layout_seq = 0;               // sequence number of the last enqueued layout
-  bool done_recorded = false;       // `done` marks an eager layout (not one captured in a graph)
-  hipEvent_t done = nullptr;        // end of the last eager layout's work
-  hipEvent_t summary_ready = nullptr;  // the last layout's host summary has landed
+  bool done_recorded = false;       // done_ev marks an eager layout (not one captured in a graph)
+  hipEvent_t done = nullptr;        // end of the last eager four-kernel layout's work
+  hipEvent_t summary_ready = nullptr;  // the last exact layout's host summary has landed
+  hipEvent_t done_ev = nullptr;     // the event that marks the end of the last eager layout's work
   hipEvent_t cm_done = nullptr;     // end of the last column-major fp8 dispatch (tok_scales free again)
   bool cm_recorded = false;
   size_t lds_count, lds_scan, lds_finalize, lds_rank, lds_small;
@@ -225,15 +226,13 @@ ep_status allocate(ep_handle* h) {
 
 void release(ep_handle* h) {
   if (!h) return;
-  if (h->summary_ready) (void)hipEventDestroy(h->summary_ready);
   if (h->cm_done) {
     if (h->cm_recorded) (void)hipEventSynchronize(h->cm_done);
     (void)hipEventDestroy(h->cm_done);
   }
-  if (h->done) {
-    if (h->done_recorded) (void)hipEventSynchronize(h->done);
-    (void)hipEventDestroy(h->done);
-  }
+  if (h->done_recorded && h->done_ev) (void)hipEventSynchronize(h->done_ev);
+  if (h->done) (void)hipEventDestroy(h->done);
+  if (h->summary_ready) (void)hipEventDestroy(h->summary_ready);
   if (h->arena) (void)hipFree(h->arena);
   if (h->summary_host) (void)hipHostFree(h->summary_host);
   delete h;
@@ -275,7 +274,11 @@ bool stream_capturing(hipStream_t s) {
 // captured; fixed windows only enqueue, so they can.  A captured layout
 // records no events: the graph's replays publish their summaries into the
 // pinned host buffer, which status queries read after the caller has waited
-// for the replay.
+// for the replay.  An eager layout records as few events as it needs, since
+// each record costs the GPU ~4.5 us (measured on MI355X): summary_ready only
+// for exact windows (the host's wait for the counts ends on it), and one
+// event for the end of all layout work -- the same event when one kernel does
+// everything.
 ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64_t* total_rows) {
   h->valid = false;
   const LayoutDims& d = h->dims;
@@ -289,12 +292,13 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
   RankOut ro{h->dst_slot, h->dst_row, h->row_slot, h->send_head, h->recv_src_idx, h->pad_rows};
   RankIn ri{h->chunk_excl_t, h->n_e, h->pad_base, h->expert_offset, h->window_row_base, h->packed_base,
             h->recv_src_base};
+  hipEvent_t end_ev = h->done;
   if (h->small_layout) {
     layout_small_kernel<<<1, kSmallThreads, h->lds_small, s>>>(d, topk_idx, h->is_token_in_rank,
                                                                h->num_tokens_per_expert, h->num_tokens_per_rank,
                                                                h->rank_prefix_matrix, fo, ri, ro);
     EP_LAUNCHED("layout_small_kernel");
-    if (!capturing) EP_HIP(hipEventRecord(h->summary_ready, s));
+    if (!h->fixed) end_ev = h->summary_ready;  // summary and ranks come from the one kernel
   } else {
     if (d.num_chunks > 0) {
       layout_count_kernel<<<d.num_chunks, kLayoutThreads, h->lds_count, s>>>(d, topk_idx, h->is_token_in_rank,
@@ -307,12 +311,14 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
     EP_LAUNCHED("layout_scan_kernel");
     layout_finalize_kernel<<<1, kFinalizeThreads, h->lds_finalize, s>>>(d, h->col_total, fo);
     EP_LAUNCHED("layout_finalize_kernel");
-    if (!capturing) EP_HIP(hipEventRecord(h->summary_ready, s));  // the finalize kernel wrote the host summary
+    if (!capturing && !h->fixed)
+      EP_HIP(hipEventRecord(h->summary_ready, s));  // the finalize kernel wrote the host summary
     // at least one workgroup, so that the padding rows are written even when T = 0
     layout_rank_kernel<<<std::max(d.num_chunks, 1), kLayoutThreads, h->lds_rank, s>>>(d, topk_idx, ri, ro);
     EP_LAUNCHED("layout_rank_kernel");
   }
-  if (!capturing) EP_HIP(hipEventRecord(h->done, s));
+  if (!capturing) EP_HIP(hipEventRecord(end_ev, s));
+  h->done_ev = end_ev;
   h->done_recorded = !capturing;
   h->counts_known = false;
   if (h->fixed) {  // fixed windows: nothing to wait for
@@ -350,7 +356,7 @@ ep_status ensure_counts(const ep_handle* hc) {
   ep_handle* h = const_cast<ep_handle*>(hc);
   if (h->counts_known) return EP_OK;
   if (h->done_recorded) {
-    const hipError_t e = hipEventSynchronize(h->done);
+    const hipError_t e = hipEventSynchronize(h->done_ev);
     if (e != hipSuccess) return fail(EP_ERR_HIP, "layout: %s", hipGetErrorString(e));
   }
   const int64_t* sm = h->summary_host;
