@@ -41,7 +41,9 @@ once with the L2s and the memory-side cache flushed by a 1 GiB scratch buffer;
 layout rows are host wall-clock times) and prints one
 JSON line per workload: layout, dispatch, cached dispatch, combine, combine
 with a bias, fixed-window dispatch, and for fp8 workloads the pre-quantised
-and column-major-scale dispatches, each with its ledger bytes and % of HBM.
+and column-major-scale dispatches, each with its ledger bytes and % of HBM;
+and the fixed-window step (layout + dispatch + combine), which needs no host
+sync, run eagerly and replayed from one captured HIP graph.
 
 `python bench.py --overlap` times the pages' overlap pattern on the DSv3 BF16
 workload: dispatch issued on the library's communication stream while the
@@ -596,6 +598,38 @@ def calls_table() -> int:
         fixed_bytes = (T * H * 2 + 8 * T * K + rows * (H * b + sf) + RF * 12 + zeroed * (H * b + sf))
         put("fixed_dispatch", lambda: ep.dispatch(hf, x_d, w_d, fp8, w.zero_padding, out=(rxf, scf, rwf, rmf)),
             fixed_bytes)
+        # The fixed-window step needs no host sync, so it can be captured in one HIP graph:
+        # layout + dispatch (+ combine of the identity experts' rows for bf16), timed on the host
+        # clock until it has finished, eagerly and as graph replays (median of 20 each).
+        def fixed_step():
+            ep.relayout(hf, topk_d)
+            ep.dispatch(hf, x_d, w_d, fp8, w.zero_padding, out=(rxf, scf, rwf, rmf))
+            if not fp8:
+                ep.combine(hf, rxf, w_d, out=out)
+
+        def host_us(fn):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(20):
+                t0 = time.perf_counter()
+                fn()
+                torch.cuda.synchronize()
+                ts.append(time.perf_counter() - t0)
+            return round(statistics.median(ts) * 1e6, 1)
+
+        r["fixed_step_eager_us"] = host_us(fixed_step)
+        eager_out = (out.clone() if not fp8 else rxf.clone())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fixed_step()
+        torch.cuda.synchronize()
+        r["fixed_step_graph_us"] = host_us(g.replay)
+        got = out if not fp8 else rxf
+        if not torch.equal(got.view(torch.uint8), eager_out.view(torch.uint8)):
+            raise RuntimeError(f"{name}: the graph replay of the fixed-window step differs from the eager step")
+        r["fixed_step_calls"] = "relayout + dispatch" + ("" if fp8 else " + combine")
+        del g, eager_out
         hf.free()
         h.free()
         del rxf, scf, rwf, rmf, out, x_d
