@@ -40,3 +40,37 @@ def test_committed_bench_line_has_every_field():
     assert d["config"]["workload"] == bench.DEFAULT_WORKLOAD
     # tokens per second of the whole step: T / ms_per_step
     assert abs(d["value"] - d["config"]["T"] / (d["ms_per_step"] * 1e-3)) / d["value"] < 1e-6
+
+
+def test_committed_kernel_trace_agrees_with_the_bench_line():
+    """The committed rocprofv3 kernel trace covers the run the committed bench line came from:
+    the trace's average duration of the roofline kernel's launches (the fresh and the cached
+    dispatch instantiations at the headline grid) agrees with the line's HIP-event average
+    launch time within 2%, and the JSON line the trace file quotes is the committed line."""
+    import re
+
+    with open(LINE) as f:
+        d = json.loads(f.read().strip().splitlines()[-1])
+    w = d["config"]["workload"]
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{w}.md")
+    with open(path) as f:
+        text = f.read()
+    r = d["roofline"]
+    assert r["kernel"] == "dispatch_kernel"
+    # rows: | `ep::dispatch_kernel<1, false, META, ...>` | grid | wg | vgpr | lds | scratch | launches | avg | median | min |
+    avgs = []
+    for m in re.finditer(r"^\| `ep::dispatch_kernel<([^>]*)>` \| (\d+) \| \d+ \| \d+ \| \d+ \| \d+ \| (\d+) \| ([\d.]+) \|",
+                         text, flags=re.M):
+        args = [a.strip() for a in m.group(1).split(",")]
+        fixed = args[4] == "true"
+        if args[1] == "false" and not fixed and int(m.group(3)) >= d["steps"]:  # bf16, exact windows, every step
+            avgs.append(float(m.group(4)))
+    # the first two such rows are the headline step's fresh and cached dispatch
+    assert len(avgs) >= 2, avgs
+    trace_avg = sum(avgs[:2]) / 2
+    assert abs(trace_avg - r["avg_launch_us"]) / r["avg_launch_us"] < 0.02, (trace_avg, r["avg_launch_us"])
+    # the JSON line the trace file quotes (possibly cut short) is the committed line's
+    quoted = [ln for ln in text.splitlines() if ln.startswith('{"metric"')]
+    assert quoted, "the trace file quotes no JSON line"
+    m = re.search(r'"value": ([0-9.e+]+)', quoted[-1])
+    assert m and float(m.group(1)) == d["value"], (m and m.group(1), d["value"])
