@@ -48,7 +48,10 @@ sync, run eagerly and replayed from one captured HIP graph.
 `python bench.py --overlap` times the pages' overlap pattern on the DSv3 BF16
 workload: dispatch issued on the library's communication stream while the
 shared experts (a bf16 MLP, hidden 7168 -> 2 x 2048 -> 7168, torch.matmul)
-run on the compute stream, against the two run back to back.
+run on the compute stream, against the two run back to back.  It runs at
+several tokens-per-rank counts (`--overlap-tokens`, default 128,512,4096:
+decode-sized batches to the full workload), one JSON line each, GPU time
+only (each timed region behind a head start).
 """
 
 from __future__ import annotations
@@ -642,7 +645,20 @@ def calls_table() -> int:
 # overlap with compute
 # ---------------------------------------------------------------------------
 
-def overlap_table(workload: str, steps: int) -> int:
+def overlap_table(workload: str, steps: int, tokens_per_rank: list[int]) -> int:
+    """The overlap pattern at each tokens-per-rank count S (the workload scaled to S): one
+    JSON line per S."""
+    import synth
+
+    for S in tokens_per_rank:
+        w = synth.CONFIGS[workload]
+        if S != w.S:
+            w = synth.scaled(w, S=S)
+        _overlap_one(w, steps)
+    return 0
+
+
+def _overlap_one(w, steps: int) -> None:
     import statistics
 
     import numpy as np
@@ -653,7 +669,6 @@ def overlap_table(workload: str, steps: int) -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = synth.CONFIGS[workload]
     T, K, H = w.T, w.K, w.H
     topk_d = torch.from_numpy(synth.gen_routing(w)).to(dev)
     x_d = torch.from_numpy(synth.gen_x(w).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -689,6 +704,7 @@ def overlap_table(workload: str, steps: int) -> int:
         torch.cuda.synchronize()
         ts = []
         for _ in range(steps):
+            _head_start()  # the host's launches stay outside the events: GPU time only
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             fn()
@@ -705,10 +721,9 @@ def overlap_table(workload: str, steps: int) -> int:
     res["hidden_frac_of_dispatch"] = (res["serial_us"] - res["overlapped_us"]) / d
     flops = 2.0 * T * H * 2 * inter + 2.0 * T * inter * H
     res["shared_experts_TFLOPs"] = flops / (sh * 1e-6) / 1e12
-    out = {"workload": workload, "overlap": {k: round(v, 3) for k, v in res.items()}}
+    out = {"workload": w.name, "P": w.P, "S": w.S, "T": T, "overlap": {k: round(v, 3) for k, v in res.items()}}
     h.free()
     print(json.dumps(out), flush=True)
-    return 0
 
 
 # ---------------------------------------------------------------------------
@@ -821,6 +836,8 @@ def main() -> int:
     ap.add_argument("--no-configs", action="store_true", help="skip the per-call legs of the other workloads")
     ap.add_argument("--calls", action="store_true", help="per-call table over all workloads")
     ap.add_argument("--overlap", action="store_true", help="dispatch overlapped with shared experts")
+    ap.add_argument("--overlap-tokens", default="128,512,4096",
+                    help="--overlap: tokens per rank to run at (the workload scaled), comma-separated")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run a plain torch copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -832,7 +849,8 @@ def main() -> int:
     if args.calls:
         return calls_table()
     if args.overlap:
-        return overlap_table(args.workload, args.steps)
+        wl = args.workload if args.workload != DEFAULT_WORKLOAD else "dsv3-bf16-p8-s4096-e256-k8-h7168"
+        return overlap_table(wl, args.steps, [int(v) for v in args.overlap_tokens.split(",")])
 
     import numpy as np
     import torch
