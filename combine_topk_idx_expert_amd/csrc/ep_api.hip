@@ -220,7 +220,10 @@ ep_status allocate(ep_handle* h) {
     return fail(EP_ERR_SHAPE, "layout needs %zu bytes of LDS per workgroup, the device has %d (E=%d P=%d K=%d)",
                 lds_need, lds_max, d.E, d.P, d.K);
   // small batches: one launch for the whole layout when it fits one workgroup
-  h->small_layout = d.num_chunks <= kSmallChunks && h->lds_small <= kSmallLdsMax && h->lds_small <= (size_t)lds_max;
+  // and its chunks are light enough for one wave each
+  const int64_t chunk_slots = (int64_t)std::min(d.S, kChunk) * d.K;
+  h->small_layout = d.num_chunks <= kSmallChunks && chunk_slots <= kSmallMaxChunkSlots &&
+                    h->lds_small <= kSmallLdsMax && h->lds_small <= (size_t)lds_max;
   return EP_OK;
 }
 

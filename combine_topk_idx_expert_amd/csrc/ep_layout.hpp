@@ -692,6 +692,12 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(LayoutDims 
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallChunks = kSmallThreads / kWave;  // one wave per chunk
 constexpr size_t kSmallLdsMax = 64 * 1024;           // bytes: beyond this the four-kernel path runs
+// Slots (tokens x top-k) of the fullest chunk up to which the one-workgroup
+// layout runs: one wave counts and ranks a whole chunk there, where the
+// four-kernel path spreads a chunk over four waves.  Measured on MI355X at
+// 8 chunks: 128 slots a chunk is 6-12 us faster in one workgroup, 256 is even
+// and 384 or more is slower.
+constexpr int kSmallMaxChunkSlots = 256;
 
 // LDS of layout_small_kernel, in bytes:
 //   int32: histograms [C][ncols] | column totals [ncols] | staged experts
@@ -792,7 +798,7 @@ __global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
       if (sh >= 0) o.send_head[(p.u0 + i / d.K) * d.P + ex[i] / d.El] = sh;
     }
   }
-  padding_rows(d, 0, 1, tid, kSmallThreads, in, o);
+  padding_rows(d, wv, kSmallThreads / kWave, lane, kWave, in, o);  // wave w: experts w, w + 16, ...
   EP_TIMING_MARK(EP_TK_SMALL, 7);
 }
 

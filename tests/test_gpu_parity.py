@@ -120,10 +120,14 @@ def test_layout_small(w, holes):
 
 # Shapes of at most 16 chunks of 64 tokens, whose layout runs as one workgroup, and one of
 # 17 chunks just past that limit (four kernels).
+# Decode-sized batches.  The one-workgroup layout runs for at most 16 chunks whose fullest
+# chunk holds at most 256 slots (tokens x top-k); the others take the four-kernel path.
 SMALL_BATCH = [
-    wl.Workload("sb-p4-s64-e16-k2", 4, 64, 16, 2, 512, 16, True, "uniform", seed=31),       # 4 chunks
-    wl.Workload("sb-p16-s64-e64-k6", 16, 64, 64, 6, 256, 8, True, "uniform", seed=32),      # 16 chunks
-    wl.Workload("sb-p8-s100-e256-k8", 8, 100, 256, 8, 1024, 128, True, "uniform", seed=33),  # 16 ragged chunks
+    wl.Workload("sb-p4-s64-e16-k2", 4, 64, 16, 2, 512, 16, True, "uniform", seed=31),       # 4 chunks, one WG
+    wl.Workload("sb-p16-s64-e64-k4", 16, 64, 64, 4, 256, 8, True, "uniform", seed=37),      # 16 chunks, one WG
+    wl.Workload("sb-p8-s100-e256-k2", 8, 100, 256, 2, 1024, 128, True, "uniform", seed=38),  # 16 ragged, one WG
+    wl.Workload("sb-p16-s64-e64-k6", 16, 64, 64, 6, 256, 8, True, "uniform", seed=32),      # 16 chunks, 4 kernels
+    wl.Workload("sb-p8-s100-e256-k8", 8, 100, 256, 8, 1024, 128, True, "uniform", seed=33),  # 16 ragged, 4 kernels
     wl.Workload("sb-p1-s1-e8-k3", 1, 1, 8, 3, 128, 4, True, "uniform", seed=34),            # 1 token
     wl.Workload("sb-p2-s7-e512-k4", 2, 7, 512, 4, 256, 3, True, "uniform", seed=35),         # many experts
     wl.Workload("sb-p17-s64-e34-k3", 17, 64, 34, 3, 256, 2, True, "uniform", seed=36),      # 17 chunks
