@@ -624,7 +624,7 @@ __device__ __forceinline__ void padding_rows(const LayoutDims& d, int e_begin, i
   }
 }
 
-// Also writes the padding rows of experts blockIdx.x, blockIdx.x + grid, ...
+// Also writes the padding rows of its share of the experts (wave by wave, see below).
 // LDS: per-wave counters [W][E+P+1] (experts, then ranks) | staged experts
 //      [64*K] | send positions [64*K]
 __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(LayoutDims d,
@@ -682,7 +682,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(LayoutDims 
       if (sh >= 0) out[(i / d.K) * d.P + ex[i] / d.El] = sh;
     }
   }
-  padding_rows(d, blockIdx.x, gridDim.x, tid, kLayoutThreads, in, o);
+  // wave w of workgroup b: experts b * W + w, then every grid * W further; its lanes the rows
+  padding_rows(d, blockIdx.x * kLayoutWaves + wv, gridDim.x * kLayoutWaves, lane, kWave, in, o);
   EP_TIMING_MARK(EP_TK_RANK, 7);
 }
 
