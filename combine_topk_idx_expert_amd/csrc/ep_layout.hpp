@@ -32,10 +32,11 @@
 //     the global stable order by (u, j).  The same kernel writes the
 //     padding-row list and send_head.
 //
-// Small batches (at most kSmallChunks chunks) run all four steps in one
-// 16-wave workgroup instead (layout_small_kernel): wave c counts and ranks
-// chunk c, the scans and the finalize step run between workgroup barriers on
-// LDS-resident histograms, and the handle arrays come out identical.
+// Small batches (at most kSmallChunks chunks, none holding more than
+// kSmallMaxChunkSlots slots) run all four steps in one 16-wave workgroup
+// instead (layout_small_kernel): wave c counts and ranks chunk c, the scans
+// and the finalize step run between workgroup barriers on LDS-resident
+// histograms, and the handle arrays come out identical.
 #pragma once
 
 #include "ep_device.hpp"
