@@ -162,3 +162,15 @@ def test_buffer_size_hint_needs_no_gpu(L):
         ep.buffer_size_hint(ep.Config(P, S, H, K, E + 1, A))
     with pytest.raises(ep.EpError):
         ep.buffer_size_hint(ep.Config(P, S, 136, K, E, A), fp8=True)
+
+
+def test_debug_timing_needs_the_timing_build(L):
+    """ep_debug_timing reads the device timing slots only in a library built with
+    EP_DEVICE_TIMING=1; the ordinary build refuses with EP_ERR_SHAPE and says why, before any
+    HIP call."""
+    import numpy as np
+
+    slots = np.zeros(8, np.uint64)
+    assert L.ep_debug_timing(slots.ctypes.data, 8) == -2  # EP_ERR_SHAPE
+    assert b"EP_DEVICE_TIMING" in L.ep_last_error()
+    assert not slots.any()
