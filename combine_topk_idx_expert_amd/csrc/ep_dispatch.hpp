@@ -199,6 +199,23 @@ __device__ __forceinline__ void store_pacing() {
   }
 }
 
+// fp8 rows with row-major scales: each 16-byte chunk position issues its code
+// store, then (lanes 0..3) its scale store, so a row is 2 * NC stores.  Stores
+// complete in issue order; this pacing waits for the row's code stores only,
+// leaving the last scale store in flight.  Used for pre-quantised input, where
+// it measured 2-5% faster on MI355X than waiting for every store; with the
+// quantisation in the wave it ranged from 1% faster to 2% slower at the
+// DeepSeek-V3 shape (1-2% faster under Zipf routing), so those waves keep the
+// plain pacing.
+template <int NC>
+__device__ __forceinline__ void store_pacing_fp8() {
+  if constexpr (EP_DISPATCH_ROWS_IN_FLIGHT > 0) {
+    constexpr int want = 2 * NC * (EP_DISPATCH_ROWS_IN_FLIGHT - 1) + 1;
+    constexpr int allow = want < 15 ? want : 15;
+    __builtin_amdgcn_s_waitcnt(0x0F70 | allow);
+  }
+}
+
 // scales: fp8 row-major scales to zero with the row (null: none); with UE8M0
 // they are the row's H/32 exponent bytes, zeroed four per lane (lanes 0..3).
 template <int NC, bool FP8, bool UE8M0 = false>
@@ -362,7 +379,10 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
             if (fused_scales && lane < 4 && blk < nblk) a.recv_scales[(int64_t)row * nblk + blk] = sc[c];
           }
         }
-        store_pacing<NC>();
+        if (PREQ && fused_scales)
+          store_pacing_fp8<NC>();
+        else
+          store_pacing<NC>();
       }
     }
   } else if (gw < token_items + pad_items) {
