@@ -106,6 +106,8 @@ SMALL = [
     wl.Workload("s1-p8-s1-e64-k8", 8, 1, 64, 8, 512, 16, True, "uniform", seed=6),
     wl.Workload("big-e-p64-s33-e1024-k16", 64, 33, 1024, 16, 256, 32, True, "uniform", seed=7),
     wl.Workload("k32-p2-s70-e64-k32", 2, 70, 64, 32, 128, 3, True, "uniform", seed=8),
+    wl.Workload("h8-p4-s40-e16-k3", 4, 40, 16, 3, 8, 4, True, "uniform", seed=9),  # smallest hidden: one chunk a row
+    wl.Workload("h24-p3-s50-e24-k12", 3, 50, 24, 12, 24, 2, True, "uniform", seed=10),  # K > 8: register combine, 3 chunks
 ]
 
 
@@ -623,7 +625,7 @@ def check_fixed_layout(lay, h, W):
     np.testing.assert_array_equal(wb, np.arange(lay.P + 1) * W)
 
 
-FIXED_CASES = [SMALL[0], SMALL[1], SMALL[2], SMALL[4], SMALL[6], SMALL[7]]
+FIXED_CASES = [SMALL[0], SMALL[1], SMALL[2], SMALL[4], SMALL[6], SMALL[7], SMALL[10]]
 
 
 @pytest.mark.parametrize("w", FIXED_CASES, ids=lambda w: w.name)
