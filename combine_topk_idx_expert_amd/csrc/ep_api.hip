@@ -260,6 +260,28 @@ ep_status wait_summary(ep_handle* h) {
   return EP_OK;
 }
 
+// Identities the finalize step guarantees between the words of the host
+// summary: the windows start at 0 and end at the total row count, each holds
+// its rows (exact windows; symmetric ones may hold more), and the receive
+// total is the sum of the per-rank receive counts.  The words and the
+// sequence number reach host memory as separate writes over the bus, so the
+// host checks them before it trusts a row count that sizes the caller's
+// buffers.
+bool summary_consistent(const ep_handle* h) {
+  const int64_t* sm = h->summary_host;
+  const int P = h->dims.P;
+  const int64_t* ne = sm + kSummaryHeader;
+  const int64_t* nr = ne + P;
+  const int64_t* wb = nr + P;
+  if (wb[0] != 0 || wb[P] != sm[0]) return false;
+  int64_t recv = 0;
+  for (int r = 0; r < P; ++r) {
+    recv += nr[r];
+    if (!h->fixed && wb[r + 1] - wb[r] < ne[r]) return false;
+  }
+  return recv == sm[3];
+}
+
 // True when `s` is capturing into a graph.  A failing query (for instance of
 // the null stream while another stream captures) counts as "not capturing"
 // and its error is cleared so that the launch checks below do not see it.
@@ -333,6 +355,11 @@ ep_status run_layout(ep_handle* h, const int64_t* topk_idx, hipStream_t s, int64
   // The host needs only the summary; the rank kernel keeps running meanwhile,
   // so the caller's next launches queue up behind it without a gap.
   if (ep_status st = wait_summary(h); st != EP_OK) return st;
+  if (!summary_consistent(h)) {  // read it again once the layout's writes have all landed
+    const hipError_t e = hipEventSynchronize(h->summary_ready);
+    if (e != hipSuccess) return fail(EP_ERR_HIP, "layout: %s", hipGetErrorString(e));
+    if (!summary_consistent(h)) return fail(EP_ERR_HIP, "layout summary in host memory is inconsistent");
+  }
   const int64_t* sm = h->summary_host;
   if (sm[2] != 0) return fail(EP_ERR_ROUTING, "topk_idx holds an expert id outside {-1} U [0, %d)", d.E);
   if (sm[0] >= ((int64_t)1 << 31))
@@ -362,6 +389,7 @@ ep_status ensure_counts(const ep_handle* hc) {
     const hipError_t e = hipEventSynchronize(h->done_ev);
     if (e != hipSuccess) return fail(EP_ERR_HIP, "layout: %s", hipGetErrorString(e));
   }
+  if (!summary_consistent(h)) return fail(EP_ERR_HIP, "layout summary in host memory is inconsistent");
   const int64_t* sm = h->summary_host;
   h->total_pad = sm[1];
   h->sum_recv = sm[3];
