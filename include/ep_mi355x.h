@@ -139,6 +139,10 @@ typedef struct ep_handle ep_handle; /* opaque; owns its device arrays */
  * returns, and later work on `stream` is ordered after it.  Fixed mode: returns as soon as the work is enqueued, with
  * total_rows = P * num_worst_rows; a routing error does not fail the call
  * (the bad slots are treated as unused) and is reported by ep_handle_status.
+ * Before the host uses the counts it checks identities between them (window
+ * bases from 0 to total_rows, each window holding its rows, the receive
+ * total); counts that still disagree once the layout has finished are
+ * EP_ERR_HIP, never a wrong total_rows.
  * Errors: EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_OVERFLOW, EP_ERR_ROUTING (exact
  * mode), EP_ERR_NOMEM, EP_ERR_HIP.
  */
